@@ -1,0 +1,177 @@
+"""Seeded synthetic MoE layers and token batches.
+
+This module only draws random inputs: it holds none of the layer's arithmetic
+(no routing, no grouping, no dequantisation, no expert FFN, no combine).  Both
+the CPU oracle (``oracle/``) and the GPU path's tests and benchmark take their
+inputs from here, so the two sides see the same bytes.
+
+Workloads follow the pages' GLM-5.2-style MoE layer: 256 routed experts with
+8 routed + 1 shared active per token, each routed expert a contiguous ~19 MB
+int4 block (yunpan.plus article, "capability 1: VRAM/RAM/NVMe as one tier";
+zhichai.net article, "the sparsity loophole" and the tier diagram), plus
+smaller layers of the same family for parity tests.
+
+Recipe (fixed, seeded, reproducible):
+
+* one ``numpy.random.SeedSequence(20261200 + cfg)`` per workload, spawned into
+  child streams in a fixed order: router weights, expert-popularity
+  permutation, token batches, then one stream per routed expert, shared expert
+  last; a draw from one stream never shifts another, so any single expert can
+  be regenerated alone;
+* router weights W_r ~ N(0, 0.02), float32, shape [E, d];
+* router bias (only where a workload asks for skew): a Zipf(s=1.1)
+  popularity p_r = r^-1.1 / sum_r' r'^-1.1 over ranks r = 1..E, ranks
+  assigned to experts by a seeded permutation, bias_e = ln p_rank(e), float32;
+* activations N(0, 1), float32 for the tiny workload, otherwise rounded to
+  bfloat16 (round to nearest even); the float32 view returned alongside holds
+  exactly the bfloat16 values;
+* expert weights: uniform random bytes, so every int4 code is uniform over
+  the two's-complement range [-8, 7]; group scales U[0.005, 0.02] rounded to
+  IEEE float16 (all normal numbers).
+
+Expert block byte layout (one contiguous block per expert, row-major
+[out][in], element 2j of a row in the low nibble of byte j, scales IEEE fp16,
+one scale per 64 consecutive input elements of a row)::
+
+    q_gate[f][d/2] | q_up[f][d/2] | q_down[d][f/2] |
+    s_gate[f][d/64] | s_up[f][d/64] | s_down[d][f/64]
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+
+GROUP = 64
+SEED_BASE = 20261200
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerShape:
+    d: int
+    f: int
+    n_experts: int
+    top_k: int
+    f_shared: int          # 0: no shared expert
+    zipf_bias: bool
+    x_dtype: str           # "f32" or "bf16"
+    group: int = GROUP
+
+
+# The five workloads: tiny parity layer, small-expert decode layer,
+# many-small-experts layer with a shared expert and skewed routing, the
+# ~19 MB-expert layer for decode, and the same layer for 2048-token prefill.
+WORKLOADS = {
+    1: dict(shape=LayerShape(512, 256, 8, 2, 0, False, "f32"), tokens=(4,)),
+    2: dict(shape=LayerShape(2048, 1024, 64, 8, 0, False, "bf16"), tokens=(1, 16)),
+    3: dict(shape=LayerShape(2048, 512, 256, 8, 512, True, "bf16"), tokens=(64,)),
+    4: dict(shape=LayerShape(6144, 2048, 256, 8, 2048, False, "bf16"), tokens=(1, 8)),
+    5: dict(shape=LayerShape(6144, 2048, 256, 8, 2048, True, "bf16"), tokens=(2048,)),
+}
+
+
+def block_bytes(d: int, f: int, group: int = GROUP) -> int:
+    """Bytes of one expert block in the layout above."""
+    n = 3 * d * f
+    return n // 2 + (n // group) * 2
+
+
+def block_offsets(d: int, f: int, group: int = GROUP) -> dict:
+    """Byte offsets of the six sub-arrays inside one expert block."""
+    o = {}
+    pos = 0
+    for name, size in (("q_gate", f * d // 2), ("q_up", f * d // 2), ("q_down", d * f // 2),
+                       ("s_gate", f * (d // group) * 2), ("s_up", f * (d // group) * 2),
+                       ("s_down", d * (f // group) * 2)):
+        o[name] = pos
+        pos += size
+    o["end"] = pos
+    return o
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+    Inputs here are finite N(0,1) draws, so no NaN handling is needed."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass
+class Layer:
+    cfg: int
+    shape: LayerShape
+    w_router: np.ndarray              # [E, d] float32
+    bias: Optional[np.ndarray]        # [E] float32 or None
+    experts: np.ndarray               # [E, block_bytes] uint8 (rows not drawn are zero)
+    shared: Optional[np.ndarray]      # [block_bytes] uint8 or None
+    drawn: np.ndarray                 # [E] bool: which expert blocks were drawn
+
+    @property
+    def expert_bytes(self) -> int:
+        return block_bytes(self.shape.d, self.shape.f, self.shape.group)
+
+
+def _streams(cfg: int):
+    sh = WORKLOADS[cfg]["shape"]
+    ss = np.random.SeedSequence(SEED_BASE + cfg)
+    kids = ss.spawn(3 + sh.n_experts + 1)
+    return sh, kids
+
+
+def _draw_block(ss: np.random.SeedSequence, d: int, f: int, group: int, out: np.ndarray) -> None:
+    rng = np.random.Generator(np.random.PCG64(ss))
+    nq = 3 * d * f // 2
+    ns = 3 * d * f // group
+    out[:nq] = np.frombuffer(rng.bytes(nq), dtype=np.uint8)
+    out[nq:nq + 2 * ns] = rng.uniform(0.005, 0.02, ns).astype(np.float16).view(np.uint8)
+
+
+def make_layer(cfg: int, experts: Optional[Sequence[int]] = None) -> Layer:
+    """Draw the layer of workload ``cfg``.  ``experts`` limits which routed
+    expert blocks are drawn (None: all); the others stay zero bytes."""
+    sh, kids = _streams(cfg)
+    E, d, f = sh.n_experts, sh.d, sh.f
+    rng_w = np.random.Generator(np.random.PCG64(kids[0]))
+    w_router = (rng_w.standard_normal((E, d)) * 0.02).astype(np.float32)
+    bias = None
+    if sh.zipf_bias:
+        rng_p = np.random.Generator(np.random.PCG64(kids[1]))
+        rank = rng_p.permutation(E) + 1                      # rank of expert e, 1..E
+        pr = np.arange(1, E + 1, dtype=np.float64) ** -1.1
+        pr /= pr.sum()
+        bias = np.log(pr[rank - 1]).astype(np.float32)
+    bb = block_bytes(d, f, sh.group)
+    blocks = np.zeros((E, bb), dtype=np.uint8)
+    drawn = np.zeros(E, dtype=bool)
+    ids = range(E) if experts is None else sorted(set(int(e) for e in experts))
+    for e in ids:
+        _draw_block(kids[3 + e], d, f, sh.group, blocks[e])
+        drawn[e] = True
+    shared = None
+    if sh.f_shared:
+        assert sh.f_shared == f, "shared expert uses the routed expert's block shape"
+        shared = np.zeros(bb, dtype=np.uint8)
+        _draw_block(kids[3 + E], d, f, sh.group, shared)
+    return Layer(cfg, sh, w_router, bias, blocks, shared, drawn)
+
+
+def make_tokens(cfg: int, T: int, batch: int = 0):
+    """Token batch ``batch`` of workload ``cfg`` with T tokens.
+
+    Returns (x_device_bits, x_f32): for bf16 workloads x_device_bits is the
+    uint16 bfloat16 bit pattern [T, d] and x_f32 the exact float32 values;
+    for the float32 workload both are the same float32 array."""
+    sh, kids = _streams(cfg)
+    ss = kids[2].spawn(batch + 1)[batch] if batch else kids[2]
+    rng = np.random.Generator(np.random.PCG64(ss))
+    x = rng.standard_normal((T, sh.d)).astype(np.float32)
+    if sh.x_dtype == "f32":
+        return x, x
+    bits = bf16_round(x)
+    return bits, bf16_to_f32(bits)
