@@ -179,22 +179,28 @@ def batch_union(topk_idx: np.ndarray, n_experts: int):
     inv_perm[s] the grouped position of slot s
     active      experts with counts > 0, ascending (first n_active entries;
                 the rest is filled with -1)
+
+    A slot whose expert id lies outside [0, E) is not grouped: it is not
+    counted, has no grouped position (inv_perm = -1) and adds nothing in the
+    combine.  (The pages never produce such ids; this is the library's rule.)
     """
     flat = [int(e) for e in np.asarray(topk_idx).reshape(-1)]
     n = len(flat)
     counts = [0] * n_experts
     for e in flat:
-        counts[e] += 1
+        if 0 <= e < n_experts:
+            counts[e] += 1
     offsets = [0] * (n_experts + 1)
     for e in range(n_experts):
         offsets[e + 1] = offsets[e] + counts[e]
     fill = list(offsets[:n_experts])
-    perm = [0] * n
+    perm = [-1] * n
     for s, e in enumerate(flat):          # slots visited in id order: stable
-        perm[fill[e]] = s
-        fill[e] += 1
-    inv_perm = [0] * n
-    for i, s in enumerate(perm):
+        if 0 <= e < n_experts:
+            perm[fill[e]] = s
+            fill[e] += 1
+    inv_perm = [-1] * n
+    for i, s in enumerate(perm[:offsets[n_experts]]):
         inv_perm[s] = i
     active = [e for e in range(n_experts) if counts[e] > 0]
     n_active = len(active)
@@ -251,7 +257,8 @@ def combine(y, y_shared, inv_perm, topk_w, top_k):
     out = np.zeros((T, y.shape[1]), dtype=np.float64)
     for j in range(top_k):
         rows = np.asarray(inv_perm, dtype=np.int64).reshape(T, top_k)[:, j]
-        out += w[:, j:j + 1] * y[rows]
+        routed = rows >= 0
+        out[routed] += w[routed, j:j + 1] * y[rows[routed]]
     if y_shared is not None:
         out += y_shared
     return out

@@ -17,7 +17,8 @@ Recipe (fixed, seeded, reproducible):
   child streams in a fixed order: router weights, expert-popularity
   permutation, token batches, then one stream per routed expert, shared expert
   last; a draw from one stream never shifts another, so any single expert can
-  be regenerated alone;
+  be regenerated alone (the 2048-token prefill workload takes its router
+  weights and expert blocks from the ~19 MB-expert decode workload's streams);
 * router weights W_r ~ N(0, 0.02), float32, shape [E, d];
 * router bias (only where a workload asks for skew): a Zipf(s=1.1)
   popularity p_r = r^-1.1 / sum_r' r'^-1.1 over ranks r = 1..E, ranks
@@ -25,7 +26,7 @@ Recipe (fixed, seeded, reproducible):
 * activations N(0, 1), float32 for the tiny workload, otherwise rounded to
   bfloat16 (round to nearest even); the float32 view returned alongside holds
   exactly the bfloat16 values;
-* expert weights: uniform random bytes, so every int4 code is uniform over
+* expert weights: uniform random bytes (``integers(0, 256)``), so every int4 code is uniform over
   the two's-complement range [-8, 7]; group scales U[0.005, 0.02] rounded to
   IEEE float16 (all normal numbers).
 
@@ -38,6 +39,7 @@ one scale per 64 consecutive input elements of a row)::
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 from typing import Optional, Sequence
 
@@ -67,8 +69,11 @@ WORKLOADS = {
     2: dict(shape=LayerShape(2048, 1024, 64, 8, 0, False, "bf16"), tokens=(1, 16)),
     3: dict(shape=LayerShape(2048, 512, 256, 8, 512, True, "bf16"), tokens=(64,)),
     4: dict(shape=LayerShape(6144, 2048, 256, 8, 2048, False, "bf16"), tokens=(1, 8)),
-    5: dict(shape=LayerShape(6144, 2048, 256, 8, 2048, True, "bf16"), tokens=(2048,)),
+    5: dict(shape=LayerShape(6144, 2048, 256, 8, 2048, True, "bf16"), tokens=(2048,),
+            layer_of=4),
 }
+# Workload 5 runs on workload 4's layer (same router weights and expert
+# blocks); only its Zipf router bias and its token batches are its own.
 
 
 def block_bytes(d: int, f: int, group: int = GROUP) -> int:
@@ -118,24 +123,28 @@ class Layer:
 
 
 def _streams(cfg: int):
+    """(shape, layer streams, token stream) of a workload."""
     sh = WORKLOADS[cfg]["shape"]
-    ss = np.random.SeedSequence(SEED_BASE + cfg)
-    kids = ss.spawn(3 + sh.n_experts + 1)
-    return sh, kids
+    own = np.random.SeedSequence(SEED_BASE + cfg).spawn(3 + sh.n_experts + 1)
+    base = WORKLOADS[cfg].get("layer_of", cfg)
+    kids = own if base == cfg else np.random.SeedSequence(SEED_BASE + base).spawn(3 + sh.n_experts + 1)
+    kids = list(kids)
+    kids[1] = own[1]          # the popularity permutation is always the workload's own
+    return sh, kids, own[2]
 
 
 def _draw_block(ss: np.random.SeedSequence, d: int, f: int, group: int, out: np.ndarray) -> None:
     rng = np.random.Generator(np.random.PCG64(ss))
     nq = 3 * d * f // 2
     ns = 3 * d * f // group
-    out[:nq] = np.frombuffer(rng.bytes(nq), dtype=np.uint8)
+    out[:nq] = rng.integers(0, 256, size=nq, dtype=np.uint8)
     out[nq:nq + 2 * ns] = rng.uniform(0.005, 0.02, ns).astype(np.float16).view(np.uint8)
 
 
 def make_layer(cfg: int, experts: Optional[Sequence[int]] = None) -> Layer:
     """Draw the layer of workload ``cfg``.  ``experts`` limits which routed
     expert blocks are drawn (None: all); the others stay zero bytes."""
-    sh, kids = _streams(cfg)
+    sh, kids, _ = _streams(cfg)
     E, d, f = sh.n_experts, sh.d, sh.f
     rng_w = np.random.Generator(np.random.PCG64(kids[0]))
     w_router = (rng_w.standard_normal((E, d)) * 0.02).astype(np.float32)
@@ -150,9 +159,10 @@ def make_layer(cfg: int, experts: Optional[Sequence[int]] = None) -> Layer:
     blocks = np.zeros((E, bb), dtype=np.uint8)
     drawn = np.zeros(E, dtype=bool)
     ids = range(E) if experts is None else sorted(set(int(e) for e in experts))
-    for e in ids:
-        _draw_block(kids[3 + e], d, f, sh.group, blocks[e])
-        drawn[e] = True
+    ids = list(ids)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, max(1, len(ids)))) as ex:
+        list(ex.map(lambda e: _draw_block(kids[3 + e], d, f, sh.group, blocks[e]), ids))
+    drawn[ids] = True
     shared = None
     if sh.f_shared:
         assert sh.f_shared == f, "shared expert uses the routed expert's block shape"
@@ -167,8 +177,8 @@ def make_tokens(cfg: int, T: int, batch: int = 0):
     Returns (x_device_bits, x_f32): for bf16 workloads x_device_bits is the
     uint16 bfloat16 bit pattern [T, d] and x_f32 the exact float32 values;
     for the float32 workload both are the same float32 array."""
-    sh, kids = _streams(cfg)
-    ss = kids[2].spawn(batch + 1)[batch] if batch else kids[2]
+    sh, _, tok = _streams(cfg)
+    ss = tok.spawn(batch + 1)[batch] if batch else tok
     rng = np.random.Generator(np.random.PCG64(ss))
     x = rng.standard_normal((T, sh.d)).astype(np.float32)
     if sh.x_dtype == "f32":

@@ -466,3 +466,14 @@ def test_expert_geometry_matches_the_pages():
     per_tok_gb = v("active_routed_per_token") * blk * layers / 1e9
     assert abs(per_tok_gb - v("routed_gigabytes_changing_per_token_approx")) / 11 < 0.15
     assert v("total_params_billion") * 0.5 == v("int4_model_gigabytes")
+
+
+def test_union_skips_out_of_range_ids():
+    topk = np.array([[2, 9], [-1, 1], [2, 1]], dtype=np.int32)   # E = 4: 9 and -1 are not experts
+    counts, offsets, perm, inv, active, n_active = oracle.batch_union(topk, 4)
+    assert counts.tolist() == [0, 2, 2, 0]
+    assert offsets.tolist() == [0, 0, 2, 4, 4]
+    assert perm[:4].tolist() == [3, 5, 0, 4]
+    assert inv.tolist() == [2, -1, -1, 0, 3, 1]
+    out = oracle.combine(np.arange(12.0).reshape(6, 2), None, inv, np.ones((3, 2)), 2)
+    assert out.tolist() == [[4.0, 5.0], [0.0, 1.0], [6.0 + 2.0, 7.0 + 3.0]]
