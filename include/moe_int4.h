@@ -1,0 +1,199 @@
+/*
+ * moe_int4.h -- C ABI of one MoE layer's routed-expert FFN over int4
+ * group-quantised weights, on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (pages: zhichai.net, "744亿参数塞进25GB内存：colibrì如何用1300行C代码把
+ * 不可能变成可能", section on MoE sparsity; yunpan.plus article on Colibrì,
+ * sections "capability 2" and "capability 3"):
+ *
+ *   moe_route       router logits, top-k of E experts per token, softmax
+ *                   renormalised over the chosen k
+ *   moe_union       batch-union: group the T*k routing slots by expert so an
+ *                   expert's weights are read once for all tokens routed to it
+ *                   (the unit a cluster worker receives: one layer's routed
+ *                   batch-union)
+ *   moe_expert_ffn  int4 gs64 dequant fused into a SwiGLU expert for every
+ *                   expert in the union, plus the always-active shared expert
+ *   moe_combine     gate-weighted sum of each token's k expert outputs plus
+ *                   the shared expert's output
+ *
+ * Conventions common to every call:
+ *  - Every pointer argument except `shape` is a DEVICE pointer owned by the
+ *    caller.  The library allocates nothing, keeps no state between calls,
+ *    and never synchronises the host.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    legacy default stream).  Data-dependent sizes (counts, n_active) stay on
+ *    the device: later calls read them there.
+ *  - Arguments are checked before anything is enqueued.  On any error the call
+ *    returns a non-zero status, enqueues nothing and leaves every output
+ *    untouched.  There is never a silent fallback to another precision or
+ *    algorithm (the pages' rule that precision and router semantics never
+ *    change silently: yunpan.plus article, "capability 4").
+ *  - A kernel launch failure returns MOE_ERR_HIP; faults during execution
+ *    surface at the caller's next synchronisation of `stream`.
+ *  - Calls are thread-safe.  Calls that share a workspace buffer must be
+ *    ordered (same stream, or synchronised).
+ *  - T == 0 (an empty batch) is valid: moe_union writes empty grouping
+ *    outputs; the other calls enqueue nothing and return MOE_OK.
+ */
+#ifndef MOE_INT4_H
+#define MOE_INT4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  MOE_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree        */
+  MOE_ERR_DTYPE = 3,       /* dtype not allowed for this call or path         */
+  MOE_ERR_ALIGN = 4,       /* a pointer is not aligned as documented          */
+  MOE_ERR_UNSUPPORTED = 5, /* well-formed but not provided (e.g. group != 64) */
+  MOE_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required      */
+  MOE_ERR_HIP = 7          /* a HIP launch failed                             */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Which expert-FFN kernel family runs (moe_expert_ffn):
+ *  DECODE_F32    HBM-bound int4 GEMV for small batches; activations bf16 or
+ *                f32; h, y and y_shared are float32 (fp32 accumulation).
+ *  PREFILL_BF16  grouped GEMM on bf16 MFMA for large batches; activations
+ *                must be bf16; h, y and y_shared are bfloat16 (fp32
+ *                accumulation).  An f32 x is rejected, never rounded. */
+typedef enum { MOE_PATH_DECODE_F32 = 0, MOE_PATH_PREFILL_BF16 = 1 } moe_path;
+
+/* Layer geometry.
+ *  d          hidden size; multiple of 64, 64..8192
+ *  f          routed-expert intermediate size; multiple of 64, 64..8192
+ *  n_experts  routed experts E, 1..1024
+ *  top_k      experts per token k, 1..min(E, 32)
+ *  group      int4 quantisation group along the input dimension; must be 64
+ *             (gs64, the grouping the pages recommend over per-row scales:
+ *             yunpan.plus article, "capability 4"; ssnai.com digest,
+ *             prerequisites)
+ *  f_shared   0 = no shared expert; otherwise the shared expert's
+ *             intermediate size, which must equal f (same block layout) */
+typedef struct {
+  int32_t d;
+  int32_t f;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t group;
+  int32_t f_shared;
+} moe_shape;
+
+/* Bytes of one expert block; 0 if d, f or group is not valid.  An expert
+ * is one contiguous block (the pages keep and evict each ~19 MB int4 expert
+ * as one piece: zhichai.net, section on why mmap falls short), laid out as
+ *
+ *   q_gate[f][d/2] | q_up[f][d/2] | q_down[d][f/2] |
+ *   s_gate[f][d/64] | s_up[f][d/64] | s_down[d][f/64]
+ *
+ * q_*: int4 codes, row-major [out][in], element 2j of a row in the low
+ *      nibble of byte j, each nibble a two's-complement value in [-8, 7];
+ * s_*: IEEE float16 scales, one per 64 consecutive input elements of a row;
+ * weight[r][c] = q[r][c] * s[r][c/64].
+ * Gate and up are [f][d] (input d), down is [d][f] (input f).
+ * Equals 3*d*f/2 + 3*d*f/group*2; 20,054,016 bytes at d=6144, f=2048. */
+size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group);
+
+/* Scratch bytes moe_route needs for T tokens (router logits, float64). */
+size_t moe_route_workspace_bytes(const moe_shape* shape, int32_t T);
+
+/* Router: for every token t,
+ *   l[t][e] = sum_i x[t][i] * w_router[e][i] + bias[e]     (float64)
+ *   S_t     = the top_k experts with the largest l[t][e]; equal logits are
+ *             ordered by lower expert id; S_t is written in descending logit
+ *             order
+ *   w[t][j] = exp(l_j - l_0) / sum_{j'} exp(l_j' - l_0) over S_t
+ * (pages: zhichai.net, MoE sparsity section -- the router picks 8 of 256
+ * experts per token; the gating function, precision and tie rule are not on
+ * the pages: softmax renormalised over the chosen k, float64 logits so the
+ * selection does not depend on summation order, lower id first on ties).
+ *  x         [T][d], bf16 or f32 (x_dt), row-major, 16-byte aligned
+ *  w_router  [E][d] float32, row-major, 16-byte aligned
+ *  bias      [E] float32, or NULL for none; added before both selection and
+ *            weighting
+ *  topk_idx  out [T][top_k] int32 expert ids
+ *  topk_w    out [T][top_k] float32 gate weights (sum to 1 per token)
+ *  workspace >= moe_route_workspace_bytes(shape, T) bytes, 256-byte aligned
+ * Non-finite logits give unspecified (but in-range) results. */
+moe_status moe_route(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
+                     const float* w_router, const float* bias, int32_t* topk_idx,
+                     float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Batch-union grouping of the T*top_k routing slots (slot id s = t*top_k + j
+ * routes token t to expert topk_idx[t][j]); pages: yunpan.plus article,
+ * "capability 2" (an expert needed by several positions of a batch is read
+ * once) and "capability 3" (a worker runs the FFN on one layer's routed
+ * batch-union).
+ *  counts    out [E]    slots routed to each expert
+ *  offsets   out [E+1]  exclusive prefix sum of counts (offsets[E] = slots)
+ *  perm      out [T*k]  slot id at each grouped position, ordered by expert
+ *                       ascending, then slot id ascending
+ *  inv_perm  out [T*k]  grouped position of each slot
+ *  active    out [E]    experts with counts > 0 ascending, then -1 padding
+ *  n_active  out [1]    number of such experts
+ * The result is deterministic (no dependence on atomic ordering).  An entry
+ * of topk_idx outside [0, E) is not grouped: it gets inv_perm = -1, is not
+ * counted, and moe_combine treats it as a zero contribution. */
+moe_status moe_union(const moe_shape* shape, int32_t T, const int32_t* topk_idx,
+                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                     int32_t* active, int32_t* n_active, void* stream);
+
+/* Scratch bytes moe_expert_ffn needs for T tokens on `path`. */
+size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path);
+
+/* Expert FFN over the batch-union: for every active expert e and each of its
+ * grouped positions p in [offsets[e], offsets[e+1]), with token
+ * t = perm[p] / top_k,
+ *   y[p] = W_down_e ( silu(W_gate_e x[t]) * (W_up_e x[t]) ),  silu(z) = z/(1+e^-z)
+ * with every weight dequantised from int4 as q * s (group 64 along the input
+ * dimension); and for the shared expert (if shape->f_shared) and every token,
+ *   y_shared[t] = the same SwiGLU with the shared block
+ * (pages: zhichai.net, MoE sparsity and three-tier sections -- 8 routed + 1
+ * shared expert active per layer, int4 experts; the SwiGLU form is not on
+ * the pages and is this library's reading).
+ *  x         [T][d]; DECODE: bf16 or f32; PREFILL: bf16 only
+ *  experts   E blocks of moe_expert_bytes(d, f, group) bytes, back to back,
+ *            16-byte aligned
+ *  shared    one block, or NULL iff shape->f_shared == 0
+ *  offsets, perm, active, n_active: moe_union's outputs for this batch
+ *  y         out [T*top_k][d], grouped order; float32 (DECODE) or bf16
+ *            (PREFILL); rows of unused positions are not written
+ *  y_shared  out [T][d] same dtype, or NULL iff no shared expert
+ *  workspace >= moe_ffn_workspace_bytes(shape, T, path), 256-byte aligned */
+moe_status moe_expert_ffn(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
+                          const uint8_t* experts, const uint8_t* shared,
+                          const int32_t* offsets, const int32_t* perm, const int32_t* active,
+                          const int32_t* n_active, moe_path path, void* y, void* y_shared,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gate-weighted combine:
+ *   out[t] = sum_{j < top_k} topk_w[t][j] * y[inv_perm[t*top_k + j]] + y_shared[t]
+ * summed in j order in float32, no atomics (pages: zhichai.net, MoE
+ * sparsity section -- 8 routed experts plus the "+1" shared expert; weights
+ * on the shared expert are not on the pages: it is added with weight 1).
+ *  y         [T*top_k][d] (y_dt), grouped order, from moe_expert_ffn
+ *  y_shared  [T][d] (y_dt) or NULL for none
+ *  inv_perm  [T*top_k] from moe_union
+ *  topk_w    [T][top_k] from moe_route
+ *  out       out [T][d], out_dt (f32 or bf16, round to nearest even)
+ * y, y_shared and out must be 16-byte aligned. */
+moe_status moe_combine(const moe_shape* shape, int32_t T, const void* y, const void* y_shared,
+                       moe_dtype y_dt, const int32_t* inv_perm, const float* topk_w, void* out,
+                       moe_dtype out_dt, void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_str(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_INT4_H */

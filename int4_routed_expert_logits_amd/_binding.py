@@ -1,0 +1,182 @@
+"""ctypes binding of libmoe_int4.so: one Python function per C entry point,
+with the same name.  Argument marshalling only -- every step of the layer
+runs in the library's HIP kernels.  PyTorch supplies device memory and the
+current HIP stream.
+
+Loading fails loudly when the library has not been built; there is no other
+implementation behind these functions.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_int32, c_size_t, c_void_p, POINTER
+
+LIB_NAME = "libmoe_int4.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN = 0, 1, 2, 3, 4
+MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 5, 6, 7
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
+                4: "MOE_ERR_ALIGN", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_WORKSPACE",
+                7: "MOE_ERR_HIP"}
+MOE_F32, MOE_BF16 = 0, 1
+MOE_PATH_DECODE_F32, MOE_PATH_PREFILL_BF16 = 0, 1
+
+# every function include/moe_int4.h declares
+EXPORTS = ("moe_expert_bytes", "moe_route_workspace_bytes", "moe_route", "moe_union",
+           "moe_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_status_str")
+
+
+class Shape(ctypes.Structure):
+    """moe_shape: d, f, n_experts, top_k, group, f_shared (all int32)."""
+    _fields_ = [("d", c_int32), ("f", c_int32), ("n_experts", c_int32), ("top_k", c_int32),
+                ("group", c_int32), ("f_shared", c_int32)]
+
+    def __repr__(self):
+        return (f"Shape(d={self.d}, f={self.f}, n_experts={self.n_experts}, top_k={self.top_k}, "
+                f"group={self.group}, f_shared={self.f_shared})")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)} ({_status_text(status)})")
+
+
+_lib = None
+
+
+def load():
+    """Load the shared library (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m int4_routed_expert_logits_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sp = POINTER(Shape)
+    lib.moe_expert_bytes.argtypes = [c_int32, c_int32, c_int32]
+    lib.moe_expert_bytes.restype = c_size_t
+    lib.moe_route_workspace_bytes.argtypes = [sp, c_int32]
+    lib.moe_route_workspace_bytes.restype = c_size_t
+    lib.moe_ffn_workspace_bytes.argtypes = [sp, c_int32, c_int32]
+    lib.moe_ffn_workspace_bytes.restype = c_size_t
+    lib.moe_route.argtypes = [sp, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.moe_route.restype = c_int32
+    lib.moe_union.argtypes = [sp, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_void_p]
+    lib.moe_union.restype = c_int32
+    lib.moe_expert_ffn.argtypes = [sp, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                   c_void_p, c_size_t, c_void_p]
+    lib.moe_expert_ffn.restype = c_int32
+    lib.moe_combine.argtypes = [sp, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                c_void_p, c_int32, c_void_p]
+    lib.moe_combine.restype = c_int32
+    lib.moe_status_str.argtypes = [c_int32]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return load().moe_status_str(status).decode()
+    except Exception:  # pragma: no cover - only when the library itself is missing
+        return "?"
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+
+def _ptr(t):
+    """Device address of a tensor (None -> NULL).  Raw integers pass through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _shape(shape):
+    if isinstance(shape, Shape):
+        return shape
+    return Shape(*shape)
+
+
+# ----------------------------------------------------------------------------
+# the C entry points, one to one
+# ----------------------------------------------------------------------------
+
+def moe_expert_bytes(d: int, f: int, group: int = 64) -> int:
+    return load().moe_expert_bytes(d, f, group)
+
+
+def moe_route_workspace_bytes(shape, T: int) -> int:
+    return load().moe_route_workspace_bytes(ctypes.byref(_shape(shape)), T)
+
+
+def moe_ffn_workspace_bytes(shape, T: int, path: int) -> int:
+    return load().moe_ffn_workspace_bytes(ctypes.byref(_shape(shape)), T, path)
+
+
+def moe_status_str(status: int) -> str:
+    return load().moe_status_str(status).decode()
+
+
+def moe_route(shape, x, w_router, bias, topk_idx, topk_w, workspace, stream=None):
+    """x [T, d] bf16/f32; writes topk_idx [T, k] int32 and topk_w [T, k] f32."""
+    sh = _shape(shape)
+    _check("moe_route", load().moe_route(
+        ctypes.byref(sh), x.shape[0], _ptr(x), _dtype(x), _ptr(w_router), _ptr(bias),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def moe_union(shape, T, topk_idx, counts, offsets, perm, inv_perm, active, n_active, stream=None):
+    sh = _shape(shape)
+    _check("moe_union", load().moe_union(
+        ctypes.byref(sh), T, _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
+        _ptr(inv_perm), _ptr(active), _ptr(n_active), _stream(stream)))
+
+
+def moe_expert_ffn(shape, x, experts, shared, offsets, perm, active, n_active, path, y, y_shared,
+                   workspace, stream=None):
+    sh = _shape(shape)
+    _check("moe_expert_ffn", load().moe_expert_ffn(
+        ctypes.byref(sh), x.shape[0], _ptr(x), _dtype(x), _ptr(experts), _ptr(shared),
+        _ptr(offsets), _ptr(perm), _ptr(active), _ptr(n_active), path, _ptr(y), _ptr(y_shared),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_combine(shape, y, y_shared, inv_perm, topk_w, out, stream=None):
+    sh = _shape(shape)
+    _check("moe_combine", load().moe_combine(
+        ctypes.byref(sh), out.shape[0], _ptr(y), _ptr(y_shared), _dtype(y), _ptr(inv_perm),
+        _ptr(topk_w), _ptr(out), _dtype(out), _stream(stream)))

@@ -1,0 +1,191 @@
+// C ABI of the library (declared in include/moe_int4.h).  Every argument is
+// checked here, on the host, before anything is enqueued; the checks use no
+// HIP call, so every error path is exercised without a GPU.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "moe_int4.h"
+
+namespace {
+
+constexpr int kMaxDim = 8192;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int64_t kMaxSlots = int64_t(1) << 24;  // T * top_k
+constexpr size_t kWorkspaceAlign = 256;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t n) { return (n + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign; }
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_NULL;
+  if (s->d <= 0 || s->f <= 0 || s->n_experts <= 0 || s->top_k <= 0 || s->group <= 0 ||
+      s->f_shared < 0)
+    return MOE_ERR_SHAPE;
+  if (s->group != 64) return MOE_ERR_UNSUPPORTED;
+  if (s->d % 64 != 0 || s->f % 64 != 0) return MOE_ERR_SHAPE;
+  if (s->d > kMaxDim || s->f > kMaxDim) return MOE_ERR_UNSUPPORTED;
+  if (s->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (s->top_k > s->n_experts) return MOE_ERR_SHAPE;
+  if (s->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (s->f_shared != 0 && s->f_shared != s->f) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_tokens(const moe_shape* s, int32_t T) {
+  if (T < 0) return MOE_ERR_SHAPE;
+  if (static_cast<int64_t>(T) * s->top_k > kMaxSlots) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
+  return MOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group) {
+  if (group != 64 || d <= 0 || f <= 0 || d % 64 || f % 64) return 0;
+  const size_t n = 3ull * static_cast<size_t>(d) * static_cast<size_t>(f);
+  return n / 2 + n / group * 2;
+}
+
+size_t moe_route_workspace_bytes(const moe_shape* shape, int32_t T) {
+  if (check_shape(shape) != MOE_OK || T < 0) return 0;
+  return round_up(static_cast<size_t>(T) * shape->n_experts * sizeof(double));
+}
+
+moe_status moe_route(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
+                     const float* w_router, const float* bias, int32_t* topk_idx,
+                     float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(shape, T)) != MOE_OK) return st;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_w || !workspace) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(workspace, kWorkspaceAlign) ||
+      !aligned(topk_idx, 4) || !aligned(topk_w, 4) || (bias && !aligned(bias, 4)))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_route_workspace_bytes(shape, T)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_route(T, shape->d, shape->n_experts, shape->top_k, x,
+                                      x_dt == MOE_BF16, w_router, bias,
+                                      static_cast<double*>(workspace), topk_idx, topk_w,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_union(const moe_shape* shape, int32_t T, const int32_t* topk_idx,
+                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                     int32_t* active, int32_t* n_active, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(shape, T)) != MOE_OK) return st;
+  if (!counts || !offsets || !active || !n_active) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_idx || !perm || !inv_perm)) return MOE_ERR_NULL;
+  if (!aligned(counts, 4) || !aligned(offsets, 4) || !aligned(active, 4) ||
+      !aligned(n_active, 4) || (T > 0 && (!aligned(topk_idx, 4) || !aligned(perm, 4) ||
+                                          !aligned(inv_perm, 4))))
+    return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_union(T * shape->top_k, shape->n_experts, topk_idx, counts,
+                                      offsets, perm, inv_perm, active, n_active,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path) {
+  if (check_shape(shape) != MOE_OK || T < 0) return 0;
+  const bool sh = shape->f_shared != 0;
+  if (path == MOE_PATH_DECODE_F32)
+    return round_up(moe::ffn_decode_workspace(T, shape->top_k, shape->f, sh));
+  if (path == MOE_PATH_PREFILL_BF16)
+    return round_up(moe::ffn_prefill_workspace(T, shape->top_k, shape->f, sh));
+  return 0;
+}
+
+moe_status moe_expert_ffn(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
+                          const uint8_t* experts, const uint8_t* shared,
+                          const int32_t* offsets, const int32_t* perm, const int32_t* active,
+                          const int32_t* n_active, moe_path path, void* y, void* y_shared,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(shape, T)) != MOE_OK) return st;
+  if (path != MOE_PATH_DECODE_F32 && path != MOE_PATH_PREFILL_BF16) return MOE_ERR_UNSUPPORTED;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (path == MOE_PATH_PREFILL_BF16 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
+  const bool has_shared = shape->f_shared != 0;
+  if (T == 0) return MOE_OK;
+  if (!x || !experts || !offsets || !perm || !active || !n_active || !y || !workspace)
+    return MOE_ERR_NULL;
+  if (has_shared != (shared != nullptr) || has_shared != (y_shared != nullptr))
+    return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(experts, 16) || (shared && !aligned(shared, 16)) ||
+      !aligned(y, 16) || (y_shared && !aligned(y_shared, 16)) ||
+      !aligned(workspace, kWorkspaceAlign) || !aligned(offsets, 4) || !aligned(perm, 4) ||
+      !aligned(active, 4) || !aligned(n_active, 4))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_ffn_workspace_bytes(shape, T, path)) return MOE_ERR_WORKSPACE;
+  moe::FfnProblem p{};
+  p.T = T;
+  p.d = shape->d;
+  p.f = shape->f;
+  p.E = shape->n_experts;
+  p.k = shape->top_k;
+  p.has_shared = has_shared;
+  p.x_bf16 = x_dt == MOE_BF16;
+  p.block_bytes = moe_expert_bytes(shape->d, shape->f, shape->group);
+  p.x = x;
+  p.experts = experts;
+  p.shared = shared;
+  p.offsets = offsets;
+  p.perm = perm;
+  p.active = active;
+  p.n_active = n_active;
+  p.y = y;
+  p.y_shared = y_shared;
+  p.workspace = workspace;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(path == MOE_PATH_DECODE_F32 ? moe::launch_ffn_decode(p, s)
+                                                : moe::launch_ffn_prefill(p, s));
+}
+
+moe_status moe_combine(const moe_shape* shape, int32_t T, const void* y, const void* y_shared,
+                       moe_dtype y_dt, const int32_t* inv_perm, const float* topk_w, void* out,
+                       moe_dtype out_dt, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(shape, T)) != MOE_OK) return st;
+  if ((y_dt != MOE_F32 && y_dt != MOE_BF16) || (out_dt != MOE_F32 && out_dt != MOE_BF16))
+    return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (!y || !inv_perm || !topk_w || !out) return MOE_ERR_NULL;
+  if ((shape->f_shared != 0) != (y_shared != nullptr)) return MOE_ERR_NULL;
+  if (!aligned(y, 16) || (y_shared && !aligned(y_shared, 16)) || !aligned(out, 16) ||
+      !aligned(inv_perm, 4) || !aligned(topk_w, 4))
+    return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_combine(T, shape->d, shape->top_k, y, y_shared,
+                                        y_dt == MOE_BF16, inv_perm, topk_w, out,
+                                        out_dt == MOE_BF16, static_cast<hipStream_t>(stream)));
+}
+
+const char* moe_status_str(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or sizes disagree";
+    case MOE_ERR_DTYPE: return "dtype not allowed for this call or path";
+    case MOE_ERR_ALIGN: return "a pointer is not aligned as documented";
+    case MOE_ERR_UNSUPPORTED: return "well-formed request this library does not provide";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "a HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal host-side launchers, one per kernel family.  Arguments have been
+// validated by the C-ABI layer (api.cpp) before any of these is called; each
+// returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace moe {
+
+// Launch through hipLaunchKernel so the launch status comes back directly,
+// without touching the thread's sticky last-error state.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                  hipStream_t stream, Args&&... args) {
+  std::tuple<KArgs...> held(static_cast<KArgs>(std::forward<Args>(args))...);
+  return std::apply(
+      [&](auto&... a) {
+        void* ptrs[] = {static_cast<void*>(&a)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem,
+                               stream);
+      },
+      held);
+}
+
+// route.hip: float64 logits then top-k + renormalised softmax.
+hipError_t launch_route(int T, int d, int E, int k, const void* x, bool x_bf16,
+                        const float* w_router, const float* bias, double* logits,
+                        int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+// union.hip: batch-union grouping in one workgroup.
+hipError_t launch_union(int n_slots, int E, const int32_t* topk_idx, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* active,
+                        int32_t* n_active, hipStream_t stream);
+
+struct FfnProblem {
+  int T, d, f, E, k;
+  bool has_shared;
+  bool x_bf16;
+  size_t block_bytes;
+  const void* x;
+  const uint8_t* experts;
+  const uint8_t* shared;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* active;
+  const int32_t* n_active;
+  void* y;
+  void* y_shared;
+  void* workspace;
+};
+
+// ffn_decode.hip: int4 GEMV, float32 intermediate and outputs.
+size_t ffn_decode_workspace(int T, int k, int f, bool has_shared);
+hipError_t launch_ffn_decode(const FfnProblem& p, hipStream_t stream);
+
+// ffn_prefill.hip: grouped GEMM on bf16 MFMA, bf16 intermediate and outputs.
+size_t ffn_prefill_workspace(int T, int k, int f, bool has_shared);
+hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream);
+
+// combine.hip
+hipError_t launch_combine(int T, int d, int k, const void* y, const void* y_shared, bool y_bf16,
+                          const int32_t* inv_perm, const float* topk_w, void* out,
+                          bool out_bf16, hipStream_t stream);
+
+}  // namespace moe

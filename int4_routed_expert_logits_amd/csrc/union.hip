@@ -1,0 +1,145 @@
+// Batch-union grouping (pages: yunpan.plus article, "capability 2" -- an
+// expert needed by several positions of one batch is read once; "capability
+// 3" -- a worker receives one layer's routed batch-union and runs the FFN).
+//
+// One workgroup of 512 threads does the whole grouping in LDS: a histogram of
+// the T*k routing slots per expert, an exclusive scan into offsets, the
+// active-expert list, then a stable counting sort of the slots.  Slots are
+// taken in chunks of 512 in id order; inside a chunk each wavefront ranks its
+// lanes among equal keys with ballots, and wavefronts are ordered by a
+// per-chunk table of per-wave key counts, so the permutation is the stable
+// one regardless of the order in which hardware atomics land.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxE = 1024;
+
+// Exclusive scan of n <= 1024 ints in LDS (in place), returns the total.
+__device__ int block_exclusive_scan(int* a, int n, int* tmp) {
+  // each thread owns two consecutive entries
+  const int tid = threadIdx.x;
+  const int i0 = 2 * tid, i1 = 2 * tid + 1;
+  const int v0 = i0 < n ? a[i0] : 0;
+  const int v1 = i1 < n ? a[i1] : 0;
+  int s = v0 + v1;
+  // inclusive scan of s over the 512 threads: wave scan then wave totals
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = s;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) tmp[wv] = incl;
+  __syncthreads();
+  int wave_base = 0;
+  for (int w = 0; w < wv; ++w) wave_base += tmp[w];
+  int total = 0;
+  for (int w = 0; w < kWaves; ++w) total += tmp[w];
+  const int excl = wave_base + incl - s;
+  __syncthreads();
+  if (i0 < n) a[i0] = excl;
+  if (i1 < n) a[i1] = excl + v0;
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kThreads) void batch_union(const int32_t* __restrict__ topk_idx,
+                                                        int n, int E, int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ perm,
+                                                        int32_t* __restrict__ inv_perm,
+                                                        int32_t* __restrict__ active,
+                                                        int32_t* __restrict__ n_active) {
+  __shared__ int cnt[kMaxE];
+  __shared__ int start[kMaxE];    // next free grouped position per expert
+  __shared__ int flag[kMaxE];
+  __shared__ int wave_cnt[kWaves][kMaxE];
+  __shared__ int scan_tmp[kWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+
+  for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
+  for (int i = tid; i < kWaves * kMaxE; i += kThreads) (&wave_cnt[0][0])[i] = 0;
+  __syncthreads();
+  for (int s = tid; s < n; s += kThreads) {
+    const int e = topk_idx[s];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    counts[e] = cnt[e];
+    start[e] = cnt[e];
+    flag[e] = cnt[e] > 0 ? 1 : 0;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(start, E, scan_tmp);
+  const int n_act = block_exclusive_scan(flag, E, scan_tmp);
+  for (int e = tid; e < E; e += kThreads) {
+    offsets[e] = start[e];
+    if (cnt[e] > 0) active[flag[e]] = e;
+  }
+  for (int i = n_act + tid; i < E; i += kThreads) active[i] = -1;
+  if (tid == 0) {
+    offsets[E] = total;
+    n_active[0] = n_act;
+  }
+  __syncthreads();
+
+  // Stable placement, one chunk of kThreads slots at a time.
+  for (int c0 = 0; c0 < n; c0 += kThreads) {
+    const int s = c0 + tid;
+    int e = s < n ? topk_idx[s] : -1;
+    const bool valid = e >= 0 && e < E;
+    if (!valid) e = -1;
+    int rank = 0;
+    // rank among lower lanes of this wave with the same key
+    uint64_t pending = __ballot(valid);
+    const uint64_t lower = (1ull << lane) - 1ull;
+    while (pending) {
+      const int leader = __ffsll(static_cast<unsigned long long>(pending)) - 1;
+      const int key = __shfl(e, leader, 64);
+      const uint64_t same = __ballot(valid && e == key);
+      if (valid && e == key) rank = __popcll(same & lower);
+      if (lane == leader) wave_cnt[wv][key] = __popcll(same);
+      pending &= ~same;
+    }
+    __syncthreads();
+    if (s < n) {
+      if (valid) {
+        int pos = start[e] + rank;
+        for (int w = 0; w < wv; ++w) pos += wave_cnt[w][e];
+        perm[pos] = s;
+        inv_perm[s] = pos;
+      } else {
+        inv_perm[s] = -1;
+      }
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kThreads) {
+      int add = 0;
+      for (int w = 0; w < kWaves; ++w) {
+        add += wave_cnt[w][ee];
+        wave_cnt[w][ee] = 0;
+      }
+      start[ee] += add;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_union(int n_slots, int E, const int32_t* topk_idx, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* active,
+                        int32_t* n_active, hipStream_t stream) {
+  return launch(batch_union, dim3(1), dim3(kThreads), 0, stream, topk_idx, n_slots, E, counts,
+                offsets, perm, inv_perm, active, n_active);
+}
+
+}  // namespace moe

@@ -1,0 +1,160 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/moe_int4.h declares,
+and reject malformed calls before enqueueing anything.  Every call below has
+at least one defect, so none of them reaches a kernel launch: they are safe on
+a machine with or without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_routed_expert_logits_amd as moe
+from int4_routed_expert_logits_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_int4.h")
+
+P = 1 << 20          # a 256-byte aligned stand-in address (never dereferenced)
+MIS = P + 4          # misaligned for 16-byte checks
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(lib):
+    decl = declared_functions()
+    assert decl == sorted(B.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+    # and nothing declared is missing from the dynamic symbol table
+    handle = ctypes.CDLL(moe.LIB_PATH)
+    for name in decl:
+        assert ctypes.cast(getattr(handle, name), ctypes.c_void_p).value
+
+
+def shp(d=512, f=256, E=8, k=2, group=64, fs=0):
+    return B.Shape(d, f, E, k, group, fs)
+
+
+def test_expert_bytes(lib):
+    assert lib.moe_expert_bytes(6144, 2048, 64) == 20_054_016
+    assert lib.moe_expert_bytes(512, 256, 64) == 208_896
+    assert lib.moe_expert_bytes(2048, 1024, 64) == 3_342_336
+    assert lib.moe_expert_bytes(2048, 512, 64) == 1_671_168
+    assert lib.moe_expert_bytes(6144, 2048, 32) == 0
+    assert lib.moe_expert_bytes(100, 2048, 64) == 0
+
+
+def test_workspace_sizes(lib):
+    s = shp(6144, 2048, 256, 8, 64, 2048)
+    assert moe.moe_route_workspace_bytes(s, 2048) == 2048 * 256 * 8
+    assert moe.moe_ffn_workspace_bytes(s, 1, moe.MOE_PATH_DECODE_F32) >= (8 + 1) * 2048 * 4
+    assert moe.moe_ffn_workspace_bytes(s, 2048, moe.MOE_PATH_PREFILL_BF16) >= 2048 * 9 * 2048 * 2
+    for v in (moe.moe_route_workspace_bytes(s, 3), moe.moe_ffn_workspace_bytes(s, 3, 0)):
+        assert v % 256 == 0
+    assert moe.moe_route_workspace_bytes(shp(group=32), 4) == 0
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert moe.moe_status_str(code)
+    assert moe.moe_status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("shape,status", [
+    (shp(d=0), B.MOE_ERR_SHAPE), (shp(d=96), B.MOE_ERR_SHAPE), (shp(f=-64), B.MOE_ERR_SHAPE),
+    (shp(group=32), B.MOE_ERR_UNSUPPORTED), (shp(d=16384), B.MOE_ERR_UNSUPPORTED),
+    (shp(E=2048, k=8), B.MOE_ERR_UNSUPPORTED), (shp(E=4, k=5), B.MOE_ERR_SHAPE),
+    (shp(E=64, k=33), B.MOE_ERR_UNSUPPORTED), (shp(fs=128), B.MOE_ERR_UNSUPPORTED),
+    (shp(k=0), B.MOE_ERR_SHAPE),
+])
+def test_bad_shapes_are_rejected_by_every_call(lib, shape, status):
+    s = ctypes.byref(shape)
+    assert lib.moe_route(s, 4, P, 0, P, None, P, P, P, 1 << 20, None) == status
+    assert lib.moe_union(s, 4, P, P, P, P, P, P, P, None) == status
+    assert lib.moe_expert_ffn(s, 4, P, 0, P, None, P, P, P, P, 0, P, None, P, 1 << 30, None) == status
+    assert lib.moe_combine(s, 4, P, None, 0, P, P, P, 0, None) == status
+
+
+def test_null_shape(lib):
+    assert lib.moe_route(None, 4, P, 0, P, None, P, P, P, 1 << 20, None) == B.MOE_ERR_NULL
+
+
+def test_route_argument_checks(lib):
+    s = ctypes.byref(shp())
+    ws = 4 * 8 * 8
+    assert lib.moe_route(s, -1, P, 0, P, None, P, P, P, ws, None) == B.MOE_ERR_SHAPE
+    assert lib.moe_route(s, 4, P, 7, P, None, P, P, P, ws, None) == B.MOE_ERR_DTYPE
+    assert lib.moe_route(s, 4, None, 0, P, None, P, P, P, ws, None) == B.MOE_ERR_NULL
+    assert lib.moe_route(s, 4, P, 0, None, None, P, P, P, ws, None) == B.MOE_ERR_NULL
+    assert lib.moe_route(s, 4, P, 0, P, None, P, P, None, ws, None) == B.MOE_ERR_NULL
+    assert lib.moe_route(s, 4, MIS, 0, P, None, P, P, P, ws, None) == B.MOE_ERR_ALIGN
+    assert lib.moe_route(s, 4, P, 0, P, None, P, P, P + 16, ws, None) == B.MOE_ERR_ALIGN
+    assert lib.moe_route(s, 4, P, 0, P, None, P, P, P, ws - 1, None) == B.MOE_ERR_WORKSPACE
+    # an empty batch is a no-op
+    assert lib.moe_route(s, 0, None, 0, None, None, None, None, None, 0, None) == B.MOE_OK
+
+
+def test_union_argument_checks(lib):
+    s = ctypes.byref(shp())
+    assert lib.moe_union(s, 4, None, P, P, P, P, P, P, None) == B.MOE_ERR_NULL
+    assert lib.moe_union(s, 4, P, None, P, P, P, P, P, None) == B.MOE_ERR_NULL
+    assert lib.moe_union(s, 4, P, P, P, P, P, P, None, None) == B.MOE_ERR_NULL
+    assert lib.moe_union(s, 4, P + 2, P, P, P, P, P, P, None) == B.MOE_ERR_ALIGN
+    assert lib.moe_union(s, -3, P, P, P, P, P, P, P, None) == B.MOE_ERR_SHAPE
+    assert lib.moe_union(s, 1 << 24, P, P, P, P, P, P, P, None) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_ffn_argument_checks(lib):
+    s = ctypes.byref(shp())
+    big = 1 << 30
+    dec, pre = B.MOE_PATH_DECODE_F32, B.MOE_PATH_PREFILL_BF16
+    ok_args = dict(x=P, xdt=0, ex=P, sh=None, off=P, perm=P, act=P, na=P, path=dec, y=P, ys=None, ws=P, wsb=big)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return lib.moe_expert_ffn(s, 4, a["x"], a["xdt"], a["ex"], a["sh"], a["off"], a["perm"],
+                                  a["act"], a["na"], a["path"], a["y"], a["ys"], a["ws"], a["wsb"], None)
+    # f32 activations on the bf16 prefill path are rejected, never rounded
+    assert call(path=pre, xdt=0) == B.MOE_ERR_DTYPE
+    assert call(path=5) == B.MOE_ERR_UNSUPPORTED
+    assert call(xdt=3) == B.MOE_ERR_DTYPE
+    assert call(x=None) == B.MOE_ERR_NULL
+    assert call(ex=None) == B.MOE_ERR_NULL
+    assert call(na=None) == B.MOE_ERR_NULL
+    assert call(ws=None) == B.MOE_ERR_NULL
+    assert call(sh=P) == B.MOE_ERR_NULL            # shared block given but no shared expert
+    assert call(ex=MIS) == B.MOE_ERR_ALIGN
+    assert call(y=MIS) == B.MOE_ERR_ALIGN
+    assert call(ws=P + 64) == B.MOE_ERR_ALIGN
+    assert call(wsb=16) == B.MOE_ERR_WORKSPACE
+    s2 = ctypes.byref(shp(fs=256))
+    assert lib.moe_expert_ffn(s2, 4, P, 0, P, None, P, P, P, P, dec, P, P, P, big, None) == B.MOE_ERR_NULL
+    assert lib.moe_expert_ffn(s2, 4, P, 0, P, P, P, P, P, P, dec, P, None, P, big, None) == B.MOE_ERR_NULL
+    assert lib.moe_expert_ffn(s, 0, None, 0, None, None, None, None, None, None, dec, None, None, None, 0, None) == B.MOE_OK
+
+
+def test_combine_argument_checks(lib):
+    s = ctypes.byref(shp())
+    assert lib.moe_combine(s, 4, P, None, 2, P, P, P, 0, None) == B.MOE_ERR_DTYPE
+    assert lib.moe_combine(s, 4, P, None, 0, P, P, P, 9, None) == B.MOE_ERR_DTYPE
+    assert lib.moe_combine(s, 4, None, None, 0, P, P, P, 0, None) == B.MOE_ERR_NULL
+    assert lib.moe_combine(s, 4, P, P, 0, P, P, P, 0, None) == B.MOE_ERR_NULL   # y_shared without a shared expert
+    assert lib.moe_combine(s, 4, P, None, 0, P, P, MIS, 0, None) == B.MOE_ERR_ALIGN
+    assert lib.moe_combine(s, 0, None, None, 0, None, None, None, 0, None) == B.MOE_OK
+
+
+def test_binding_names_match_the_c_entry_points():
+    for name in B.EXPORTS:
+        assert callable(getattr(moe, name)), name
