@@ -1,0 +1,354 @@
+"""GPU parity: every step of the layer through the C ABI against the CPU
+oracle on the same seeded inputs.
+
+Routing indices and the batch-union grouping must match bit-exactly; gate
+weights within 1e-6; expert outputs and the layer output within
+2e-3 * rms(reference) on the float32 decode path.  Workloads run at their
+full sizes; where the oracle would need minutes (the 8-token decode batch of
+the ~19 MB-expert layer touches ~57 experts) it computes sampled tokens one
+by one instead.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import int4_routed_expert_logits_amd as moe
+from int4_routed_expert_logits_amd.layer import LayerBuffers, run_layer
+
+pytestmark = pytest.mark.gpu
+
+DEC = moe.MOE_PATH_DECODE_F32
+TOL_DECODE = 2e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# inputs on the device
+# ----------------------------------------------------------------------------
+
+_layers = {}
+
+
+def dev_layer(cfg, router_only=False):
+    key = (cfg, router_only)
+    if key not in _layers:
+        if not router_only:
+            for k in [k for k in _layers if not k[1]]:
+                del _layers[k]
+            torch.cuda.empty_cache()
+        L = synth.make_layer(cfg, experts=[] if router_only else None)
+        dev = dict(
+            w_router=torch.from_numpy(L.w_router).cuda(),
+            bias=None if L.bias is None else torch.from_numpy(L.bias).cuda(),
+            experts=None if router_only else torch.from_numpy(L.experts).cuda(),
+            shared=None if (router_only or L.shared is None) else torch.from_numpy(L.shared).cuda(),
+        )
+        _layers[key] = (L, dev)
+    return _layers[key]
+
+
+def dev_x(bits):
+    if bits.dtype == np.uint16:
+        return torch.from_numpy(bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+    return torch.from_numpy(bits.copy()).cuda()
+
+
+def tokens(cfg, T, batch=0):
+    bits, xf = synth.make_tokens(cfg, T, batch)
+    return dev_x(bits), xf
+
+
+def rel_err(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref))) / max(rms, 1e-300)
+
+
+def min_gap(logits, k):
+    s = -np.sort(-logits, axis=1)
+    return float(np.min(s[:, k - 1] - s[:, k])) if logits.shape[1] > k else float("inf")
+
+
+# ----------------------------------------------------------------------------
+# router
+# ----------------------------------------------------------------------------
+
+ROUTE_CASES = [(1, 4), (1, 3), (2, 1), (2, 16), (3, 64), (3, 5), (4, 1), (4, 8), (4, 33), (5, 2048)]
+
+
+@pytest.mark.parametrize("cfg,T", ROUTE_CASES)
+def test_route_parity(cfg, T):
+    say(f"route cfg={cfg} T={T}")
+    L, dev = dev_layer(cfg, router_only=True)
+    x, xf = tokens(cfg, T)
+    sh = moe.shape_of(L.shape)
+    k = sh.top_k
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_route_workspace_bytes(sh, T), dtype=torch.uint8, device="cuda")
+    moe.moe_route(sh, x, dev["w_router"], dev["bias"], idx, w, ws)
+    torch.cuda.synchronize()
+    ridx, rw, lg = oracle.route(xf, L.w_router, L.bias, k)
+    gap = min_gap(lg, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx), f"top-k differs (smallest k/k+1 logit gap {gap:.3e})"
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-6
+    # the gpu logits themselves (float64, summation order aside)
+    glg = ws[: T * sh.n_experts * 8].view(torch.float64).reshape(T, sh.n_experts).cpu().numpy()
+    assert np.max(np.abs(glg - lg)) <= 1e-12 * max(1.0, np.max(np.abs(lg)))
+
+
+def test_route_ties_go_to_lower_id():
+    say("route ties")
+    sh = moe.Shape(64, 64, 6, 3, 64, 0)
+    x = torch.zeros((2, 64), dtype=torch.float32, device="cuda")
+    wr = torch.zeros((6, 64), dtype=torch.float32, device="cuda")
+    b = torch.tensor([0.0, 1.0, 1.0, 0.5, 1.0, 1.0], device="cuda")
+    idx = torch.empty((2, 3), dtype=torch.int32, device="cuda")
+    w = torch.empty((2, 3), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_route_workspace_bytes(sh, 2), dtype=torch.uint8, device="cuda")
+    moe.moe_route(sh, x, wr, b, idx, w, ws)
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == [[1, 2, 4], [1, 2, 4]]
+    assert np.allclose(w.cpu().numpy(), 1.0 / 3.0, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------
+# batch-union
+# ----------------------------------------------------------------------------
+
+def run_union(topk, E):
+    T, k = topk.shape
+    sh = moe.Shape(64, 64, E, k, 64, 0)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    n = max(T * k, 1)
+    outs = dict(counts=torch.full((E,), -7, **i32), offsets=torch.full((E + 1,), -7, **i32),
+                perm=torch.full((n,), -7, **i32), inv_perm=torch.full((n,), -7, **i32),
+                active=torch.full((E,), -7, **i32), n_active=torch.full((1,), -7, **i32))
+    ti = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).cuda() if T else None
+    moe.moe_union(sh, T, ti, outs["counts"], outs["offsets"], outs["perm"], outs["inv_perm"],
+                  outs["active"], outs["n_active"])
+    torch.cuda.synchronize()
+    return {k_: v.cpu().numpy() for k_, v in outs.items()}
+
+
+def check_union(topk, E):
+    got = run_union(topk, E)
+    counts, offsets, perm, inv, active, n_active = oracle.batch_union(topk, E)
+    n = topk.size
+    assert np.array_equal(got["counts"], counts)
+    assert np.array_equal(got["offsets"], offsets)
+    assert np.array_equal(got["n_active"], n_active)
+    assert np.array_equal(got["active"], active)
+    g = int(offsets[E])
+    assert np.array_equal(got["perm"][:g], perm[:g])
+    assert np.array_equal(got["inv_perm"][:n], inv)
+
+
+@pytest.mark.parametrize("cfg,T", [(1, 4), (2, 16), (3, 64), (4, 8), (5, 2048)])
+def test_union_parity_on_workload_routing(cfg, T):
+    say(f"union cfg={cfg} T={T}")
+    L, _ = dev_layer(cfg, router_only=True)
+    _, xf = synth.make_tokens(cfg, T)
+    idx, _, _ = oracle.route(xf, L.w_router, L.bias, L.shape.top_k)
+    check_union(idx, L.shape.n_experts)
+
+
+@pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (1000, 1, 8, 1), (100, 32, 1024, 2),
+                                        (777, 8, 256, 3), (3000, 6, 40, 4), (513, 2, 3, 5)])
+def test_union_parity_random(T, k, E, seed):
+    say(f"union random T={T} k={k} E={E}")
+    rng = np.random.default_rng(seed)
+    topk = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    check_union(topk, E)
+
+
+def test_union_all_slots_to_one_expert():
+    say("union single expert")
+    check_union(np.full((4096, 1), 5, dtype=np.int32), 8)
+
+
+def test_union_skips_out_of_range_ids():
+    say("union invalid ids")
+    topk = np.array([[2, 9], [-1, 1], [2, 1], [3, 0]], dtype=np.int32)
+    check_union(topk, 4)
+
+
+def test_union_empty_batch():
+    say("union empty")
+    got = run_union(np.zeros((0, 4), dtype=np.int32), 16)
+    assert np.all(got["counts"] == 0) and np.all(got["offsets"] == 0)
+    assert got["n_active"][0] == 0 and np.all(got["active"] == -1)
+
+
+# ----------------------------------------------------------------------------
+# combine
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ybf16,obf16,shared", [(False, False, True), (False, False, False),
+                                               (True, True, True), (False, True, True)])
+def test_combine_parity(ybf16, obf16, shared):
+    say(f"combine ybf16={ybf16} obf16={obf16} shared={shared}")
+    rng = np.random.default_rng(11)
+    T, k, d, E = 37, 8, 640, 64
+    topk = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    _, _, _, inv, _, _ = oracle.batch_union(topk, E)
+    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    y = rng.standard_normal((T * k, d)).astype(np.float32)
+    ys = rng.standard_normal((T, d)).astype(np.float32) if shared else None
+    ydt = torch.bfloat16 if ybf16 else torch.float32
+    yd = torch.from_numpy(y).cuda().to(ydt)
+    ysd = torch.from_numpy(ys).cuda().to(ydt) if shared else None
+    out = torch.empty((T, d), dtype=torch.bfloat16 if obf16 else torch.float32, device="cuda")
+    sh = moe.Shape(d, 64, E, k, 64, 64 if shared else 0)
+    moe.moe_combine(sh, yd, ysd, torch.from_numpy(inv).cuda(), torch.from_numpy(w).cuda(), out)
+    torch.cuda.synchronize()
+    yr = yd.float().cpu().numpy()
+    ysr = ysd.float().cpu().numpy() if shared else None
+    ref = oracle.combine(yr, ysr, inv, w, k)
+    got = out.float().cpu().numpy()
+    if obf16:
+        # round-to-nearest bf16 output: within half an ulp, at most 2^-8 |v|
+        rms = np.sqrt(np.mean(ref ** 2))
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * rms)
+    else:
+        assert rel_err(got, ref) <= 1e-6
+
+
+# ----------------------------------------------------------------------------
+# whole layer, decode path
+# ----------------------------------------------------------------------------
+
+def gpu_layer(cfg, T, batch=0, path=DEC, experts_override=None):
+    L, dev = dev_layer(cfg)
+    x, xf = tokens(cfg, T, batch)
+    sh = moe.shape_of(L.shape)
+    buf = LayerBuffers.allocate(sh, T, path)
+    ex = dev["experts"] if experts_override is None else experts_override
+    run_layer(x, dev["w_router"], dev["bias"], ex, dev["shared"], buf)
+    torch.cuda.synchronize()
+    return L, xf, buf
+
+
+def oracle_sampled(L, xf, sample_tokens):
+    """Oracle routing and grouping for the whole batch, expert outputs and
+    layer outputs only for the sampled tokens (one expert at a time)."""
+    sh = L.shape
+    idx, w, lg = oracle.route(xf, L.w_router, L.bias, sh.top_k)
+    union = oracle.batch_union(idx, sh.n_experts)
+    inv = union[3]
+    cache = {}
+
+    def expert_rows(e, rows):
+        if e not in cache:
+            blk = L.shared if e == "shared" else L.experts[e]
+            cache[e] = oracle.expert_weights(blk, sh.d, sh.f)
+        return oracle.swiglu(np.asarray(xf[rows], dtype=np.float64), *cache[e])
+
+    y = {}
+    out = {}
+    for t in sample_tokens:
+        acc = np.zeros(sh.d)
+        for j in range(sh.top_k):
+            p = int(inv[t * sh.top_k + j])
+            y[p] = expert_rows(int(idx[t, j]), [t])[0]
+            acc += float(w[t, j]) * y[p]
+        ys = expert_rows("shared", [t])[0] if L.shared is not None else 0.0
+        out[t] = acc + ys
+    return dict(topk_idx=idx, topk_w=w, union=union, y=y, out=out, logits=lg)
+
+
+def check_routing_and_union(buf, ref_idx, ref_w, union):
+    counts, offsets, perm, inv, active, n_active = union
+    assert np.array_equal(buf.topk_idx.cpu().numpy(), ref_idx)
+    assert np.max(np.abs(buf.topk_w.cpu().numpy() - ref_w)) <= 1e-6
+    assert np.array_equal(buf.counts.cpu().numpy(), counts)
+    assert np.array_equal(buf.offsets.cpu().numpy(), offsets)
+    n = ref_idx.size
+    assert np.array_equal(buf.perm.cpu().numpy()[:n], perm)
+    assert np.array_equal(buf.inv_perm.cpu().numpy()[:n], inv)
+    assert np.array_equal(buf.active.cpu().numpy(), active)
+    assert np.array_equal(buf.n_active.cpu().numpy(), n_active)
+
+
+FULL_CASES = [(1, 4), (1, 3), (2, 1), (2, 16), (2, 5), (3, 64), (3, 13), (4, 1)]
+
+
+@pytest.mark.parametrize("cfg,T", FULL_CASES)
+def test_layer_decode_parity(cfg, T):
+    say(f"layer decode cfg={cfg} T={T}")
+    L, xf, buf = gpu_layer(cfg, T)
+    sh = L.shape
+    ref = oracle.moe_layer(xf, L.w_router, L.bias, L.experts, L.shared, sh.d, sh.f,
+                           sh.n_experts, sh.top_k)
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"],
+                            (ref["counts"], ref["offsets"], ref["perm"], ref["inv_perm"],
+                             ref["active"], ref["n_active"]))
+    ey = rel_err(buf.y.cpu().numpy()[: T * sh.top_k], ref["y"])
+    assert ey <= TOL_DECODE, f"y error {ey:.2e} rms"
+    if L.shared is not None:
+        es = rel_err(buf.y_shared.cpu().numpy()[:T], ref["y_shared"])
+        assert es <= TOL_DECODE, f"y_shared error {es:.2e} rms"
+    eo = rel_err(buf.out.cpu().numpy(), ref["out"])
+    assert eo <= TOL_DECODE, f"out error {eo:.2e} rms"
+
+
+def test_layer_decode_parity_19mb_layer_8_tokens_sampled():
+    say("layer decode cfg=4 T=8 (sampled)")
+    L, xf, buf = gpu_layer(4, 8)
+    ref = oracle_sampled(L, xf, [0, 5])
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"], ref["union"])
+    y = buf.y.cpu().numpy()
+    ys = np.stack(list(ref["y"].values()))
+    got = np.stack([y[p] for p in ref["y"]])
+    assert rel_err(got, ys) <= TOL_DECODE
+    out = buf.out.cpu().numpy()
+    ro = np.stack([ref["out"][t] for t in sorted(ref["out"])])
+    assert rel_err(out[sorted(ref["out"])], ro) <= TOL_DECODE
+
+
+def test_decode_is_deterministic_and_batch_invariant():
+    say("decode determinism / batch invariance")
+    L, xf, buf1 = gpu_layer(2, 16)
+    out1 = buf1.out.cpu().numpy().copy()
+    _, _, buf2 = gpu_layer(2, 16)
+    assert np.array_equal(out1, buf2.out.cpu().numpy())
+    # each token alone gives bitwise the same row as inside the batch
+    Ld, dev = dev_layer(2)
+    bits, _ = synth.make_tokens(2, 16)
+    sh = moe.shape_of(Ld.shape)
+    for t in (0, 7, 15):
+        b1 = LayerBuffers.allocate(sh, 1, DEC)
+        run_layer(dev_x(bits[t:t + 1]), dev["w_router"], dev["bias"], dev["experts"], dev["shared"], b1)
+        torch.cuda.synchronize()
+        assert np.array_equal(b1.out.cpu().numpy()[0], out1[t])
+
+
+def test_doubling_down_scales_doubles_y():
+    say("down-scale doubling")
+    L, dev = dev_layer(1)
+    sh = L.shape
+    blocks = L.experts.copy()
+    sd = 3 * sh.d * sh.f // 2 + 2 * sh.f * (sh.d // 64) * 2
+    for e in range(sh.n_experts):
+        s = blocks[e, sd:].view(np.float16)
+        s *= np.float16(2.0)
+    _, _, b1 = gpu_layer(1, 4)
+    y1 = b1.y.cpu().numpy().copy()
+    _, _, b2 = gpu_layer(1, 4, experts_override=torch.from_numpy(blocks).cuda())
+    assert np.array_equal(b2.y.cpu().numpy(), 2.0 * y1)
+
+
+def test_empty_batch_is_a_no_op():
+    say("empty batch")
+    L, dev = dev_layer(1)
+    sh = moe.shape_of(L.shape)
+    buf = LayerBuffers.allocate(sh, 0, DEC)
+    run_layer(torch.empty((0, sh.d), dtype=torch.float32, device="cuda"), dev["w_router"],
+              dev["bias"], dev["experts"], dev["shared"], buf)
+    torch.cuda.synchronize()
+    assert int(buf.n_active.item()) == 0
