@@ -1,0 +1,319 @@
+"""Benchmark of the int4 routed-expert MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-graph]
+                    [--no-prefill] [--no-cpu-baseline]
+
+A step is one pass of the whole layer -- route, batch-union, expert FFN,
+combine -- over one batch of synthetic tokens, with every input already
+resident in HBM.  The headline is the 1-token decode step of the layer shaped
+like the pages' GLM-5.2 layer (d=6144, f=2048, 256 routed experts top-8 plus
+one shared expert, int4 gs64 with fp16 scales; every expert a 20,054,016-byte
+block): effective expert-weight GB/s = (active experts + shared) * block bytes
+per step / step time.  Consecutive steps run on different copies of the layer
+(``--layers``, default 8, ~41 GB of HBM) and different token batches, the way
+consecutive layers of a model follow each other, so no step finds the
+previous step's experts in the 256 MB Infinity Cache.
+
+The same run also reports the 2048-token prefill step of that layer (Zipf
+router bias, bf16 MFMA path) as tokens/s, the roofline of the dominant
+kernel (the expert FFN: HBM bytes for decode), timed with HIP events on the
+launch stream, and the CPU oracle timed on a bounded sample on the host cores.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+METRIC = "decode int4 expert GB/s (% HBM peak); prefill tokens/s per MoE layer"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--layers", type=int, default=8, help="layer copies rotated in HBM")
+    ap.add_argument("--tokens", type=int, default=1, help="decode batch (1 or 8)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graphs")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(one MI355X per process, no collectives); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import int4_routed_expert_logits_amd as moe
+    from int4_routed_expert_logits_amd.layer import LayerBuffers, run_layer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    moe.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------------ data
+    t0 = time.time()
+    L = synth.make_layer(4)
+    sh = moe.shape_of(L.shape)
+    bb = L.expert_bytes
+    # canonical blocks -> packed blocks (the one-time conversion), on the GPU
+    src = torch.from_numpy(L.experts).to(dev)
+    experts = [torch.empty_like(src)]
+    moe.moe_pack_experts(sh, L.shape.n_experts, src, experts[0])
+    del src
+    src = torch.from_numpy(L.shared[None]).to(dev)
+    shared = [torch.empty_like(src)[0]]
+    moe.moe_pack_experts(sh, 1, src, shared[0])
+    del src
+    for _ in range(1, args.layers):
+        experts.append(experts[0].clone())
+        shared.append(shared[0].clone())
+    w_router = torch.from_numpy(L.w_router).to(dev)
+    T = args.tokens
+    nb = args.layers
+    xs = []
+    for b in range(nb):
+        bits, _ = synth.make_tokens(4, T, batch=b)
+        xs.append(torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    log(f"decode data ready in {time.time() - t0:.1f}s: {args.layers} layer copies x "
+        f"{experts[0].numel() / 1e9:.2f} GB, {nb} token batches of {T}")
+
+    DEC = moe.MOE_PATH_DECODE_F32
+    bufs = [LayerBuffers.allocate(sh, T, DEC) for _ in range(nb)]
+
+    def step(i):
+        j = i % nb
+        run_layer(xs[j], w_router, None, experts[j % args.layers], shared[j % args.layers], bufs[j])
+
+    # --------------------------------------------------- per-kernel timing (events)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n_kt = max(args.steps, 2 * nb)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_kt)]
+    for i in range(n_kt):
+        j = i % nb
+        b = bufs[j]
+        moe.moe_route(sh, xs[j], w_router, None, b.topk_idx, b.topk_w, b.workspace)
+        moe.moe_union(sh, T, b.topk_idx, b.counts, b.offsets, b.perm, b.inv_perm, b.active, b.n_active)
+        ev[i][0].record(stream)
+        moe.moe_expert_ffn(sh, xs[j], experts[j % args.layers], shared[j % args.layers], b.offsets,
+                           b.perm, b.active, b.n_active, DEC, b.y, b.y_shared, b.ffn_workspace)
+        ev[i][1].record(stream)
+        moe.moe_combine(sh, b.y, b.y_shared, b.inv_perm, b.topk_w, b.out)
+    torch.cuda.synchronize()
+    ffn_ms = np.array([s.elapsed_time(e) for s, e in ev])
+    active_per_batch = [int(b.n_active.item()) for b in bufs]
+    bytes_per_batch = [(a + 1) * bb for a in active_per_batch]
+    ffn_bytes = np.array([bytes_per_batch[i % nb] for i in range(n_kt)], dtype=np.float64)
+    kern_gbps = float(np.sum(ffn_bytes) / (np.sum(ffn_ms) * 1e-3) / 1e9)
+    log(f"expert FFN kernel: mean {ffn_ms.mean() * 1e3:.1f} us, median {np.median(ffn_ms) * 1e3:.1f} us, "
+        f"{kern_gbps:.0f} GB/s over {n_kt} launches")
+
+    # --------------------------------------------------------- timed region
+    steps = args.steps
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            for i in range(nb):       # warm the capture stream
+                step(i)
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(nb):
+                step(i)
+        reps = max(1, (steps + nb - 1) // nb)
+        steps = reps * nb
+        for _ in range(max(1, args.warmup // nb)):
+            graph.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+    else:
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / steps
+    step_bytes = float(np.mean(bytes_per_batch))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"decode step: {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s ({'graph' if graph else 'eager'})")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"decode, {T} token(s) per step, layer d=6144 f=2048, 256 routed experts "
+                        f"top-8 + 1 shared, int4 gs64 fp16 scales (20,054,016 B per expert)",
+            "tokens_per_step": T,
+            "layer_copies_rotated": args.layers,
+            "launch": "hip graph" if graph else "eager",
+            "expert_blocks_per_step": round(step_bytes / bb, 3),
+            "hbm_pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "moe_expert_ffn (decode)",
+            "achieved": round(kern_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": step_bytes,
+            "avg_launch_us": round(float(ffn_ms.mean()) * 1e3, 2),
+        },
+    }
+    del graph
+
+    # --------------------------------------------------------------- prefill
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts[0], shared[0], w_router, dev)
+
+    # ----------------------------------------------------------- CPU oracle
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(L, bb)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts, shared, w_router, dev):
+    """2048-token prefill step of the same layer (Zipf router bias)."""
+    L5 = synth.make_layer(5, experts=[])
+    bias = torch.from_numpy(L5.bias).to(dev)
+    T = 2048
+    bits, _ = synth.make_tokens(5, T)
+    x = torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+    PRE = moe.MOE_PATH_PREFILL_BF16
+    buf = LayerBuffers.allocate(sh, T, PRE)
+    try:
+        run_layer(x, w_router, bias, experts, shared, buf)
+        torch.cuda.synchronize()
+    except moe.MoeError as e:
+        log(f"prefill not measured: {e}")
+        return {"status": str(e)}
+    stream = torch.cuda.current_stream()
+    n = args.prefill_steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for _ in range(3):
+        run_layer(x, w_router, bias, experts, shared, buf)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(n):
+        moe.moe_route(sh, x, w_router, bias, buf.topk_idx, buf.topk_w, buf.workspace)
+        moe.moe_union(sh, T, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.inv_perm, buf.active, buf.n_active)
+        ev[i][0].record(stream)
+        moe.moe_expert_ffn(sh, x, experts, shared, buf.offsets, buf.perm, buf.active, buf.n_active, PRE,
+                           buf.y, buf.y_shared, buf.ffn_workspace)
+        ev[i][1].record(stream)
+        moe.moe_combine(sh, buf.y, buf.y_shared, buf.inv_perm, buf.topk_w, buf.out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms = elapsed * 1e3 / n
+    ffn_ms = np.array([s.elapsed_time(e) for s, e in ev])
+    flops = 6.0 * sh.d * sh.f * (T * sh.top_k + T)
+    tflops = flops / (ffn_ms.mean() * 1e-3) / 1e12
+    n_active = int(buf.n_active.item())
+    log(f"prefill step: {ms:.3f} ms ({T / ms * 1e3:.0f} tokens/s); expert FFN {ffn_ms.mean():.3f} ms "
+        f"= {tflops:.0f} TFLOP/s ({n_active} active experts)")
+    return {
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "ms_per_step": round(ms, 4),
+        "steps": n,
+        "dtype": "bf16",
+        "workload": "prefill, 2048 tokens, same layer, Zipf(1.1) router bias",
+        "active_experts": n_active,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "moe_expert_ffn (prefill)",
+            "achieved": round(tflops, 1),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": round(float(ffn_ms.mean()) * 1e3, 1),
+        },
+    }
+
+
+def cpu_baseline(L, bb):
+    """The float64 oracle, as it stands, on the host cores: one 1-token decode
+    step of the same layer (routing, grouping, 8 routed + 1 shared expert,
+    combine), repeated until ~10 s of CPU work."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    sh = L.shape
+    reps = 0
+    elapsed = 0.0
+    blocks = 0
+    while elapsed < 10.0 and reps < 8:
+        _, xf = __import__("synth").make_tokens(4, 1, batch=100 + reps)
+        t = time.perf_counter()
+        res = oracle.moe_layer(xf, L.w_router, None, L.experts, L.shared, sh.d, sh.f,
+                               sh.n_experts, sh.top_k)
+        elapsed += time.perf_counter() - t
+        blocks += int(res["n_active"][0]) + 1
+        reps += 1
+    gbps = blocks * bb / elapsed / 1e9
+    log(f"cpu oracle: {reps} decode steps in {elapsed:.1f}s = {gbps:.4f} GB/s ({threads} threads)")
+    return {"value": round(gbps, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} one-token decode steps of the same layer ({blocks} expert blocks), "
+                      f"float64 numpy oracle, {elapsed:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -16,6 +16,8 @@
  *                   expert in the union, plus the always-active shared expert
  *   moe_combine     gate-weighted sum of each token's k expert outputs plus
  *                   the shared expert's output
+ *   moe_pack_experts one-time byte permutation of the expert blocks into the
+ *                   tiled layout the FFN kernels stream
  *
  * Conventions common to every call:
  *  - Every pointer argument except `shape` is a DEVICE pointer owned by the
@@ -32,7 +34,8 @@
  *  - A kernel launch failure returns MOE_ERR_HIP; faults during execution
  *    surface at the caller's next synchronisation of `stream`.
  *  - Calls are thread-safe.  Calls that share a workspace buffer must be
- *    ordered (same stream, or synchronised).
+ *    ordered (same stream, or synchronised); moe_expert_ffn's workspace is
+ *    reserved for moe_expert_ffn (see there).
  *  - T == 0 (an empty batch) is valid: moe_union writes empty grouping
  *    outputs; the other calls enqueue nothing and return MOE_OK.
  */
@@ -102,6 +105,23 @@ typedef struct {
  * Equals 3*d*f/2 + 3*d*f/group*2; 20,054,016 bytes at d=6144, f=2048. */
 size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group);
 
+/* Convert expert blocks from the layout above to the packed layout that
+ * moe_expert_ffn reads: a byte permutation of each block, same size, done
+ * once when the experts are loaded (as the pages' engine converts its
+ * checkpoint once before serving: ssnai.com digest, first-command section).
+ * For each matrix W [N][K] of the block (N, K multiples of 64) the codes are
+ * regrouped into tiles of 64 rows: row t*64+l, columns 32c..32c+31 go to
+ *     q_off + t*(64*K/2) + c*1024 + l*16
+ * and inside each 4-byte word (columns 8w..8w+7) the nibble of column 8w+j
+ * moves to bit 4*(j/2) + 16*(j%2); scale s[t*64+l][g] goes to
+ *     s_off + t*(2*K) + g*128 + l*2
+ * where q_off / s_off are the sub-array offsets of the canonical block.
+ *  n_blocks  number of consecutive blocks in src (0 is a no-op)
+ *  src       canonical blocks, 16-byte aligned
+ *  dst       packed blocks, 16-byte aligned, must not overlap src */
+moe_status moe_pack_experts(const moe_shape* shape, int64_t n_blocks, const uint8_t* src,
+                            uint8_t* dst, void* stream);
+
 /* Scratch bytes moe_route needs for T tokens (router logits, float64). */
 size_t moe_route_workspace_bytes(const moe_shape* shape, int32_t T);
 
@@ -161,13 +181,20 @@ size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path)
  * the pages and is this library's reading).
  *  x         [T][d]; DECODE: bf16 or f32; PREFILL: bf16 only
  *  experts   E blocks of moe_expert_bytes(d, f, group) bytes, back to back,
- *            16-byte aligned
- *  shared    one block, or NULL iff shape->f_shared == 0
+ *            in the packed layout (moe_pack_experts), 16-byte aligned
+ *  shared    one packed block, or NULL iff shape->f_shared == 0
  *  offsets, perm, active, n_active: moe_union's outputs for this batch
  *  y         out [T*top_k][d], grouped order; float32 (DECODE) or bf16
  *            (PREFILL); rows of unused positions are not written
  *  y_shared  out [T][d] same dtype, or NULL iff no shared expert
- *  workspace >= moe_ffn_workspace_bytes(shape, T, path), 256-byte aligned */
+ *  workspace >= moe_ffn_workspace_bytes(shape, T, path), 256-byte aligned.
+ *            Its first 8 KB is a control block (work tickets and per-expert
+ *            completion counters that let one launch run the down projection
+ *            of an expert as soon as its gate/up rows are done).  Zero the
+ *            whole workspace once before its first use; every call leaves
+ *            the control block zero again.  Use a workspace for
+ *            moe_expert_ffn calls only, and never for two calls that may run
+ *            at the same time. */
 moe_status moe_expert_ffn(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
                           const uint8_t* experts, const uint8_t* shared,
                           const int32_t* offsets, const int32_t* perm, const int32_t* active,

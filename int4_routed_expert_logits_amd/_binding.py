@@ -24,8 +24,9 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_DECODE_F32, MOE_PATH_PREFILL_BF16 = 0, 1
 
 # every function include/moe_int4.h declares
-EXPORTS = ("moe_expert_bytes", "moe_route_workspace_bytes", "moe_route", "moe_union",
-           "moe_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_status_str")
+EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_route_workspace_bytes", "moe_route",
+           "moe_union", "moe_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
+           "moe_status_str")
 
 
 class Shape(ctypes.Structure):
@@ -75,6 +76,8 @@ def load():
     lib.moe_combine.argtypes = [sp, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                 c_void_p, c_int32, c_void_p]
     lib.moe_combine.restype = c_int32
+    lib.moe_pack_experts.argtypes = [sp, ctypes.c_int64, c_void_p, c_void_p, c_void_p]
+    lib.moe_pack_experts.restype = c_int32
     lib.moe_status_str.argtypes = [c_int32]
     lib.moe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -136,6 +139,13 @@ def _shape(shape):
 
 def moe_expert_bytes(d: int, f: int, group: int = 64) -> int:
     return load().moe_expert_bytes(d, f, group)
+
+
+def moe_pack_experts(shape, n_blocks: int, src, dst, stream=None):
+    """Canonical expert blocks (uint8 device tensor) -> packed blocks."""
+    sh = _shape(shape)
+    _check("moe_pack_experts", load().moe_pack_experts(ctypes.byref(sh), n_blocks, _ptr(src),
+                                                       _ptr(dst), _stream(stream)))
 
 
 def moe_route_workspace_bytes(shape, T: int) -> int:

@@ -57,6 +57,22 @@ size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group) {
   return n / 2 + n / group * 2;
 }
 
+moe_status moe_pack_experts(const moe_shape* shape, int64_t n_blocks, const uint8_t* src,
+                            uint8_t* dst, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (n_blocks < 0) return MOE_ERR_SHAPE;
+  if (n_blocks == 0) return MOE_OK;
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_ALIGN;
+  const size_t bb = moe_expert_bytes(shape->d, shape->f, shape->group);
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t len = static_cast<uintptr_t>(bb) * static_cast<uintptr_t>(n_blocks);
+  if (s0 < d0 + len && d0 < s0 + len) return MOE_ERR_SHAPE;  // overlapping buffers
+  return hip_status(moe::launch_pack(shape->d, shape->f, n_blocks, bb, src, dst,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_route_workspace_bytes(const moe_shape* shape, int32_t T) {
   if (check_shape(shape) != MOE_OK || T < 0) return 0;
   return round_up(static_cast<size_t>(T) * shape->n_experts * sizeof(double));
@@ -102,7 +118,8 @@ size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path)
   if (check_shape(shape) != MOE_OK || T < 0) return 0;
   const bool sh = shape->f_shared != 0;
   if (path == MOE_PATH_DECODE_F32)
-    return round_up(moe::ffn_decode_workspace(T, shape->top_k, shape->f, sh));
+    return round_up(moe::ffn_decode_workspace(T, shape->top_k, shape->n_experts, shape->d,
+                                              shape->f, sh));
   if (path == MOE_PATH_PREFILL_BF16)
     return round_up(moe::ffn_prefill_workspace(T, shape->top_k, shape->f, sh));
   return 0;

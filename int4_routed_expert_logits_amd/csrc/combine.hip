@@ -8,6 +8,8 @@
 #include "common.h"
 #include "launch.h"
 
+#pragma clang fp contract(off)  // the fused multiply-adds are written out
+
 namespace moe {
 
 namespace {

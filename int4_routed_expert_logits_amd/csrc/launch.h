@@ -55,12 +55,16 @@ struct FfnProblem {
 };
 
 // ffn_decode.hip: int4 GEMV, float32 intermediate and outputs.
-size_t ffn_decode_workspace(int T, int k, int f, bool has_shared);
+size_t ffn_decode_workspace(int T, int k, int E, int d, int f, bool has_shared);
 hipError_t launch_ffn_decode(const FfnProblem& p, hipStream_t stream);
 
 // ffn_prefill.hip: grouped GEMM on bf16 MFMA, bf16 intermediate and outputs.
 size_t ffn_prefill_workspace(int T, int k, int f, bool has_shared);
 hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream);
+
+// pack.hip: canonical -> packed expert blocks.
+hipError_t launch_pack(int d, int f, long long n_blocks, size_t block_bytes, const uint8_t* src,
+                       uint8_t* dst, hipStream_t stream);
 
 // combine.hip
 hipError_t launch_combine(int T, int d, int k, const void* y, const void* y_shared, bool y_bf16,

@@ -30,7 +30,8 @@ class LayerBuffers:
     y: torch.Tensor
     y_shared: Optional[torch.Tensor]
     out: torch.Tensor
-    workspace: torch.Tensor   # shared by moe_route and moe_expert_ffn (stream-ordered)
+    workspace: torch.Tensor       # moe_route scratch
+    ffn_workspace: torch.Tensor   # moe_expert_ffn scratch; zeroed once, kept zero by every call
 
     @classmethod
     def allocate(cls, shape, T: int, path: int, device="cuda", out_dtype=None):
@@ -39,7 +40,8 @@ class LayerBuffers:
         i32 = dict(dtype=torch.int32, device=device)
         ydt = torch.float32 if path == B.MOE_PATH_DECODE_F32 else torch.bfloat16
         odt = out_dtype or ydt
-        ws = max(B.moe_route_workspace_bytes(sh, T), B.moe_ffn_workspace_bytes(sh, T, path), 256)
+        ws = max(B.moe_route_workspace_bytes(sh, T), 256)
+        fws = max(B.moe_ffn_workspace_bytes(sh, T, path), 256)
         return cls(
             shape=sh, T=T, path=path,
             topk_idx=torch.empty((T, k), **i32),
@@ -54,6 +56,7 @@ class LayerBuffers:
             y_shared=torch.empty((max(T, 1), d), dtype=ydt, device=device) if sh.f_shared else None,
             out=torch.empty((T, d), dtype=odt, device=device),
             workspace=torch.empty((ws,), dtype=torch.uint8, device=device),
+            ffn_workspace=torch.zeros((fws,), dtype=torch.uint8, device=device),
         )
 
 
@@ -64,6 +67,6 @@ def run_layer(x, w_router, bias, experts, shared, buf: LayerBuffers, stream=None
     B.moe_union(sh, buf.T, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.inv_perm,
                 buf.active, buf.n_active, stream)
     B.moe_expert_ffn(sh, x, experts, shared, buf.offsets, buf.perm, buf.active, buf.n_active,
-                     buf.path, buf.y, buf.y_shared, buf.workspace, stream)
+                     buf.path, buf.y, buf.y_shared, buf.ffn_workspace, stream)
     B.moe_combine(sh, buf.y, buf.y_shared, buf.inv_perm, buf.topk_w, buf.out, stream)
     return buf.out

@@ -42,14 +42,25 @@ def dev_layer(cfg, router_only=False):
                 del _layers[k]
             torch.cuda.empty_cache()
         L = synth.make_layer(cfg, experts=[] if router_only else None)
+        sh = moe.shape_of(L.shape)
         dev = dict(
             w_router=torch.from_numpy(L.w_router).cuda(),
             bias=None if L.bias is None else torch.from_numpy(L.bias).cuda(),
-            experts=None if router_only else torch.from_numpy(L.experts).cuda(),
-            shared=None if (router_only or L.shared is None) else torch.from_numpy(L.shared).cuda(),
+            experts=None if router_only else packed(sh, L.experts),
+            shared=None if (router_only or L.shared is None) else packed(sh, L.shared[None])[0],
         )
         _layers[key] = (L, dev)
     return _layers[key]
+
+
+def packed(sh, blocks):
+    """Canonical host blocks [n, bytes] -> packed device blocks (moe_pack_experts)."""
+    src = torch.from_numpy(np.ascontiguousarray(blocks)).cuda()
+    dst = torch.empty_like(src)
+    moe.moe_pack_experts(sh, src.shape[0], src, dst)
+    torch.cuda.synchronize()
+    del src
+    return dst
 
 
 def dev_x(bits):
@@ -339,7 +350,7 @@ def test_doubling_down_scales_doubles_y():
         s *= np.float16(2.0)
     _, _, b1 = gpu_layer(1, 4)
     y1 = b1.y.cpu().numpy().copy()
-    _, _, b2 = gpu_layer(1, 4, experts_override=torch.from_numpy(blocks).cuda())
+    _, _, b2 = gpu_layer(1, 4, experts_override=packed(moe.shape_of(sh), blocks))
     assert np.array_equal(b2.y.cpu().numpy(), 2.0 * y1)
 
 
@@ -352,3 +363,42 @@ def test_empty_batch_is_a_no_op():
               dev["bias"], dev["experts"], dev["shared"], buf)
     torch.cuda.synchronize()
     assert int(buf.n_active.item()) == 0
+
+
+# ----------------------------------------------------------------------------
+# packed expert layout
+# ----------------------------------------------------------------------------
+
+def np_pack_block(blk, d, f):
+    """The packed layout, restated with numpy reshapes: 64-row tiles, 32-column
+    chunks of 16 bytes per row, nibble j of each 4-byte word moved to bit
+    4*(j//2) + 16*(j%2); scales tiled [tile][group][row]."""
+    blk = np.asarray(blk, dtype=np.uint8)
+    out = np.empty_like(blk)
+    s0 = 3 * d * f // 2
+    mats = [(f, d, 0, s0), (f, d, f * d // 2, s0 + f * (d // 64) * 2),
+            (d, f, f * d, s0 + 2 * f * (d // 64) * 2)]
+    for N, K, qo, so in mats:
+        nq = N * K // 2
+        words = blk[qo:qo + nq].view("<u4").reshape(N // 64, 64, K // 32, 4).astype(np.uint64)
+        new = np.zeros_like(words)
+        for j in range(8):
+            new |= ((words >> np.uint64(4 * j)) & np.uint64(0xF)) << np.uint64(4 * (j // 2) + 16 * (j % 2))
+        tiled = new.astype("<u4").transpose(0, 2, 1, 3)          # [tile][chunk][row][word]
+        out[qo:qo + nq] = np.ascontiguousarray(tiled).view(np.uint8).reshape(-1)
+        ns = N * (K // 64) * 2
+        sc = blk[so:so + ns].view("<u2").reshape(N // 64, 64, K // 64).transpose(0, 2, 1)
+        out[so:so + ns] = np.ascontiguousarray(sc).view(np.uint8).reshape(-1)
+    return out
+
+
+@pytest.mark.parametrize("d,f,n", [(128, 192, 3), (512, 256, 2), (6144, 2048, 1)])
+def test_pack_matches_layout_definition(d, f, n):
+    say(f"pack d={d} f={f} n={n}")
+    rng = np.random.default_rng(d + f)
+    bb = oracle.expert_block_bytes(d, f)
+    blocks = rng.integers(0, 256, size=(n, bb), dtype=np.uint8)
+    sh = moe.Shape(d, f, 8, 2, 64, 0)
+    got = packed(sh, blocks).cpu().numpy()
+    for b in range(n):
+        assert np.array_equal(got[b], np_pack_block(blocks[b], d, f)), f"block {b}"
