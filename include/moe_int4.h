@@ -113,9 +113,8 @@ size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group);
  * regrouped into tiles of 64 rows: row t*64+l, columns 32c..32c+31 go to
  *     q_off + t*(64*K/2) + c*1024 + l*16
  * and inside each 4-byte word (columns 8w..8w+7) the nibble of column 8w+j
- * moves to bit 4*(j/2) + 16*(j%2); scale s[t*64+l][g] goes to
- *     s_off + t*(2*K) + g*128 + l*2
- * where q_off / s_off are the sub-array offsets of the canonical block.
+ * moves to bit 4*(j/2) + 16*(j%2), where q_off is the sub-array offset of
+ * the canonical block.  Scales are copied unchanged (row-major [N][K/64]).
  *  n_blocks  number of consecutive blocks in src (0 is a no-op)
  *  src       canonical blocks, 16-byte aligned
  *  dst       packed blocks, 16-byte aligned, must not overlap src */
@@ -187,14 +186,10 @@ size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path)
  *  y         out [T*top_k][d], grouped order; float32 (DECODE) or bf16
  *            (PREFILL); rows of unused positions are not written
  *  y_shared  out [T][d] same dtype, or NULL iff no shared expert
- *  workspace >= moe_ffn_workspace_bytes(shape, T, path), 256-byte aligned.
- *            Its first 8 KB is a control block (work tickets and per-expert
- *            completion counters that let one launch run the down projection
- *            of an expert as soon as its gate/up rows are done).  Zero the
- *            whole workspace once before its first use; every call leaves
- *            the control block zero again.  Use a workspace for
- *            moe_expert_ffn calls only, and never for two calls that may run
- *            at the same time. */
+ *  workspace >= moe_ffn_workspace_bytes(shape, T, path), 256-byte aligned,
+ *            no initial contents required: it carries the intermediate h
+ *            from the gate/up kernel to the down kernel.  Never share one
+ *            workspace between two calls that may run at the same time. */
 moe_status moe_expert_ffn(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
                           const uint8_t* experts, const uint8_t* shared,
                           const int32_t* offsets, const int32_t* perm, const int32_t* active,

@@ -75,7 +75,7 @@ moe_status moe_pack_experts(const moe_shape* shape, int64_t n_blocks, const uint
 
 size_t moe_route_workspace_bytes(const moe_shape* shape, int32_t T) {
   if (check_shape(shape) != MOE_OK || T < 0) return 0;
-  return round_up(static_cast<size_t>(T) * shape->n_experts * sizeof(double));
+  return round_up(moe::route_workspace(T, shape->d, shape->n_experts));
 }
 
 moe_status moe_route(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,

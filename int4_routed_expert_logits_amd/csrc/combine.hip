@@ -38,48 +38,66 @@ struct Vec<true> {
   }
 };
 
+template <bool YBF16>
+__device__ __forceinline__ void load_row8(const void* base, size_t i, float (&v)[8]) {
+  if constexpr (YBF16) {
+    Vec<true>::load(base, i, v);
+  } else {
+    float a[4], b[4];
+    Vec<false>::load(base, i, a);
+    Vec<false>::load(base, i + 4, b);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = a[q];
+      v[4 + q] = b[q];
+    }
+  }
+}
+
+// All k row indices and weights of a token are loaded before any y row, and
+// the y rows of 8 slots are in flight together; empty slots (inv_perm < 0)
+// leave the sum untouched.
 template <bool YBF16, bool OBF16>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
-                                                      const void* __restrict__ y_shared,
-                                                      const int32_t* __restrict__ inv_perm,
-                                                      const float* __restrict__ topk_w,
-                                                      void* __restrict__ out, int T, int d,
-                                                      int k) {
-  constexpr int V = 8;  // columns per thread (two float4 loads for f32 inputs)
+__global__ __launch_bounds__(64) void combine_kernel(const void* __restrict__ y,
+                                                     const void* __restrict__ y_shared,
+                                                     const int32_t* __restrict__ inv_perm,
+                                                     const float* __restrict__ topk_w,
+                                                     void* __restrict__ out, int T, int d,
+                                                     int k) {
+  constexpr int V = 8;   // columns per thread
+  constexpr int KU = 8;  // slots in flight
   const int t = blockIdx.y;
   const int c0 = (blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (c0 >= d) return;
   float acc[V];
 #pragma unroll
-  for (int j = 0; j < V; ++j) acc[j] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int p = inv_perm[static_cast<size_t>(t) * k + j];
-    if (p < 0) continue;
-    const float w = topk_w[static_cast<size_t>(t) * k + j];
-    float v[V];
-    if constexpr (YBF16) {
-      Vec<true>::load(y, static_cast<size_t>(p) * d + c0, v);
-    } else {
-      float a[4], b[4];
-      Vec<false>::load(y, static_cast<size_t>(p) * d + c0, a);
-      Vec<false>::load(y, static_cast<size_t>(p) * d + c0 + 4, b);
+  for (int q = 0; q < V; ++q) acc[q] = 0.0f;
+  for (int j0 = 0; j0 < k; j0 += KU) {
+    int p[KU];
+    float w[KU];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { v[q] = a[q]; v[4 + q] = b[q]; }
+    for (int jj = 0; jj < KU; ++jj) {
+      const int j = j0 + jj;
+      p[jj] = j < k ? inv_perm[static_cast<size_t>(t) * k + j] : -1;
+      w[jj] = j < k ? topk_w[static_cast<size_t>(t) * k + j] : 0.0f;
+    }
+    float v[KU][V];
+#pragma unroll
+    for (int jj = 0; jj < KU; ++jj) {
+      const size_t row = p[jj] >= 0 ? static_cast<size_t>(p[jj]) : 0;
+      load_row8<YBF16>(y, row * d + c0, v[jj]);
     }
 #pragma unroll
-    for (int q = 0; q < V; ++q) acc[q] = fmaf(w, v[q], acc[q]);
+    for (int jj = 0; jj < KU; ++jj) {
+      if (p[jj] >= 0) {
+#pragma unroll
+        for (int q = 0; q < V; ++q) acc[q] = fmaf(w[jj], v[jj][q], acc[q]);
+      }
+    }
   }
   if (y_shared) {
     float v[V];
-    if constexpr (YBF16) {
-      Vec<true>::load(y_shared, static_cast<size_t>(t) * d + c0, v);
-    } else {
-      float a[4], b[4];
-      Vec<false>::load(y_shared, static_cast<size_t>(t) * d + c0, a);
-      Vec<false>::load(y_shared, static_cast<size_t>(t) * d + c0 + 4, b);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { v[q] = a[q]; v[4 + q] = b[q]; }
-    }
+    load_row8<YBF16>(y_shared, static_cast<size_t>(t) * d + c0, v);
 #pragma unroll
     for (int q = 0; q < V; ++q) acc[q] += v[q];
   }
@@ -103,8 +121,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 hipError_t launch_combine(int T, int d, int k, const void* y, const void* y_shared, bool y_bf16,
                           const int32_t* inv_perm, const float* topk_w, void* out,
                           bool out_bf16, hipStream_t stream) {
-  const dim3 block(256);
-  const dim3 grid((d / 8 + 255) / 256, T);
+  const dim3 block(64);
+  const dim3 grid((d / 8 + 63) / 64, T);
   if (y_bf16)
     return out_bf16 ? launch(combine_kernel<true, true>, grid, block, 0, stream, y, y_shared,
                              inv_perm, topk_w, out, T, d, k)

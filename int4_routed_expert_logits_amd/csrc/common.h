@@ -38,6 +38,38 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// Lane permutation of a double inside rows of 16 lanes (DPP control CTRL).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(static_cast<uint32_t>(b)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(static_cast<uint32_t>(b >> 32)), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b)), lane));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b >> 32)), lane));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Wave-wide float64 sum over a fixed tree (pairs, quads, 8s, 16s inside each
+// row through DPP, then the four row sums), so the result does not depend on
+// scheduling; every lane receives it.  Addition is commutative in IEEE
+// arithmetic, so both lanes of each exchange hold the same partial sum.
+__device__ __forceinline__ double wave_sum_f64_tree(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 }  // namespace moe

@@ -4,22 +4,29 @@
 // yunpan.plus article, "capability 2" -- each routed expert read once for all
 // tokens of the batch that chose it).
 //
-// One launch, two phases over the packed expert blocks (pack.hip):
+// Two stream-ordered kernels over the packed expert blocks (pack.hip):
 //   gate/up  h[p] = silu(W_gate x) * (W_up x)   for every grouped position p
 //   down     y[p] = W_down h[p]
-// A work item is one wavefront: one 64-row tile of one expert's matrix
-// (gate and up together in the first phase) over one part of the input
-// dimension.  Each lane owns one row and accumulates it over the part, so
-// there is no cross-lane reduction per row.  Splitting the input dimension
-// into P parts gives enough equal, independent wavefronts to spread over all
-// 256 CUs (a 1-token step has only 9 experts x 32 gate/up tiles); the parts'
-// partial sums go to the workspace and the part that finishes last adds them
-// in part order (so the result does not depend on timing) and finishes the
-// tile: h = silu(g) * u, or the y row.  The activations of the item's tokens
-// are staged in LDS and read back as broadcasts.  Codes stream through
-// buffer loads, 16 bytes per lane, two 32-column chunks per matrix per
-// pipeline step, with the next step's loads in flight during the current
-// step's math.
+// Each is a pure streaming pass: every wavefront reads its own rows once and
+// writes finished outputs, with no counters, no partial sums in memory and
+// no waiting on other workgroups; the kernel boundary is the only
+// synchronisation between the phases (h goes through the workspace).
+//
+// Lanes split rows and the input dimension: a gate/up wavefront owns 8 rows
+// of gate and of up, each row spread over 8 lanes that take one eighth of
+// the input columns; a down wavefront owns 16 rows over 4 lanes each.  A
+// lane's partial sums are combined over its row's lanes by a fixed butterfly
+// inside the wavefront, so the summation order is fixed by the layer shape
+// and a token's result does not depend on the batch it comes in.  With 8
+// gate/up rows per wavefront a 1-token step of the ~19 MB-expert layer has
+// 9 x 256 equal gate/up wavefronts (9 per CU) and 9 x 384 down wavefronts.
+//
+// Codes stream through buffer loads, 16 bytes (32 nibbles of one row) per
+// lane; the 16-byte pieces of 8 (or 16) neighbouring rows are contiguous in
+// the packed tile, so every load instruction reads whole 128-byte lines.
+// The activations of the workgroup's tokens (x for gate/up, h for down) are
+// staged once in LDS; the parts of a row are skewed by 16 bytes so that the
+// lanes of one LDS read hit different banks.
 //
 // Dequant: with the packed nibble order, ((w >> 4i) & 0x000F000F) ^ 0x43084308
 // is the bf16 pair (136 + q_a, 136 + q_b) of two neighbouring columns, exactly
@@ -29,27 +36,13 @@
 // and the fp16 group scale applied once per 32 codes.  float32 activations
 // and the float32 h fed to the down projection are carried as bf16 hi + lo
 // pairs (16 significant bits); accumulation is float32 throughout.
-//
-// Both phases run in one persistent grid of single-wavefront workgroups.
-// Items [0, n_items1) are gate/up parts, the rest down parts, expert-slot
-// major; workgroup b takes items b, b + grid, ... in order.  The grid never
-// exceeds what the GPU holds at once, so every workgroup is resident, and a
-// workgroup finishes its gate/up items before it reaches a down item: a down
-// item waiting for its slot's h always sees it finish.  Data that crosses
-// workgroups (partial sums, h) goes through device-scope stores and loads,
-// which bypass the per-XCD L2 caches that are not coherent with each other,
-// and is published by a counter increment after the stores have completed.
 #include <algorithm>
-#include <mutex>
-#include <utility>
-#include <vector>
 
 #include "common.h"
 #include "launch.h"
 
 // Every fused multiply-add below is written out; no other contraction, so a
-// token's arithmetic is the same in every code path (one or two tokens per
-// sweep) and its result does not depend on the batch it is in.
+// token's arithmetic is the same however many tokens share a sweep.
 #pragma clang fp contract(off)
 
 namespace moe {
@@ -61,19 +54,15 @@ constexpr uint32_t kMask = 0x000F000Fu;
 constexpr uint32_t kMagicX = 0x43084308u;  // bf16 exponent 2^7 | nibble sign flip
 constexpr float kOffset = 136.0f;
 
-// Control block (int32 words) at the head of the workspace: per expert slot,
-// on its own 128-byte line, the number of gate/up tiles that have published
-// h and the number of down tiles that have finished; a flag raised if a wait
-// ever timed out; then one arrival counter per (slot, tile) of each phase.
-// Zero before the first call; every counter is zeroed again by the last
-// wavefront that uses it, so each call leaves the block zero.
-constexpr int kLineWords = 32;
-constexpr int kMaxSlots = 1025;  // 1024 experts + shared
-constexpr int kTimeout = kMaxSlots * kLineWords;
-constexpr int kTileCounters = kTimeout + kLineWords;
-constexpr uint64_t kSpinLimit = 200000000ull;  // 2 s of the 100 MHz wall clock
+constexpr int kGuRows = 8;     // gate/up rows per wavefront
+constexpr int kGuParts = 8;    // lanes per gate/up row
+constexpr int kGuWaves = 4;    // wavefronts per gate/up workgroup (32 rows)
+constexpr int kDnRows = 16;    // down rows per wavefront
+constexpr int kDnParts = 4;    // lanes per down row
+constexpr int kDnWaves = 4;    // wavefronts per down workgroup (64 rows)
+constexpr int kSkewWords = 4;  // LDS skew between the parts of a row (16 bytes)
 
-struct DecodeArgs {
+struct FfnArgs {
   const uint8_t* experts;
   const uint8_t* shared;
   size_t block_bytes;
@@ -84,33 +73,26 @@ struct DecodeArgs {
   int top_k;
   int T;
   int has_shared;
-  int slots;           // shared first (if any), then active[0 ..]
   int d, f;
   size_t q_gate, q_up, q_down, s_gate, s_up, s_down;
-  const void* x;       // [T][d] bf16 or f32
-  uint32_t* hp;        // h as bf16 pairs: [T*k + T][f/32][32] (hi pairs, then lo pairs)
-  float* hs;           // h chunk sums:    [T*k + T][f/32]
-  float* y;            // [T*k][d]
-  float* y_shared;     // [T][d]
-  int* ctrl;
-  int* tcnt1;          // [slots][tiles1] arrival counters (gate/up)
-  int* tcnt2;          // [slots][tiles2] arrival counters (down)
-  float* part1;        // [rows][tiles1][P1][2][64] gate/up partial sums (P1 > 1)
-  float* part2;        // [rows][tiles2][P2][64] down partial sums (P2 > 1)
-  int tiles1, tiles2;  // f/64, d/64
-  int P1, P2;          // input-dimension parts per tile
-  int n_items1, n_items2;
+  const void* x;  // [T][d] bf16 or f32
+  uint32_t* hp;   // h as bf16 pairs: [T*k + T][f/32][32] (16 hi words, 16 lo words)
+  float* y;       // [T*k][d]
+  float* y_shared;  // [T][d]
 };
 
 struct Slot {
   const uint8_t* blk;
-  int M;         // tokens
-  int p0;        // first grouped position (routed experts)
+  int M;   // tokens
+  int p0;  // first grouped position (routed experts)
   bool shared;
   bool live;
 };
 
-__device__ __forceinline__ Slot resolve_slot(const DecodeArgs& g, int slot) {
+// Expert slot s of the launch: the shared expert first (if any), then
+// active[0 ..].  Everything here is the same for every lane; keeping it in
+// scalar registers keeps the buffer descriptors built from it scalar.
+__device__ __forceinline__ Slot resolve_slot(const FfnArgs& g, int slot) {
   Slot s{nullptr, 0, 0, false, false};
   if (slot < g.has_shared) {
     s.blk = g.shared;
@@ -119,11 +101,10 @@ __device__ __forceinline__ Slot resolve_slot(const DecodeArgs& g, int slot) {
     s.live = true;
     return s;
   }
-  // the same for every lane: keep it in scalar registers, so the buffer
-  // descriptors built from it are scalar too
-  const int ra = slot - g.has_shared;
-  if (ra >= __builtin_amdgcn_readfirstlane(g.n_active[0])) return s;
-  const int e = __builtin_amdgcn_readfirstlane(g.active[ra]);
+  // active[] is -1 past the n_active experts of the batch, so one load tells
+  // both whether the slot is live and which expert it holds
+  const int e = __builtin_amdgcn_readfirstlane(g.active[slot - g.has_shared]);
+  if (e < 0) return s;
   s.blk = g.experts + static_cast<size_t>(e) * g.block_bytes;
   s.p0 = __builtin_amdgcn_readfirstlane(g.offsets[e]);
   s.M = __builtin_amdgcn_readfirstlane(g.offsets[e + 1]) - s.p0;
@@ -131,31 +112,11 @@ __device__ __forceinline__ Slot resolve_slot(const DecodeArgs& g, int slot) {
   return s;
 }
 
-// Position of token m of a slot in the h / y row space (shared rows follow
-// the T*k routed positions).
-__device__ __forceinline__ int row_of(const DecodeArgs& g, const Slot& sl, int m) {
+// Position of token m of a slot in the h row space (shared rows follow the
+// T*k routed positions).
+__device__ __forceinline__ int row_of(const FfnArgs& g, const Slot& sl, int m) {
   return sl.shared ? g.T * g.top_k + m : sl.p0 + m;
 }
-
-// ---------------------------------------------------------------------------
-// one pipeline step of codes + scales for NM matrices of a tile
-// ---------------------------------------------------------------------------
-
-template <int NM>
-struct Step {
-  uint4 q[NM][kStep];
-  float s[NM][kStep];
-};
-
-// Buffer resources of one tile's codes and scales for NM matrices: loads go
-// through a 128-bit scalar descriptor plus one lane offset, so no per-load
-// 64-bit addresses occupy vector registers, and a read past the tile returns
-// zero instead of touching other memory.
-template <int NM>
-struct TileRes {
-  __amdgpu_buffer_rsrc_t q[NM];
-  __amdgpu_buffer_rsrc_t s[NM];
-};
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer access
 
@@ -164,36 +125,52 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            static_cast<int>(bytes), kRsrcWord3);
 }
 
-// Loads are unconditional (chunk indices past the wavefront's range are
-// clamped to its last chunk, a cache hit), so the compiler sees the same
-// number of loads in flight on every path and can wait for exactly the step
-// it needs instead of for everything.
+// One pipeline step: kStep chunks of codes (16 bytes per lane) for NM
+// matrices.
 template <int NM>
-__device__ __forceinline__ void load_step(const TileRes<NM>& res, int c0, int ce, int cbase,
-                                          int lane, Step<NM>& d) {
+struct Step {
+  uint4 q[NM][kStep];
+};
+
+// Codes of one 64-row tile for NM matrices, as buffer resources: a 128-bit
+// scalar descriptor plus one lane offset per load.
+template <int NM>
+struct TileRes {
+  __amdgpu_buffer_rsrc_t q[NM];
+};
+
+// Chunks [c, c + kStep) of this lane's range [cb, ce).  Loads are
+// unconditional (indices past the range are clamped to its last chunk, a
+// cache hit), so every path has the same loads in flight and the compiler
+// waits for exactly the step it needs.  rt: the lane's row inside the tile.
+template <int NM>
+__device__ __forceinline__ void load_step(const TileRes<NM>& res, int c, int cb, int ce, int rt,
+                                          Step<NM>& d) {
 #pragma unroll
   for (int i = 0; i < kStep; ++i) {
-    const int c = cbase + min(c0 + i, ce - 1);
+    const int cc = max(min(c + i, ce - 1), cb);
 #pragma unroll
     for (int mat = 0; mat < NM; ++mat) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(res.q[mat], lane * 16, c * 1024, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(res.q[mat], cc * 1024 + rt * 16, 0, 0);
       d.q[mat][i] = make_uint4(v[0], v[1], v[2], v[3]);
-      const unsigned short h =
-          __builtin_amdgcn_raw_buffer_load_b16(res.s[mat], lane * 2, (c >> 1) * 128, 0);
-      d.s[mat][i] = static_cast<float>(__builtin_bit_cast(_Float16, h));
     }
   }
 }
 
-// XW: activation words per chunk in LDS (16: bf16 pairs; 32: hi pairs then lo pairs)
+// Math of one step.  xl: this lane's activations, local chunk cl of token m
+// at xl[m * tok_words + cl * XW]; xs: chunk sums at xs[m * sum_words + cl];
+// sc[mat]: the fp16 group scales of this lane's row, indexed by local group
+// (the lane's range starts at chunk cb).  XW = 16 (bf16 pairs) or 32 (16 hi
+// pairs, then 16 lo pairs).
 template <int NM, int MT, int XW>
-__device__ __forceinline__ void math_step(const Step<NM>& d, int c0, int ce, int nt,
-                                          const uint32_t* xl, const float* xs, int chunks,
+__device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int cb, int nt,
+                                          const uint32_t* xl, int tok_words, const float* xs,
+                                          int sum_words, const _Float16* const (&sc)[NM],
                                           float (&acc)[NM][MT]) {
 #pragma unroll
   for (int i = 0; i < kStep; ++i) {
-    const int c = c0 + i;
-    if (c >= ce) break;
+    const int c = cl + i;
+    if (c >= nl) break;
     float tc[NM][MT];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -202,9 +179,9 @@ __device__ __forceinline__ void math_step(const Step<NM>& d, int c0, int ce, int
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m < nt) {
-          xh[m] = *reinterpret_cast<const uint4*>(xl + (m * chunks + c) * XW + 4 * w);
+          xh[m] = *reinterpret_cast<const uint4*>(xl + m * tok_words + c * XW + 4 * w);
           if constexpr (XW == 32)
-            xo[m] = *reinterpret_cast<const uint4*>(xl + (m * chunks + c) * XW + 16 + 4 * w);
+            xo[m] = *reinterpret_cast<const uint4*>(xl + m * tok_words + c * XW + 16 + 4 * w);
         }
       }
 #pragma unroll
@@ -234,51 +211,87 @@ __device__ __forceinline__ void math_step(const Step<NM>& d, int c0, int ce, int
       }
     }
 #pragma unroll
-    for (int mat = 0; mat < NM; ++mat)
+    for (int mat = 0; mat < NM; ++mat) {
+      const float sv = static_cast<float>(sc[mat][(cb + c) >> 1]);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         if (m < nt)
-          acc[mat][m] = fmaf(d.s[mat][i], fmaf(-kOffset, xs[m * chunks + c], tc[mat][m]), acc[mat][m]);
+          acc[mat][m] = fmaf(sv, fmaf(-kOffset, xs[m * sum_words + c], tc[mat][m]), acc[mat][m]);
+    }
   }
 }
 
-// Partial sums of this wavefront over chunks cbase + [0, nc) of the tile,
-// whose activations sit in LDS at local chunk indices [0, nc): two step
+// This lane's partial sums over its chunks [cb, ce) of the tile: two step
 // buffers, the next step's loads in flight while the current step's math
-// runs.
+// runs.  Every lane runs the same number of steps (nmax = the longest part);
+// lanes past their own range do no math.
+//
+// `a` and `b` hold the first two steps' loads, issued by the caller before
+// it staged the activations, so their latency overlaps the staging.
 template <int NM, int MT, int XW>
-__device__ __forceinline__ void tile_sweep(const TileRes<NM>& res, int cbase, int nc, int nt,
-                                           const uint32_t* xl, const float* xs, int lane,
-                                           float (&acc)[NM][MT]) {
+__device__ __forceinline__ void sweep(const TileRes<NM>& res, int cb, int ce, int nmax, int rt,
+                                      int nt, const uint32_t* xl, int tok_words, const float* xs,
+                                      int sum_words, const _Float16* const (&sc)[NM], Step<NM>& a,
+                                      Step<NM>& b, float (&acc)[NM][MT]) {
 #pragma unroll
   for (int mat = 0; mat < NM; ++mat)
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[mat][m] = 0.0f;
-  if (nc <= 0) return;
-  Step<NM> a, b;
-  load_step<NM>(res, 0, nc, cbase, lane, a);
-  for (int c0 = 0; c0 < nc; c0 += 2 * kStep) {
-    load_step<NM>(res, c0 + kStep, nc, cbase, lane, b);
-    math_step<NM, MT, XW>(a, c0, nc, nt, xl, xs, nc, acc);
-    load_step<NM>(res, c0 + 2 * kStep, nc, cbase, lane, a);
-    math_step<NM, MT, XW>(b, c0 + kStep, nc, nt, xl, xs, nc, acc);
+  const int nl = ce - cb;
+  for (int c0 = 0; c0 < nmax; c0 += 2 * kStep) {
+    math_step<NM, MT, XW>(a, c0, nl, cb, nt, xl, tok_words, xs, sum_words, sc, acc);
+    load_step<NM>(res, cb + c0 + 2 * kStep, cb, ce, rt, a);
+    math_step<NM, MT, XW>(b, c0 + kStep, nl, cb, nt, xl, tok_words, xs, sum_words, sc, acc);
+    load_step<NM>(res, cb + c0 + 3 * kStep, cb, ce, rt, b);
   }
 }
 
-// ---------------------------------------------------------------------------
-// LDS staging of the item's activations (chunks [cb, ce) of the input)
-// ---------------------------------------------------------------------------
+// LDS layout of a workgroup's staged activations: token m, part p, local
+// chunk cl at word m * tok_words + p * part_words + cl * xw (part_words =
+// cpp_max * xw + kSkewWords); chunk sums at m * sum_words + p * cpp_max + cl.
+// Part p covers chunks [p * chunks / parts, (p + 1) * chunks / parts).
+struct StageLayout {
+  int parts, chunks, cpp_max, xw, part_words, tok_words, sum_words;
+  __device__ __forceinline__ int cb(int p) const { return p * chunks / parts; }
+  __device__ __forceinline__ int part_of(int c) const {
+    int p = c * parts / chunks;
+    while (cb(p + 1) <= c) ++p;
+    while (cb(p) > c) --p;
+    return p;
+  }
+};
 
-// x rows of the gate/up phase: bf16 copied as pairs, or f32 split into hi/lo.
+__device__ __forceinline__ StageLayout stage_layout(int chunks, int parts, int xw) {
+  StageLayout s;
+  s.parts = parts;
+  s.chunks = chunks;
+  s.cpp_max = (chunks + parts - 1) / parts;
+  s.xw = xw;
+  s.part_words = s.cpp_max * xw + kSkewWords;
+  s.tok_words = parts * s.part_words;
+  s.sum_words = parts * s.cpp_max;
+  return s;
+}
+
+// The fp16 scales of `rows` consecutive rows (row-major, `groups` per row,
+// contiguous in the block) into LDS.
+__device__ __forceinline__ void stage_scales(const uint8_t* src, int rows, int groups,
+                                             uint32_t* dst) {
+  const int n16 = rows * groups / 8;  // 16-byte pieces (rows is a multiple of 8)
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  for (int i = threadIdx.x; i < n16; i += blockDim.x) reinterpret_cast<uint4*>(dst)[i] = s[i];
+}
+
+// x rows of the gate/up phase: bf16 copied as pairs, or f32 split into hi/lo
+// bf16; plus each chunk's sum of the values the dot products see.
 template <bool XF32>
-__device__ __forceinline__ void stage_x(const DecodeArgs& g, const Slot& sl, int m0, int nt,
-                                        int cb, int ce, uint32_t* xl, float* xs) {
-  constexpr int XW = XF32 ? 32 : 16;
-  const int nc = ce - cb;
-  for (int i = threadIdx.x; i < nt * nc; i += kWave) {
-    const int m = i / nc, cc = i - m * nc, c = cb + cc;
-    const int tok = sl.shared ? m0 + m : g.perm[sl.p0 + m0 + m] / g.top_k;
-    uint32_t* dst = xl + (m * nc + cc) * XW;
+__device__ void stage_x(const FfnArgs& g, const Slot& sl, int m0, int nt, const StageLayout& L,
+                        uint32_t* xl, float* xs) {
+  for (int i = threadIdx.x; i < nt * L.chunks; i += blockDim.x) {
+    const int m = i / L.chunks, c = i - m * L.chunks;
+    const int p = L.part_of(c), cl = c - L.cb(p);
+    const int tok = sl.shared ? m0 + m : (g.T == 1 ? 0 : g.perm[sl.p0 + m0 + m] / g.top_k);
+    uint32_t* dst = xl + m * L.tok_words + p * L.part_words + cl * L.xw;
     float s = 0.0f;
     if constexpr (!XF32) {
       const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g.x) +
@@ -312,307 +325,195 @@ __device__ __forceinline__ void stage_x(const DecodeArgs& g, const Slot& sl, int
         dst[16 + 2 * j + 1] = lo[2] | (lo[3] << 16);
       }
     }
-    xs[m * nc + cc] = s;
+    xs[m * L.sum_words + p * L.cpp_max + cl] = s;
   }
 }
 
-// h rows of the down phase (already hi/lo pairs), read at device scope.
-__device__ __forceinline__ void stage_h(const DecodeArgs& g, const Slot& sl, int m0, int nt,
-                                        int cb, int ce, uint32_t* xl, float* xs) {
-  const int chunks = g.f / 32, nc = ce - cb;
-  for (int i = threadIdx.x; i < nt * nc * 32; i += kWave) {
-    const int m = i / (nc * 32), rest = i - m * nc * 32;
+// h rows of the down phase (hi/lo pairs), plus each chunk's sum.
+__device__ void stage_h(const FfnArgs& g, const Slot& sl, int m0, int nt, const StageLayout& L,
+                        uint32_t* xl, float* xs) {
+  for (int i = threadIdx.x; i < nt * L.chunks; i += blockDim.x) {
+    const int m = i / L.chunks, c = i - m * L.chunks;
+    const int p = L.part_of(c), cl = c - L.cb(p);
     const size_t row = row_of(g, sl, m0 + m);
-    xl[m * nc * 32 + rest] = __hip_atomic_load(g.hp + (row * chunks + cb) * 32 + rest, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-  }
-  for (int i = threadIdx.x; i < nt * nc; i += kWave) {
-    const int m = i / nc, cc = i - m * nc;
-    const size_t row = row_of(g, sl, m0 + m);
-    xs[m * nc + cc] =
-        __hip_atomic_load(g.hs + row * chunks + cb + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-__device__ __forceinline__ void wait_for(const DecodeArgs& g, const int* counter, int need) {
-  const uint64_t t0 = wall_clock64();
-  while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-    __builtin_amdgcn_s_sleep(2);
-    if (wall_clock64() - t0 > kSpinLimit) {
-      atomicOr(g.ctrl + kTimeout, 1);
-      break;
+    const uint4* src = reinterpret_cast<const uint4*>(g.hp + (row * L.chunks + c) * 32);
+    uint32_t* dst = xl + m * L.tok_words + p * L.part_words + cl * 32;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 v = src[j];
+      reinterpret_cast<uint4*>(dst)[j] = v;
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s += __uint_as_float(w[q] << 16) + __uint_as_float(w[q] & 0xFFFF0000u);
     }
+    xs[m * L.sum_words + p * L.cpp_max + cl] = s;
   }
-}
-
-__device__ __forceinline__ float load_dev(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Publish this wavefront's device-scope stores, then bump a counter; returns
-// the counter's previous value (the same in every lane).
-__device__ __forceinline__ int publish(int* counter) {
-  __builtin_amdgcn_s_waitcnt(0);  // the stores above have completed
-  __syncthreads();
-  int old = 0;
-  if (threadIdx.x == 0)
-    old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __shfl(old, 0, kWave);
-}
-
-// h of one token for this tile's 64 rows, written as bf16 hi/lo pairs plus
-// the 32-row chunk sums the down phase needs.
-__device__ __forceinline__ void write_h(const DecodeArgs& g, size_t row, int tile, float gs, float us) {
-  const int lane = threadIdx.x;
-  const int fchunks = g.f / 32;
-  const float h = silu(gs) * us;
-  const uint32_t hi = f32_to_bf16(h);
-  const uint32_t lo = f32_to_bf16(h - __uint_as_float(hi << 16));
-  const uint32_t hi_o = __shfl_xor(hi, 1, kWave), lo_o = __shfl_xor(lo, 1, kWave);
-  // row r = tile*64 + lane sits in chunk tile*2 + lane/32, pair (lane%32)/2
-  const int c = tile * 2 + (lane >> 5), j = (lane & 31) >> 1;
-  uint32_t* hrow = g.hp + (row * fchunks + c) * 32;
-  if ((lane & 1) == 0)
-    __hip_atomic_store(hrow + j, hi | (hi_o << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    __hip_atomic_store(hrow + 16 + j, lo_o | (lo << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  float part = __uint_as_float(hi << 16) + __uint_as_float(lo << 16);
-  part = group_sum(part, 32);
-  if ((lane & 31) == 0) store_dev(g.hs + row * fchunks + c, part);
 }
 
 // ---------------------------------------------------------------------------
-// the two phases
+// gate/up: one workgroup per (expert slot, 64-row tile of f), 8 wavefronts
+// of 8 rows; lane = 8 * part + row
 // ---------------------------------------------------------------------------
 
 template <int MT, bool XF32>
-__device__ void gateup_item(const DecodeArgs& g, const Slot& sl, int slot, int tile, int kp,
-                            uint32_t* xl, float* xs) {
+__global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g) {
+  extern __shared__ __align__(16) uint32_t lds[];
   constexpr int XW = XF32 ? 32 : 16;
-  const int lane = threadIdx.x;
-  const int chunks = g.d / 32;
-  const int cb = kp * chunks / g.P1, ce = (kp + 1) * chunks / g.P1;
-  const size_t tq = static_cast<size_t>(tile) * 64 * (g.d / 2), ts = static_cast<size_t>(tile) * 2 * g.d;
+  const Slot sl = resolve_slot(g, blockIdx.y);
+  if (!sl.live) return;
+  const int row0 = blockIdx.x * kGuWaves * kGuRows;  // first f-row of the workgroup
+  const int tile = row0 / 64;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & (kGuRows - 1), p = lane >> 3;
+  const int rt = row0 % 64 + wv * kGuRows + r;  // row inside the tile
+  const StageLayout L = stage_layout(g.d / 32, kGuParts, XW);
+  constexpr int kRowsWg = kGuWaves * kGuRows;
+  const int groups = g.d / 64;
+  uint32_t* scl = lds;                                    // [2][kRowsWg][groups] fp16
+  uint32_t* xl = lds + kRowsWg * groups;                  // staged x
+  float* xs = reinterpret_cast<float*>(xl + MT * L.tok_words);
+  const int cb = L.cb(p), ce = L.cb(p + 1);
+
+  const size_t tq = static_cast<size_t>(tile) * 64 * (g.d / 2);
   TileRes<2> res;
   res.q[0] = make_rsrc(sl.blk + g.q_gate + tq, 32u * g.d);
   res.q[1] = make_rsrc(sl.blk + g.q_up + tq, 32u * g.d);
-  res.s[0] = make_rsrc(sl.blk + g.s_gate + ts, 2u * g.d);
-  res.s[1] = make_rsrc(sl.blk + g.s_up + ts, 2u * g.d);
+  const int rl = wv * kGuRows + r;  // row inside the workgroup
+  const _Float16* const sc[2] = {
+      reinterpret_cast<const _Float16*>(scl) + rl * groups,
+      reinterpret_cast<const _Float16*>(scl) + (kRowsWg + rl) * groups};
+  stage_scales(sl.blk + g.s_gate + static_cast<size_t>(row0) * groups * 2, kRowsWg, groups, scl);
+  stage_scales(sl.blk + g.s_up + static_cast<size_t>(row0) * groups * 2, kRowsWg, groups,
+               scl + kRowsWg * groups / 2);
+  const int fchunks = g.f / 32;
+  const int frow = row0 + wv * kGuRows + r;
+
   for (int m0 = 0; m0 < sl.M; m0 += MT) {
     const int nt = min(MT, sl.M - m0);
+    Step<2> first, second;
+    load_step<2>(res, cb, cb, ce, rt, first);
+    load_step<2>(res, cb + kStep, cb, ce, rt, second);
     __syncthreads();
-    stage_x<XF32>(g, sl, m0, nt, cb, ce, xl, xs);
+    stage_x<XF32>(g, sl, m0, nt, L, xl, xs);
     __syncthreads();
     float acc[2][MT];
-    tile_sweep<2, MT, XW>(res, cb, ce - cb, nt, xl, xs, lane, acc);
+    sweep<2, MT, XW>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
+                     xs + p * L.cpp_max, L.sum_words, sc, first, second, acc);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m >= nt) break;
+      // sum over the row's 8 lanes (lane bits 3..5), fixed order
+      float gs = acc[0][m], us = acc[1][m];
+      gs += __shfl_xor(gs, 8, kWave);
+      us += __shfl_xor(us, 8, kWave);
+      gs += __shfl_xor(gs, 16, kWave);
+      us += __shfl_xor(us, 16, kWave);
+      gs += __shfl_xor(gs, 32, kWave);
+      us += __shfl_xor(us, 32, kWave);
+      const float h = silu(gs) * us;
+      const uint32_t hi = f32_to_bf16(h);
+      const uint32_t lo = f32_to_bf16(h - __uint_as_float(hi << 16));
+      const uint32_t hi_o = __shfl_xor(hi, 1, kWave), lo_o = __shfl_xor(lo, 1, kWave);
+      // f-row frow sits in chunk frow/32, pair (frow%32)/2
       const size_t row = row_of(g, sl, m0 + m);
-      if (g.P1 == 1) {
-        write_h(g, row, tile, acc[0][m], acc[1][m]);
-      } else {
-        float* pp = g.part1 + ((row * g.tiles1 + tile) * g.P1 + kp) * 128;
-        store_dev(pp + lane, acc[0][m]);
-        store_dev(pp + 64 + lane, acc[1][m]);
-      }
+      uint32_t* hrow = g.hp + (row * fchunks + (frow >> 5)) * 32;
+      const int j = (frow & 31) >> 1;
+      if (p == 0 && (r & 1) == 0) hrow[j] = hi | (hi_o << 16);
+      if (p == 1 && (r & 1) == 1) hrow[16 + j] = lo_o | (lo << 16);
     }
   }
-  if (g.P1 > 1) {
-    // the last part to arrive adds the parts in order and writes h
-    int* tc = g.tcnt1 + slot * g.tiles1 + tile;
-    if (publish(tc) != g.P1 - 1) return;
-    for (int m = 0; m < sl.M; ++m) {
-      const size_t row = row_of(g, sl, m);
-      const float* pp = g.part1 + (row * g.tiles1 + tile) * g.P1 * 128;
-      float gs = 0.0f, us = 0.0f;
-      for (int q = 0; q < g.P1; ++q) {
-        gs += load_dev(pp + q * 128 + lane);
-        us += load_dev(pp + q * 128 + 64 + lane);
-      }
-      write_h(g, row, tile, gs, us);
-    }
-    if (lane == 0) __hip_atomic_store(tc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // h of this tile is complete for every token of the slot
-  publish(g.ctrl + slot * kLineWords);
 }
+
+// ---------------------------------------------------------------------------
+// down: one workgroup per (expert slot, 64-row tile of d), 4 wavefronts of
+// 16 rows; lane = 16 * part + row
+// ---------------------------------------------------------------------------
 
 template <int MT>
-__device__ void down_item(const DecodeArgs& g, const Slot& sl, int slot, int tile, int kp,
-                          uint32_t* xl, float* xs) {
-  const int lane = threadIdx.x;
-  const int chunks = g.f / 32;
-  const int cb = kp * chunks / g.P2, ce = (kp + 1) * chunks / g.P2;
+__global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  const Slot sl = resolve_slot(g, blockIdx.y);
+  if (!sl.live) return;
+  const int row0 = blockIdx.x * kDnWaves * kDnRows;  // first d-row of the workgroup
+  const int tile = row0 / 64;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & (kDnRows - 1), p = lane >> 4;
+  const int rt = row0 % 64 + wv * kDnRows + r;
+  const StageLayout L = stage_layout(g.f / 32, kDnParts, 32);
+  constexpr int kRowsWg = kDnWaves * kDnRows;
+  const int groups = g.f / 64;
+  uint32_t* scl = lds;                                    // [kRowsWg][groups] fp16
+  uint32_t* xl = lds + kRowsWg * groups / 2;              // staged h
+  float* xs = reinterpret_cast<float*>(xl + MT * L.tok_words);
+  const int cb = L.cb(p), ce = L.cb(p + 1);
+
   TileRes<1> res;
   res.q[0] = make_rsrc(sl.blk + g.q_down + static_cast<size_t>(tile) * 64 * (g.f / 2), 32u * g.f);
-  res.s[0] = make_rsrc(sl.blk + g.s_down + static_cast<size_t>(tile) * 2 * g.f, 2u * g.f);
-  int* line = g.ctrl + slot * kLineWords;
-  if (lane == 0) wait_for(g, line, g.tiles1);
-  __syncthreads();
+  const int rl = wv * kDnRows + r;
+  const _Float16* const sc[1] = {reinterpret_cast<const _Float16*>(scl) + rl * groups};
+  stage_scales(sl.blk + g.s_down + static_cast<size_t>(row0) * groups * 2, kRowsWg, groups, scl);
+  const int drow = row0 + wv * kDnRows + r;
+
   for (int m0 = 0; m0 < sl.M; m0 += MT) {
     const int nt = min(MT, sl.M - m0);
+    Step<1> first, second;
+    load_step<1>(res, cb, cb, ce, rt, first);
+    load_step<1>(res, cb + kStep, cb, ce, rt, second);
     __syncthreads();
-    stage_h(g, sl, m0, nt, cb, ce, xl, xs);
+    stage_h(g, sl, m0, nt, L, xl, xs);
     __syncthreads();
     float acc[1][MT];
-    tile_sweep<1, MT, 32>(res, cb, ce - cb, nt, xl, xs, lane, acc);
+    sweep<1, MT, 32>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
+                     xs + p * L.cpp_max, L.sum_words, sc, first, second, acc);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m >= nt) break;
-      const size_t row = row_of(g, sl, m0 + m);
-      if (g.P2 == 1) {
+      float ys = acc[0][m];
+      ys += __shfl_xor(ys, 16, kWave);
+      ys += __shfl_xor(ys, 32, kWave);
+      if (p == 0) {
         float* out = sl.shared ? g.y_shared + static_cast<size_t>(m0 + m) * g.d
                                : g.y + static_cast<size_t>(sl.p0 + m0 + m) * g.d;
-        out[tile * 64 + lane] = acc[0][m];
-      } else {
-        store_dev(g.part2 + ((row * g.tiles2 + tile) * g.P2 + kp) * 64 + lane, acc[0][m]);
+        out[drow] = ys;
       }
     }
   }
-  if (g.P2 > 1) {
-    int* tc = g.tcnt2 + slot * g.tiles2 + tile;
-    if (publish(tc) != g.P2 - 1) return;
-    for (int m = 0; m < sl.M; ++m) {
-      const size_t row = row_of(g, sl, m);
-      const float* pp = g.part2 + (row * g.tiles2 + tile) * g.P2 * 64;
-      float ys = 0.0f;
-      for (int q = 0; q < g.P2; ++q) ys += load_dev(pp + q * 64 + lane);
-      float* out = sl.shared ? g.y_shared + static_cast<size_t>(m) * g.d
-                             : g.y + static_cast<size_t>(sl.p0 + m) * g.d;
-      out[tile * 64 + lane] = ys;
-    }
-    if (lane == 0) __hip_atomic_store(tc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // the slot's last down tile clears both slot counters for the next call
-  __syncthreads();
-  if (lane == 0 &&
-      __hip_atomic_fetch_add(line + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g.tiles2 - 1) {
-    __hip_atomic_store(line, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(line + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
+
+int gu_lds_bytes(int d, int mt, bool xf32) {
+  const int chunks = d / 32, cpp = (chunks + kGuParts - 1) / kGuParts, xw = xf32 ? 32 : 16;
+  const int scales = kGuWaves * kGuRows * (d / 64);  // words: two matrices of fp16
+  return (scales + mt * (kGuParts * (cpp * xw + kSkewWords) + kGuParts * cpp)) * 4;
+}
+
+int dn_lds_bytes(int f, int mt) {
+  const int chunks = f / 32, cpp = (chunks + kDnParts - 1) / kDnParts;
+  const int scales = kDnWaves * kDnRows * (f / 64) / 2;
+  return (scales + mt * (kDnParts * (cpp * 32 + kSkewWords) + kDnParts * cpp)) * 4;
+}
+
+constexpr int kMaxLds = 64 * 1024;
 
 template <int MT, bool XF32>
-__global__ __launch_bounds__(kWave) void decode_ffn(DecodeArgs g, int lds_words) {
-  extern __shared__ __align__(16) uint32_t lds[];
-  uint32_t* xl = lds;                                   // activations of the part
-  float* xs = reinterpret_cast<float*>(lds + lds_words);  // their chunk sums
-  const int n_items = g.n_items1 + g.n_items2;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    if (item < g.n_items1) {
-      const int per_slot = g.tiles1 * g.P1;
-      const int slot = item / per_slot, r = item - slot * per_slot;
-      const Slot sl = resolve_slot(g, slot);
-      if (!sl.live) continue;
-      gateup_item<MT, XF32>(g, sl, slot, r / g.P1, r % g.P1, xl, xs);
-    } else {
-      const int it = item - g.n_items1;
-      const int per_slot = g.tiles2 * g.P2;
-      const int slot = it / per_slot, r = it - slot * per_slot;
-      const Slot sl = resolve_slot(g, slot);
-      if (!sl.live) continue;
-      down_item<MT>(g, sl, slot, r / g.P2, r % g.P2, xl, xs);
-    }
-  }
-}
-
-// Parts per tile: from the layer shape alone (about 24 gate/up or 16 down
-// chunks per part, a power of two up to 16), so a token's summation order --
-// and its result, bit for bit -- does not depend on the batch it comes in.
-// The 1-token step of the ~19 MB-expert layer gets 9 x 32 x 8 = 2304 gate/up
-// and 9 x 96 x 4 = 3456 down wavefronts.  Batches of more than 64 tokens have
-// enough tiles by themselves and use one part (no partial-sum traffic).
-constexpr int kSplitMaxTokens = 64;
-
-int parts_for(int chunks, int per_part, int T) {
-  if (T > kSplitMaxTokens) return 1;
-  int p = 1;
-  while (chunks / p > per_part && p < 16) p *= 2;
-  return p;
-}
-
-struct Layout {
-  int P1, P2;
-  size_t ctrl_words, hp, hs, part1, part2, total;  // byte offsets / sizes
-};
-
-Layout layout_for(int T, int k, int E, int d, int f, bool has_shared) {
-  Layout l{};
-  const int slots = (has_shared ? 1 : 0) + std::min(E, T * k);
-  const int tiles1 = f / 64, tiles2 = d / 64;
-  l.P1 = parts_for(d / 32, 24, T);
-  l.P2 = parts_for(f / 32, 16, T);
-  const size_t rows = static_cast<size_t>(T) * (k + (has_shared ? 1 : 0));
-  l.ctrl_words = kTileCounters + static_cast<size_t>(slots) * (tiles1 + tiles2);
-  size_t off = (l.ctrl_words * 4 + 255) / 256 * 256;
-  l.hp = off;
-  off += rows * f * 4;
-  l.hs = off;
-  off += (rows * (f / 32) * 4 + 255) / 256 * 256;
-  l.part1 = off;
-  if (l.P1 > 1) off += rows * tiles1 * l.P1 * 128 * 4;
-  l.part2 = off;
-  if (l.P2 > 1) off += rows * tiles2 * l.P2 * 64 * 4;
-  l.total = off;
-  return l;
-}
-
-int lds_words_for(int d, int f, int P1, int P2, int mt, bool xf32) {
-  const int c1 = (d / 32 + P1 - 1) / P1, c2 = (f / 32 + P2 - 1) / P2;
-  return mt * std::max(c1 * (xf32 ? 32 : 16), c2 * 32);
-}
-
-size_t lds_bytes_for(int d, int f, int P1, int P2, int mt, bool xf32) {
-  const int c1 = (d / 32 + P1 - 1) / P1, c2 = (f / 32 + P2 - 1) / P2;
-  return (static_cast<size_t>(lds_words_for(d, f, P1, P2, mt, xf32)) + mt * std::max(c1, c2)) * 4;
-}
-
-constexpr size_t kMaxLds = 64 * 1024;
-
-// Workgroups of a kernel the GPU holds at once, for a given LDS size: the
-// persistent grid must not exceed it.  Cached per (kernel, device, LDS size).
-int resident_capacity(const void* kernel, size_t lds) {
-  static std::mutex mu;
-  static std::vector<std::pair<std::pair<const void*, int>, std::pair<size_t, int>>> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  for (const auto& e : cache)
-    if (e.first.first == kernel && e.first.second == dev && e.second.first == lds) return e.second.second;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWave, lds) != hipSuccess ||
-      per_cu <= 0)
-    return 0;
-  cache.push_back({{kernel, dev}, {lds, cus * per_cu}});
-  return cus * per_cu;
-}
-
-template <int MT, bool XF32>
-hipError_t launch_mt(const DecodeArgs& g, hipStream_t s) {
-  auto kernel = decode_ffn<MT, XF32>;
-  const int words = lds_words_for(g.d, g.f, g.P1, g.P2, MT, XF32);
-  const size_t lds = lds_bytes_for(g.d, g.f, g.P1, g.P2, MT, XF32);
-  const int cap = resident_capacity(reinterpret_cast<const void*>(kernel), lds);
-  if (cap <= 0) return hipErrorInvalidValue;
-  const int grid = std::min(cap, g.n_items1 + g.n_items2);
-  return launch(kernel, dim3(static_cast<unsigned>(grid)), dim3(kWave), lds, s, g, words);
+hipError_t launch_mt(const FfnArgs& g, int slots, hipStream_t s) {
+  const dim3 g1(g.f / (kGuWaves * kGuRows), slots), g2(g.d / (kDnWaves * kDnRows), slots);
+  hipError_t err = launch(decode_gateup<MT, XF32>, g1, dim3(kGuWaves * kWave),
+                          gu_lds_bytes(g.d, MT, XF32), s, g);
+  if (err != hipSuccess) return err;
+  return launch(decode_down<MT>, g2, dim3(kDnWaves * kWave), dn_lds_bytes(g.f, MT), s, g);
 }
 
 }  // namespace
 
-size_t ffn_decode_workspace(int T, int k, int E, int d, int f, bool has_shared) {
-  return layout_for(T, k, E, d, f, has_shared).total;
+size_t ffn_decode_workspace(int T, int k, int /*E*/, int /*d*/, int f, bool has_shared) {
+  const size_t rows = static_cast<size_t>(T) * (k + (has_shared ? 1 : 0));
+  return rows * f * 4;  // h as bf16 hi/lo pairs
 }
 
 hipError_t launch_ffn_decode(const FfnProblem& p, hipStream_t stream) {
   const size_t dd = p.d, ff = p.f;
-  const Layout l = layout_for(p.T, p.k, p.E, p.d, p.f, p.has_shared);
-  DecodeArgs g{};
+  FfnArgs g{};
   g.experts = p.experts;
   g.shared = p.shared;
   g.block_bytes = p.block_bytes;
@@ -623,7 +524,6 @@ hipError_t launch_ffn_decode(const FfnProblem& p, hipStream_t stream) {
   g.top_k = p.k;
   g.T = p.T;
   g.has_shared = p.has_shared ? 1 : 0;
-  g.slots = g.has_shared + std::min(p.E, p.T * p.k);
   g.d = p.d;
   g.f = p.f;
   g.q_gate = 0;
@@ -633,28 +533,25 @@ hipError_t launch_ffn_decode(const FfnProblem& p, hipStream_t stream) {
   g.s_up = g.s_gate + ff * (dd / 64) * 2;
   g.s_down = g.s_up + ff * (dd / 64) * 2;
   g.x = p.x;
-  char* ws = static_cast<char*>(p.workspace);
-  g.ctrl = reinterpret_cast<int*>(ws);
-  g.tcnt1 = g.ctrl + kTileCounters;
-  g.tiles1 = p.f / 64;
-  g.tiles2 = p.d / 64;
-  g.tcnt2 = g.tcnt1 + static_cast<size_t>(g.slots) * g.tiles1;
-  g.hp = reinterpret_cast<uint32_t*>(ws + l.hp);
-  g.hs = reinterpret_cast<float*>(ws + l.hs);
-  g.part1 = reinterpret_cast<float*>(ws + l.part1);
-  g.part2 = reinterpret_cast<float*>(ws + l.part2);
+  g.hp = static_cast<uint32_t*>(p.workspace);
   g.y = static_cast<float*>(p.y);
   g.y_shared = static_cast<float*>(p.y_shared);
-  g.P1 = l.P1;
-  g.P2 = l.P2;
-  g.n_items1 = g.slots * g.tiles1 * g.P1;
-  g.n_items2 = g.slots * g.tiles2 * g.P2;
+  const int slots = g.has_shared + std::min(p.E, p.T * p.k);
   const bool xf32 = !p.x_bf16;
-  // two tokens per sweep when experts can hold several and the LDS fits
-  const bool two = p.T >= 2 && lds_bytes_for(p.d, p.f, l.P1, l.P2, 2, xf32) <= kMaxLds;
-  if (!two && lds_bytes_for(p.d, p.f, l.P1, l.P2, 1, xf32) > kMaxLds) return hipErrorNotSupported;
-  if (xf32) return two ? launch_mt<2, true>(g, stream) : launch_mt<1, true>(g, stream);
-  return two ? launch_mt<2, false>(g, stream) : launch_mt<1, false>(g, stream);
+  // tokens per sweep: as many as the batch offers, up to 4, LDS permitting
+  int mt = p.T >= 4 ? 4 : (p.T >= 2 ? 2 : 1);
+  while (mt > 1 && (gu_lds_bytes(p.d, mt, xf32) > kMaxLds || dn_lds_bytes(p.f, mt) > kMaxLds))
+    mt /= 2;
+  if (gu_lds_bytes(p.d, mt, xf32) > kMaxLds || dn_lds_bytes(p.f, mt) > kMaxLds)
+    return hipErrorNotSupported;
+  if (xf32) {
+    if (mt == 4) return launch_mt<4, true>(g, slots, stream);
+    if (mt == 2) return launch_mt<2, true>(g, slots, stream);
+    return launch_mt<1, true>(g, slots, stream);
+  }
+  if (mt == 4) return launch_mt<4, false>(g, slots, stream);
+  if (mt == 2) return launch_mt<2, false>(g, slots, stream);
+  return launch_mt<1, false>(g, slots, stream);
 }
 
 }  // namespace moe

@@ -11,10 +11,9 @@
 // one contiguous kilobyte.  Inside each 4-byte word (8 columns 8w..8w+7) the
 // nibble of column 8w+j moves to bit 4*(j/2) + 16*(j%2), so that
 // (word >> 4i) & 0x000F000F holds columns (8w+2i, 8w+2i+1) in its two
-// 16-bit halves.  Scales follow the same tiling:
-//     s_off + t*(2*K) + g*128 + l*2      (group g = 64 columns)
-// The offsets q_off / s_off of the six sub-arrays are those of the canonical
-// block.
+// 16-bit halves.  Scales keep the canonical row-major order [N][K/64]: a
+// kernel stages the scales of its rows (contiguous) once.  The offsets
+// q_off / s_off of the six sub-arrays are those of the canonical block.
 #include <algorithm>
 
 #include "common.h"
@@ -99,12 +98,9 @@ __global__ __launch_bounds__(256) void pack_scales(PackArgs a) {
       if (u < g.sunits) break;
       u -= g.sunits;
     }
-    const int gpr = g.K / 64;  // groups per row
-    const int r = static_cast<int>(u / gpr), gi = static_cast<int>(u % gpr);
     const uint16_t* s = reinterpret_cast<const uint16_t*>(a.src + b * a.block_bytes + g.s_off);
     uint16_t* d = reinterpret_cast<uint16_t*>(a.dst + b * a.block_bytes + g.s_off);
-    d[static_cast<size_t>(r / 64) * (64 * gpr) + static_cast<size_t>(gi) * 64 + (r % 64)] =
-        s[static_cast<size_t>(r) * gpr + gi];
+    d[u] = s[u];
   }
 }
 

@@ -31,7 +31,7 @@ class LayerBuffers:
     y_shared: Optional[torch.Tensor]
     out: torch.Tensor
     workspace: torch.Tensor       # moe_route scratch
-    ffn_workspace: torch.Tensor   # moe_expert_ffn scratch; zeroed once, kept zero by every call
+    ffn_workspace: torch.Tensor   # moe_expert_ffn scratch (the intermediate h)
 
     @classmethod
     def allocate(cls, shape, T: int, path: int, device="cuda", out_dtype=None):
@@ -56,7 +56,7 @@ class LayerBuffers:
             y_shared=torch.empty((max(T, 1), d), dtype=ydt, device=device) if sh.f_shared else None,
             out=torch.empty((T, d), dtype=odt, device=device),
             workspace=torch.empty((ws,), dtype=torch.uint8, device=device),
-            ffn_workspace=torch.zeros((fws,), dtype=torch.uint8, device=device),
+            ffn_workspace=torch.empty((fws,), dtype=torch.uint8, device=device),
         )
 
 

@@ -108,9 +108,75 @@ def test_route_parity(cfg, T):
     gap = min_gap(lg, k)
     assert np.array_equal(idx.cpu().numpy(), ridx), f"top-k differs (smallest k/k+1 logit gap {gap:.3e})"
     assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-6
-    # the gpu logits themselves (float64, summation order aside)
-    glg = ws[: T * sh.n_experts * 8].view(torch.float64).reshape(T, sh.n_experts).cpu().numpy()
+    # the gpu logits themselves (float64, summation order aside); small batches
+    # leave per-part partial sums in the workspace, large ones whole logits
+    P = route_parts(T, sh.d, sh.n_experts)
+    raw = ws[: T * sh.n_experts * max(P, 1) * 8].view(torch.float64).cpu().numpy()
+    if P:
+        part = raw.reshape(T, sh.n_experts, P)
+        glg = part[:, :, 0].copy()
+        for p in range(1, P):
+            glg += part[:, :, p]
+        if L.bias is not None:
+            glg += L.bias.astype(np.float64)
+    else:
+        glg = raw.reshape(T, sh.n_experts)
     assert np.max(np.abs(glg - lg)) <= 1e-12 * max(1.0, np.max(np.abs(lg)))
+
+
+def route_parts(T, d, E):
+    """Parts the small-batch logit kernel splits each router row into (0 for
+    the tiled large-batch kernel); mirrors the library's host rule."""
+    if T > 32:
+        return 0
+    P = min(max(2048 // E, 1), 16)
+    return max(1, min(P, d // 256)) if P > d // 256 else P
+
+
+def _route_fine(E, k, T=1):
+    """Logits 1 + e*2^-30 (exact in float64, all equal after rounding to
+    float32), so only the float64 comparison can order them."""
+    sh = moe.Shape(64, 64, E, k, 64, 0)
+    x = torch.zeros((T, 64), dtype=torch.float32, device="cuda")
+    x[:, 0] = 1.0
+    x[:, 1] = 2.0 ** -30
+    wr = torch.zeros((E, 64), dtype=torch.float32, device="cuda")
+    wr[:, 0] = 1.0
+    wr[:, 1] = torch.arange(E, dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_route_workspace_bytes(sh, T), dtype=torch.uint8, device="cuda")
+    moe.moe_route(sh, x, wr, None, idx, w, ws)
+    torch.cuda.synchronize()
+    ridx, rw, _ = oracle.route(x.cpu().numpy(), wr.cpu().numpy(), None, k)
+    return idx.cpu().numpy(), w.cpu().numpy(), ridx, rw
+
+
+def test_route_float64_order_below_float32_resolution():
+    """64 experts whose float32 keys all tie: the candidate ranking decides."""
+    say("route fine float64 order, E=64")
+    idx, w, ridx, rw = _route_fine(64, 4)
+    assert idx.tolist() == [[63, 62, 61, 60]]
+    assert np.array_equal(idx, ridx) and np.max(np.abs(w - rw)) <= 1e-6
+
+
+def test_route_mass_tie_fallback():
+    """More than 64 experts share the float32 cut: the exact argmax rounds."""
+    say("route mass tie, E=100")
+    idx, w, ridx, rw = _route_fine(100, 8, T=3)
+    assert idx.tolist() == [list(range(99, 91, -1))] * 3
+    assert np.array_equal(idx, ridx) and np.max(np.abs(w - rw)) <= 1e-6
+    # all-equal logits: lowest ids win, equal weights
+    sh = moe.Shape(64, 64, 128, 8, 64, 0)
+    x = torch.zeros((2, 64), dtype=torch.bfloat16, device="cuda")
+    wr = torch.zeros((128, 64), dtype=torch.float32, device="cuda")
+    idx = torch.empty((2, 8), dtype=torch.int32, device="cuda")
+    w = torch.empty((2, 8), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_route_workspace_bytes(sh, 2), dtype=torch.uint8, device="cuda")
+    moe.moe_route(sh, x, wr, None, idx, w, ws)
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == [list(range(8))] * 2
+    assert np.allclose(w.cpu().numpy(), 0.125, atol=0)
 
 
 def test_route_ties_go_to_lower_id():
@@ -372,7 +438,7 @@ def test_empty_batch_is_a_no_op():
 def np_pack_block(blk, d, f):
     """The packed layout, restated with numpy reshapes: 64-row tiles, 32-column
     chunks of 16 bytes per row, nibble j of each 4-byte word moved to bit
-    4*(j//2) + 16*(j%2); scales tiled [tile][group][row]."""
+    4*(j//2) + 16*(j%2); scales unchanged."""
     blk = np.asarray(blk, dtype=np.uint8)
     out = np.empty_like(blk)
     s0 = 3 * d * f // 2
@@ -387,8 +453,7 @@ def np_pack_block(blk, d, f):
         tiled = new.astype("<u4").transpose(0, 2, 1, 3)          # [tile][chunk][row][word]
         out[qo:qo + nq] = np.ascontiguousarray(tiled).view(np.uint8).reshape(-1)
         ns = N * (K // 64) * 2
-        sc = blk[so:so + ns].view("<u2").reshape(N // 64, 64, K // 64).transpose(0, 2, 1)
-        out[so:so + ns] = np.ascontiguousarray(sc).view(np.uint8).reshape(-1)
+        out[so:so + ns] = blk[so:so + ns]
     return out
 
 
