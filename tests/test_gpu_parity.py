@@ -318,25 +318,31 @@ def oracle_sampled(L, xf, sample_tokens):
     idx, w, lg = oracle.route(xf, L.w_router, L.bias, sh.top_k)
     union = oracle.batch_union(idx, sh.n_experts)
     inv = union[3]
-    cache = {}
-
-    def expert_rows(e, rows):
-        if e not in cache:
-            blk = L.shared if e == "shared" else L.experts[e]
-            cache[e] = oracle.expert_weights(blk, sh.d, sh.f)
-        return oracle.swiglu(np.asarray(xf[rows], dtype=np.float64), *cache[e])
-
-    y = {}
-    out = {}
+    # expert -> sampled tokens that use it; one expert's weights in memory at a time
+    need = {}
+    for t in sample_tokens:
+        for j in range(sh.top_k):
+            need.setdefault(int(idx[t, j]), []).append(t)
+        if L.shared is not None:
+            need.setdefault("shared", []).append(t)
+    rows = {}
+    for e, toks in need.items():
+        blk = L.shared if e == "shared" else L.experts[e]
+        wts = oracle.expert_weights(blk, sh.d, sh.f)
+        res = oracle.swiglu(np.asarray(xf[toks], dtype=np.float64), *wts)
+        for t, r in zip(toks, res):
+            rows[(e, t)] = r
+        del wts
+    y, ysh, out = {}, {}, {}
     for t in sample_tokens:
         acc = np.zeros(sh.d)
         for j in range(sh.top_k):
             p = int(inv[t * sh.top_k + j])
-            y[p] = expert_rows(int(idx[t, j]), [t])[0]
+            y[p] = rows[(int(idx[t, j]), t)]
             acc += float(w[t, j]) * y[p]
-        ys = expert_rows("shared", [t])[0] if L.shared is not None else 0.0
-        out[t] = acc + ys
-    return dict(topk_idx=idx, topk_w=w, union=union, y=y, out=out, logits=lg)
+        ysh[t] = rows[("shared", t)] if L.shared is not None else np.zeros(sh.d)
+        out[t] = acc + ysh[t]
+    return dict(topk_idx=idx, topk_w=w, union=union, y=y, y_shared=ysh, out=out, logits=lg)
 
 
 def check_routing_and_union(buf, ref_idx, ref_w, union):
@@ -467,3 +473,75 @@ def test_pack_matches_layout_definition(d, f, n):
     got = packed(sh, blocks).cpu().numpy()
     for b in range(n):
         assert np.array_equal(got[b], np_pack_block(blocks[b], d, f)), f"block {b}"
+
+
+# ----------------------------------------------------------------------------
+# whole layer, prefill path (bf16 MFMA grouped GEMM)
+# ----------------------------------------------------------------------------
+
+PRE = moe.MOE_PATH_PREFILL_BF16
+TOL_PREFILL = 2e-2
+
+
+def prefill_err(got, ref):
+    """Largest error of a bf16 prefill output in units of the stated bound:
+    2e-2 * rms(ref) for the arithmetic, plus the output's own round-to-
+    nearest bf16 rounding of up to 2^-8 * |ref| (outputs here reach ~6.5
+    rms, where that rounding alone is ~2.5e-2 rms).  <= 1 passes."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return float(np.max(np.abs(got - ref) / (TOL_PREFILL * rms + 2.0 ** -8 * np.abs(ref))))
+PREFILL_FULL = [(2, 16), (2, 5), (3, 64), (3, 13)]
+
+
+@pytest.mark.parametrize("cfg,T", PREFILL_FULL)
+def test_layer_prefill_parity(cfg, T):
+    """bf16 x through route, union, the MFMA FFN and a bf16 combine, against
+    the float64 oracle at the 2e-2 * rms bound of the bf16 path."""
+    say(f"layer prefill cfg={cfg} T={T}")
+    L, xf, buf = gpu_layer(cfg, T, path=PRE)
+    sh = L.shape
+    ref = oracle.moe_layer(xf, L.w_router, L.bias, L.experts, L.shared, sh.d, sh.f,
+                           sh.n_experts, sh.top_k)
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"],
+                            (ref["counts"], ref["offsets"], ref["perm"], ref["inv_perm"],
+                             ref["active"], ref["n_active"]))
+    ey = prefill_err(buf.y.float().cpu().numpy()[: T * sh.top_k], ref["y"])
+    assert ey <= 1.0, f"y error {ey:.2f} x bound"
+    if L.shared is not None:
+        es = prefill_err(buf.y_shared.float().cpu().numpy()[:T], ref["y_shared"])
+        assert es <= 1.0, f"y_shared error {es:.2f} x bound"
+    eo = prefill_err(buf.out.float().cpu().numpy(), ref["out"])
+    assert eo <= 1.0, f"out error {eo:.2f} x bound"
+
+
+@pytest.mark.parametrize("cfg,T,sample", [(4, 40, [0, 17, 39]), (5, 2048, [0, 1000, 2047])])
+def test_layer_prefill_parity_19mb_layer_sampled(cfg, T, sample):
+    """The ~19 MB-expert layer: 40 tokens (many one-token experts) and the
+    2048-token Zipf-routed batch (experts of up to ~1600 rows, the shared
+    expert over all 2048); every expert output of the sampled tokens and
+    their layer outputs against the oracle."""
+    say(f"layer prefill cfg={cfg} T={T} (sampled {sample})")
+    L, xf, buf = gpu_layer(cfg, T, path=PRE)
+    ref = oracle_sampled(L, xf, sample)
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"], ref["union"])
+    y = buf.y.float().cpu().numpy()
+    got = np.stack([y[p] for p in ref["y"]])
+    assert prefill_err(got, np.stack(list(ref["y"].values()))) <= 1.0
+    ysh = buf.y_shared.float().cpu().numpy()
+    assert prefill_err(ysh[sample], np.stack([ref["y_shared"][t] for t in sample])) <= 1.0
+    out = buf.out.float().cpu().numpy()
+    assert prefill_err(out[sample], np.stack([ref["out"][t] for t in sample])) <= 1.0
+
+
+def test_prefill_empty_batch():
+    """T = 0 is a valid call that enqueues nothing."""
+    say("prefill empty batch")
+    L, dev = dev_layer(2)
+    sh = moe.shape_of(L.shape)
+    buf = LayerBuffers.allocate(sh, 0, PRE)
+    x = torch.empty((0, sh.d), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_ffn(sh, x, dev["experts"], None, buf.offsets, buf.perm, buf.active,
+                       buf.n_active, PRE, buf.y, None, buf.ffn_workspace)
+    torch.cuda.synchronize()
