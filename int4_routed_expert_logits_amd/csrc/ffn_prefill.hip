@@ -9,10 +9,20 @@
 //
 // Work: for every expert slot (the shared expert first, then the active
 // routed experts) its rows -- the grouped positions, i.e. the tokens that
-// chose it -- are cut into M-tiles of 32.  A workgroup of 4 wavefronts takes
-// one M-tile and 256 output columns; each wavefront computes 32 rows x 64
-// columns with v_mfma_f32_32x32x16_bf16, streaming its weights straight from
-// the packed tile into registers.  A small kernel first lists the M-tiles.
+// chose it -- are cut into M-tiles: 128-row tiles while at least 96 rows are
+// left, the rest in 32-row tiles.  A small kernel lists both kinds.
+//  * 128-row tiles (the heavy experts of a Zipf-routed batch, the shared
+//    expert): compute-bound.  A workgroup of 4 wavefronts stages the
+//    activations and the codes of one 64-column scale group in LDS (double
+//    buffered), and each wavefront computes 64 rows x 32 or 64 columns with
+//    v_mfma_f32_32x32x16_bf16.
+//  * 32-row tiles (the many experts with a handful of tokens): bound by the
+//    weight stream.  The activations of a group go through LDS, each
+//    wavefront keeps 4 groups of its own codes in flight in registers and
+//    multiplies both 16-row blocks with v_mfma_f32_16x16x32_bf16.
+// The weights are read once per tile; the codes go from memory straight to
+// MFMA operands (in registers, or through LDS where 4 wavefronts share
+// them).
 //
 // Dequant into the MFMA: a 4-byte word of the packed codes holds 8
 // consecutive input columns, and ((w >> 4i) & 0x000F000F) ^ 0x43084308 is
@@ -38,13 +48,13 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 32;        // rows per M-tile
-constexpr int kWaveCols = 64;  // output columns per wavefront
-constexpr int kWaves = 4;      // wavefronts per workgroup
-constexpr int kWgCols = kWaves * kWaveCols;
+constexpr int kBM = 32;        // rows per small M-tile
+constexpr int kBigM = 128;     // rows per big M-tile
+constexpr int kBigMinRows = 96;  // fewest rows a big tile is used for
 constexpr uint32_t kMask = 0x000F000Fu;
 constexpr uint32_t kMagicX = 0x43084308u;
 constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kMaxLds = 160 * 1024;
 
 struct PrefillArgs {
   const uint8_t* experts;
@@ -63,8 +73,10 @@ struct PrefillArgs {
   uint16_t* h;         // [T*k + T][f] bf16
   uint16_t* y;         // [T*k][d] bf16
   uint16_t* y_shared;  // [T][d] bf16
-  int2* tiles;         // (slot, first row) of every M-tile
+  int2* tiles;         // (slot, first row) of every 32-row M-tile
   int* n_tiles;
+  int2* big_tiles;     // (slot, first row) of every 128-row M-tile
+  int* n_big;
 };
 
 struct Slot {
@@ -95,14 +107,25 @@ __device__ __forceinline__ int row_of(const PrefillArgs& g, const Slot& sl, int 
 }
 
 // ---------------------------------------------------------------------------
-// M-tile list: one workgroup, slots in chunks of 1024
+// M-tile lists: one workgroup, slots in chunks of 1024.  A slot's rows go to
+// 128-row tiles while at least 96 rows are left for the next one, the rest
+// to 32-row tiles.
 // ---------------------------------------------------------------------------
 
+__device__ __forceinline__ void big_small(int M, int& nb, int& ns) {
+  nb = M / kBigM + ((M % kBigM) >= kBigMinRows ? 1 : 0);
+  const int rem = max(0, M - nb * kBigM);
+  ns = (rem + kBM - 1) / kBM;
+}
+
 __global__ __launch_bounds__(1024) void prefill_tiles(PrefillArgs g) {
-  __shared__ int wave_tot[16];
-  __shared__ int base_s;
+  __shared__ int tot_b[16], tot_s[16];
+  __shared__ int base_b, base_s;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if (tid == 0) base_s = 0;
+  if (tid == 0) {
+    base_b = 0;
+    base_s = 0;
+  }
   __syncthreads();
   for (int s0 = 0; s0 < g.slots; s0 += 1024) {
     const int slot = s0 + tid;
@@ -115,25 +138,45 @@ __global__ __launch_bounds__(1024) void prefill_tiles(PrefillArgs g) {
         if (e >= 0) M = g.offsets[e + 1] - g.offsets[e];
       }
     }
-    const int nt = (M + kBM - 1) / kBM;
-    int incl = nt;
+    int nb, ns;
+    big_small(M, nb, ns);
+    int ib = nb, is = ns;  // inclusive scans over the workgroup
     for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
+      const int ob = __shfl_up(ib, off, 64), os = __shfl_up(is, off, 64);
+      if (lane >= off) {
+        ib += ob;
+        is += os;
+      }
     }
-    if (lane == 63) wave_tot[wv] = incl;
+    if (lane == 63) {
+      tot_b[wv] = ib;
+      tot_s[wv] = is;
+    }
     __syncthreads();
-    int before = base_s;
-    for (int w = 0; w < wv; ++w) before += wave_tot[w];
-    int total = 0;
-    for (int w = 0; w < 16; ++w) total += wave_tot[w];
-    const int pos = before + incl - nt;
-    for (int i = 0; i < nt; ++i) g.tiles[pos + i] = make_int2(slot, i * kBM);
+    int pb = base_b, ps = base_s, all_b = 0, all_s = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wv) {
+        pb += tot_b[w];
+        ps += tot_s[w];
+      }
+      all_b += tot_b[w];
+      all_s += tot_s[w];
+    }
+    pb += ib - nb;
+    ps += is - ns;
+    for (int i = 0; i < nb; ++i) g.big_tiles[pb + i] = make_int2(slot, i * kBigM);
+    for (int i = 0; i < ns; ++i) g.tiles[ps + i] = make_int2(slot, nb * kBigM + i * kBM);
     __syncthreads();
-    if (tid == 0) base_s += total;
+    if (tid == 0) {
+      base_b += all_b;
+      base_s += all_s;
+    }
     __syncthreads();
   }
-  if (tid == 0) g.n_tiles[0] = base_s;
+  if (tid == 0) {
+    g.n_tiles[0] = base_s;
+    g.n_big[0] = base_b;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -181,83 +224,16 @@ __device__ __forceinline__ f32x16_t offset_correction(float S, int half) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), z, 0, 0, 0);
 }
 
-// One K step (a 64-column scale group) of NM matrices x 2 column halves.
-template <int NM>
-struct KStep {
-  uint4 a[4];         // A fragments j = 0..3 (8 bf16 each)
-  uint4 q[NM][2];     // codes: 16 bytes = 4 words = 4 B fragments
-  float s[NM][2];     // group scales of this lane's columns
-};
-
-template <int NM>
-__device__ __forceinline__ void load_kstep(const uint16_t* arow, bool arow_ok, int grp,
-                                           const __amdgpu_buffer_rsrc_t (&rq)[NM],
-                                           const uint16_t* const (&srow)[NM][2], int col,
-                                           int half, KStep<NM>& st) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    st.a[j] = arow_ok ? *reinterpret_cast<const uint4*>(arow + grp * 64 + half * 32 + j * 8)
-                      : make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int mat = 0; mat < NM; ++mat) {
-#pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-          rq[mat], (2 * grp + half) * 1024 + (ns * 32 + col) * 16, 0, 0);
-      st.q[mat][ns] = make_uint4(v[0], v[1], v[2], v[3]);
-      st.s[mat][ns] = static_cast<float>(__builtin_bit_cast(_Float16, srow[mat][ns][grp]));
-    }
-  }
-}
-
-template <int NM>
-__device__ __forceinline__ void math_kstep(const KStep<NM>& st, int half,
-                                           f32x16_t (&acc)[NM][2]) {
-  float S = frag_sum(st.a[0]) + frag_sum(st.a[1]) + frag_sum(st.a[2]) + frag_sum(st.a[3]);
-  S += __shfl_xor(S, 32, kWave);
-  const f32x16_t corr = offset_correction(S, half);
-#pragma unroll
-  for (int mat = 0; mat < NM; ++mat) {
-#pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
-      f32x16_t p = corr;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(st.a[j]),
-                                                    dequant_word(word_of(st.q[mat][ns], j)), p,
-                                                    0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mat][ns][i] = fmaf(st.s[mat][ns], p[i], acc[mat][ns][i]);
-    }
-  }
-}
-
-// acc[mat][ns] = this wavefront's 32 x 64 tile of A [32 x K] times the
-// packed matrices (rows n0 .. n0+63 of each, K input columns), K/64 steps,
-// the next step's loads in flight during the current step's MFMAs.
-template <int NM>
-__device__ __forceinline__ void gemm_tile(const uint16_t* arow, bool arow_ok, int groups,
-                                          const __amdgpu_buffer_rsrc_t (&rq)[NM],
-                                          const uint16_t* const (&srow)[NM][2], int col,
-                                          int half, f32x16_t (&acc)[NM][2]) {
-#pragma unroll
-  for (int mat = 0; mat < NM; ++mat)
-#pragma unroll
-    for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mat][ns][i] = 0.0f;
-  KStep<NM> cur, nxt;
-  load_kstep<NM>(arow, arow_ok, 0, rq, srow, col, half, cur);
-  for (int grp = 0; grp < groups; ++grp) {
-    if (grp + 1 < groups) load_kstep<NM>(arow, arow_ok, grp + 1, rq, srow, col, half, nxt);
-    math_kstep<NM>(cur, half, acc);
-    cur = nxt;
-  }
-}
-
+// Buffer descriptor for `bytes` bytes at `base`.  The base is the same in
+// every lane; reading it through readfirstlane keeps the descriptor in
+// scalar registers even where the compiler cannot prove that.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), kRsrcWord3);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32)));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0), static_cast<int>(bytes),
+                                           kRsrcWord3);
 }
 
 // Output element i of a 32x32 MFMA tile held by lane (col, half) is row
@@ -265,112 +241,449 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ int out_row(int i, int half) { return (i >> 2) * 8 + half * 4 + (i & 3); }
 
 // ---------------------------------------------------------------------------
-// gate/up
+// 32-row tiles (small experts and the rows big tiles leave): bound by the
+// weight stream.  The workgroup stages the tile's activations for one
+// 64-column group at a time in LDS (double-buffered, with each row's sum);
+// every wavefront owns 16*NSUB columns of each of NM matrices, keeps kRing
+// groups of its codes in flight in registers, and multiplies both 16-row
+// blocks with v_mfma_f32_16x16x32_bf16, so each code is loaded and
+// dequantized once per tile.
+//
+// K order inside a 64-column group: lane quarter kq (lane / 16) covers the
+// 16 columns 16*kq .. 16*kq + 15, the first 8 in MFMA step 0 and the next 8
+// in step 1 -- for the codes one 8-byte load (words 2*(kq%2), +1 of chunk
+// kq/2), for the activations one 32-byte run.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kWaves * kWave) void prefill_gateup(PrefillArgs g) {
-  const int ti = blockIdx.y;
-  if (ti >= __builtin_amdgcn_readfirstlane(g.n_tiles[0])) return;
-  const int2 tile = g.tiles[ti];
-  const int slot = __builtin_amdgcn_readfirstlane(tile.x);
-  const int m0 = __builtin_amdgcn_readfirstlane(tile.y);
-  const Slot sl = resolve_slot(g, slot);
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * kWgCols + wv * kWaveCols;  // first f-row of this wavefront
-  if (n0 >= g.f) return;
-  const int col = lane & 31, half = lane >> 5;
-  const int m = m0 + col;
-  const bool ok = m < sl.M;
-  int tok = 0;
-  if (ok) tok = sl.shared ? m : g.perm[sl.p0 + m] / g.top_k;
-  const uint16_t* arow = g.x + static_cast<size_t>(tok) * g.d;
-  const size_t tq = static_cast<size_t>(n0 / 64) * 64 * (g.d / 2);
-  const __amdgpu_buffer_rsrc_t rq[2] = {make_rsrc(sl.blk + g.q_gate + tq, 32u * g.d),
-                                        make_rsrc(sl.blk + g.q_up + tq, 32u * g.d)};
-  const int groups = g.d / 64;
-  const uint16_t* sg = reinterpret_cast<const uint16_t*>(sl.blk + g.s_gate);
-  const uint16_t* su = reinterpret_cast<const uint16_t*>(sl.blk + g.s_up);
-  const uint16_t* const srow[2][2] = {
-      {sg + static_cast<size_t>(n0 + col) * groups, sg + static_cast<size_t>(n0 + 32 + col) * groups},
-      {su + static_cast<size_t>(n0 + col) * groups, su + static_cast<size_t>(n0 + 32 + col) * groups}};
-  f32x16_t acc[2][2];
-  gemm_tile<2>(arow, ok, groups, rq, srow, col, half, acc);
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRing = 4;  // groups of codes in flight per wavefront
+constexpr int kSmallRB = 2;  // 16-row blocks per small tile
+constexpr int kALdS = 72;    // LDS row stride of the small tile's A (bf16)
+constexpr int kSmallNSubGU = 4;  // 16-column subtiles per wavefront: gate/up (x2 matrices)
+constexpr int kSmallNSubDN = 8;  //   and down
+
+template <int NM, int NSUB>
+struct SmallCodes {
+  uint2 q[NM][NSUB];     // 2 words = 2 B fragments per subtile
+  _Float16 s[NM][NSUB];  // group scales of this lane's columns
+};
+
+template <int NM, int NSUB>
+__device__ __forceinline__ void small_codes(int grp, int groups, int kq,
+                                            const __amdgpu_buffer_rsrc_t (&rq)[NM],
+                                            const uint16_t* const (&srow)[NM][NSUB], int rt0,
+                                            SmallCodes<NM, NSUB>& st) {
+  const int gg = min(grp, groups - 1);
 #pragma unroll
-  for (int ns = 0; ns < 2; ++ns) {
-    const int n = n0 + ns * 32 + col;
+  for (int mat = 0; mat < NM; ++mat) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int mm = m0 + out_row(i, half);
-      if (mm < sl.M) {
-        const float hv = silu(acc[0][ns][i]) * acc[1][ns][i];
-        g.h[static_cast<size_t>(row_of(g, sl, mm)) * g.f + n] = f32_to_bf16(hv);
+    for (int sb = 0; sb < NSUB; ++sb) {
+      const int rt = rt0 + sb * 16;  // row from the first packed tile of the wavefront
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+          rq[mat], (rt >> 6) * 32 * (groups * 64) + (2 * gg + (kq >> 1)) * 1024 + (rt & 63) * 16 +
+                       (kq & 1) * 8, 0, 0);
+      st.q[mat][sb] = make_uint2(v[0], v[1]);
+      st.s[mat][sb] = __builtin_bit_cast(_Float16, srow[mat][sb][gg]);
+    }
+  }
+}
+
+__device__ __forceinline__ f32x4_t offset_correction16(float S, int kq) {
+  const uint32_t s_hi = f32_to_bf16(S);
+  const float r1 = S - __uint_as_float(s_hi << 16);
+  const uint32_t s_mid = f32_to_bf16(r1);
+  const float r2 = r1 - __uint_as_float(s_mid << 16);
+  const uint32_t s_lo = f32_to_bf16(r2);
+  const uint32_t m136 = f32_to_bf16(-136.0f);
+  uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+  if (kq == 0) {
+    a = make_uint4(s_hi | (s_mid << 16), s_lo, 0, 0);
+    b = make_uint4(m136 | (m136 << 16), m136, 0, 0);
+  }
+  f32x4_t z = {};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), z, 0, 0, 0);
+}
+
+// abuf: [32 rows][kALdS] bf16 then 32 row sums (float).
+template <int NM, int NSUB>
+__device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCodes<NM, NSUB>& st,
+                                           int col, int kq,
+                                           f32x4_t (&acc)[kSmallRB][NM][NSUB]) {
+  uint4 a[kSmallRB][2];
+  f32x4_t corr[kSmallRB];
+#pragma unroll
+  for (int rb = 0; rb < kSmallRB; ++rb) {
+    const int r = rb * 16 + col;
+    const uint4* ap = reinterpret_cast<const uint4*>(abuf + (r * kALdS + kq * 16) / 2);
+    a[rb][0] = ap[0];
+    a[rb][1] = ap[1];
+    corr[rb] = offset_correction16(reinterpret_cast<const float*>(abuf + 32 * kALdS / 2)[r], kq);
+  }
+#pragma unroll
+  for (int mat = 0; mat < NM; ++mat) {
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+      const bf16x8_t b0 = dequant_word(st.q[mat][sb].x), b1 = dequant_word(st.q[mat][sb].y);
+      const float sv = static_cast<float>(st.s[mat][sb]);
+#pragma unroll
+      for (int rb = 0; rb < kSmallRB; ++rb) {
+        f32x4_t p = corr[rb];
+        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][0]), b0, p, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][1]), b1, p, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[rb][mat][sb][e] = fmaf(sv, p[e], acc[rb][mat][sb][e]);
       }
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// down
-// ---------------------------------------------------------------------------
+// Staging of one group of the tile's A: thread t holds 8 columns of row
+// t / 8; the row's sum is reduced over its 8 threads (fixed order).
+__device__ __forceinline__ uint4 small_a_load(const uint16_t* arow, int grp) {
+  return arow ? *reinterpret_cast<const uint4*>(arow + grp * 64 + (threadIdx.x & 7) * 8)
+              : make_uint4(0, 0, 0, 0);
+}
 
-__global__ __launch_bounds__(kWaves * kWave) void prefill_down(PrefillArgs g) {
+__device__ __forceinline__ void small_a_store(uint32_t* abuf, const uint4& v) {
+  const int t = threadIdx.x, r = t >> 3, c8 = t & 7;
+  reinterpret_cast<uint4*>(abuf + (r * kALdS + c8 * 8) / 2)[0] = v;
+  float s = frag_sum(v);
+  s += __shfl_xor(s, 1, kWave);
+  s += __shfl_xor(s, 2, kWave);
+  s += __shfl_xor(s, 4, kWave);
+  if (c8 == 0) reinterpret_cast<float*>(abuf + 32 * kALdS / 2)[r] = s;
+}
+
+constexpr int kSmallBufWords = 32 * kALdS / 2 + 32;
+
+template <int NM, int NSUB, bool DOWN>
+__global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
+  constexpr int kWaveN = 16 * NSUB;
+  __shared__ __align__(16) uint32_t abufs[2][kSmallBufWords];
   const int ti = blockIdx.y;
   if (ti >= __builtin_amdgcn_readfirstlane(g.n_tiles[0])) return;
+  const int N = DOWN ? g.d : g.f, K = DOWN ? g.f : g.d;
   const int2 tile = g.tiles[ti];
   const int slot = __builtin_amdgcn_readfirstlane(tile.x);
   const int m0 = __builtin_amdgcn_readfirstlane(tile.y);
   const Slot sl = resolve_slot(g, slot);
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * kWgCols + wv * kWaveCols;  // first d-row of this wavefront
-  if (n0 >= g.d) return;
-  const int col = lane & 31, half = lane >> 5;
-  const int m = m0 + col;
-  const bool ok = m < sl.M;
-  const uint16_t* arow = g.h + static_cast<size_t>(ok ? row_of(g, sl, m) : 0) * g.f;
-  const size_t tq = static_cast<size_t>(n0 / 64) * 64 * (g.f / 2);
-  const __amdgpu_buffer_rsrc_t rq[1] = {make_rsrc(sl.blk + g.q_down + tq, 32u * g.f)};
-  const int groups = g.f / 64;
-  const uint16_t* sd = reinterpret_cast<const uint16_t*>(sl.blk + g.s_down);
-  const uint16_t* const srow[1][2] = {
-      {sd + static_cast<size_t>(n0 + col) * groups, sd + static_cast<size_t>(n0 + 32 + col) * groups}};
-  f32x16_t acc[1][2];
-  gemm_tile<1>(arow, ok, groups, rq, srow, col, half, acc);
+  const int groups = K / 64;
+  // A staging: thread t -> row t / 8 of the tile
+  const uint16_t* srcrow = nullptr;
+  {
+    const int m = m0 + (threadIdx.x >> 3);
+    if (m < sl.M) {
+      if (DOWN) {
+        srcrow = g.h + static_cast<size_t>(row_of(g, sl, m)) * g.f;
+      } else {
+        const int tok = sl.shared ? m : g.perm[sl.p0 + m] / g.top_k;
+        srcrow = g.x + static_cast<size_t>(tok) * g.d;
+      }
+    }
+  }
+  // the wavefront index is uniform: keep it (and the descriptors built from
+  // it) in scalar registers
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wv) * kWaveN;  // first output column of this wavefront
+  const bool active = n0 < N;                     // (barriers below need every wavefront)
+  const int col = lane & 15, kq = lane >> 4;
+  const int nb = active ? n0 : 0;
+  const size_t tq = static_cast<size_t>(nb / 64) * 32 * K;
+  const size_t qoff[2] = {DOWN ? g.q_down : g.q_gate, g.q_up};
+  const size_t soff[2] = {DOWN ? g.s_down : g.s_gate, g.s_up};
+  // packed tiles of this wavefront inside the matrix (reads past them give 0)
+  const int ntv = min((kWaveN + 63) / 64, (N - nb) / 64);
+  __amdgpu_buffer_rsrc_t rq[NM];
+  const uint16_t* srow[NM][NSUB];
 #pragma unroll
-  for (int ns = 0; ns < 2; ++ns) {
-    const int n = n0 + ns * 32 + col;
+  for (int mat = 0; mat < NM; ++mat) {
+    rq[mat] = make_rsrc(sl.blk + qoff[mat] + tq, 32u * K * ntv);
+    const uint16_t* sb = reinterpret_cast<const uint16_t*>(sl.blk + soff[mat]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int mm = m0 + out_row(i, half);
-      if (mm < sl.M) {
+    for (int s = 0; s < NSUB; ++s)
+      srow[mat][s] = sb + static_cast<size_t>(min(nb + s * 16 + col, N - 1)) * groups;
+  }
+  const int rt0 = nb % 64 + col;  // this lane's row inside the packed tile (subtile 0)
+
+  f32x4_t acc[kSmallRB][NM][NSUB];
+#pragma unroll
+  for (int rb = 0; rb < kSmallRB; ++rb)
+#pragma unroll
+    for (int mat = 0; mat < NM; ++mat)
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) acc[rb][mat][s] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  SmallCodes<NM, NSUB> ring[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) small_codes<NM, NSUB>(i, groups, kq, rq, srow, rt0, ring[i]);
+  uint4 anext = small_a_load(srcrow, 0);
+  small_a_store(abufs[0], anext);
+  __syncthreads();
+  for (int g0 = 0; g0 < groups; g0 += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      const int grp = g0 + i;
+      if (grp < groups) {
+        if (grp + 1 < groups) anext = small_a_load(srcrow, grp + 1);
+        if (active) small_math<NM, NSUB>(abufs[grp & 1], ring[i], col, kq, acc);
+        if (grp + 1 < groups) small_a_store(abufs[(grp + 1) & 1], anext);
+        __syncthreads();
+      }
+      small_codes<NM, NSUB>(grp + kRing, groups, kq, rq, srow, rt0, ring[i]);
+    }
+  }
+  if (!active) return;
+  // lane (col, kq) holds rows 4*kq + e of each block, column col of every subtile
+#pragma unroll
+  for (int rb = 0; rb < kSmallRB; ++rb) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int mm = m0 + rb * 16 + 4 * kq + e;
+      if (mm >= sl.M) continue;
+      if constexpr (DOWN) {
         uint16_t* out = sl.shared ? g.y_shared + static_cast<size_t>(mm) * g.d
                                   : g.y + static_cast<size_t>(sl.p0 + mm) * g.d;
-        out[n] = f32_to_bf16(acc[0][ns][i]);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          if (n0 + s * 16 + col < N) out[n0 + s * 16 + col] = f32_to_bf16(acc[rb][0][s][e]);
+      } else {
+        uint16_t* hrow = g.h + static_cast<size_t>(row_of(g, sl, mm)) * g.f;
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          hrow[n0 + s * 16 + col] = f32_to_bf16(silu(acc[rb][0][s][e]) * acc[rb][1][s][e]);
       }
     }
   }
 }
 
-// Upper bound of the M-tiles of a launch: every slot's rows rounded up.
-int max_tiles(int T, int k, int slots, bool has_shared) {
-  return (T * k + (has_shared ? T : 0)) / kBM + slots;
+// ---------------------------------------------------------------------------
+// 128-row tiles: A and the codes staged in LDS (double-buffered per 64-column
+// scale group) and shared by the 4 wavefronts, 2 along M x 2 along N; each
+// wavefront computes 64 rows x 32*NS columns of each of NM matrices.
+// ---------------------------------------------------------------------------
+
+constexpr int kALd = 72;  // LDS row stride of A in bf16 (64 + 16 bytes of padding)
+
+template <int NM, int NS>
+struct Big {
+  static constexpr int kWaveCols = 32 * NS;
+  static constexpr int kWgCols = 2 * kWaveCols;
+  static constexpr int kTilesN = kWgCols / 64;            // packed 64-row tiles per matrix
+  static constexpr int kAWords = kBigM * kALd / 2;        // A buffer (32-bit words)
+  static constexpr int kBWords = NM * kWgCols * 32 / 4;   // codes of one group
+  static constexpr int kBufWords = kAWords + kBigM + kBWords;
+  static int lds_bytes(int groups) {
+    return (2 * kBufWords + NM * kWgCols * groups / 2) * 4;
+  }
+};
+
+// Global loads of one group: this thread's 32 A columns of its row (rowp,
+// null past the slot's rows) and one 16-byte piece of the codes.
+// Packed tiles at or past ntv (the matrix ends there) read as zero.
+template <int NM, int NS>
+__device__ __forceinline__ void big_load(const uint16_t* rowp, int ahalf, int grp, int K, int ntv,
+                                         const uint8_t* const (&qbase)[NM], uint4 (&ra)[4],
+                                         uint4& rb) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    ra[j] = rowp ? *reinterpret_cast<const uint4*>(rowp + grp * 64 + ahalf * 32 + j * 8)
+                 : make_uint4(0, 0, 0, 0);
+  constexpr int kPer = 256 / NM;  // threads per matrix
+  const int t = threadIdx.x;
+  const int mat = t / kPer, r = t % kPer;
+  const int tt = r / 128, h = (r / 64) & 1, row = r & 63;
+  const uint8_t* src = qbase[0];
+#pragma unroll
+  for (int mm = 1; mm < NM; ++mm)
+    if (mat == mm) src = qbase[mm];
+  rb = tt < ntv ? *reinterpret_cast<const uint4*>(src + static_cast<size_t>(tt) * 32 * K +
+                                                  static_cast<size_t>(2 * grp + h) * 1024 + row * 16)
+                : make_uint4(0, 0, 0, 0);
 }
 
+// The loaded group into LDS buffer `buf`: A rows, their sums, the codes.
+template <int NM, int NS>
+__device__ __forceinline__ void big_store(uint32_t* buf, int arow, int ahalf, const uint4 (&ra)[4],
+                                          const uint4& rb) {
+  using C = Big<NM, NS>;
+  uint4* a = reinterpret_cast<uint4*>(buf + (arow * kALd + ahalf * 32) / 2);
+  float part = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = ra[j];
+    part += frag_sum(ra[j]);
+  }
+  const float other = __shfl_xor(part, 1, kWave);
+  if (ahalf == 0) reinterpret_cast<float*>(buf + C::kAWords)[arow] = part + other;
+  constexpr int kPer = 256 / NM;
+  const int t = threadIdx.x;
+  const int mat = t / kPer, r = t % kPer;
+  const int tt = r / 128, h = (r / 64) & 1, row = r & 63;
+  reinterpret_cast<uint4*>(buf + C::kAWords + kBigM)[(mat * 2 + h) * C::kWgCols + tt * 64 + row] = rb;
+}
+
+template <int NM, int NS>
+__device__ __forceinline__ void big_math(const uint32_t* buf, const uint16_t* sc, int groups,
+                                         int grp, int wm, int wn, int col, int half,
+                                         f32x16_t (&acc)[2][NM][NS]) {
+  using C = Big<NM, NS>;
+  uint4 a[2][4];
+  f32x16_t corr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wm * 64 + i * 32 + col;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[i][j] = *reinterpret_cast<const uint4*>(buf + (r * kALd + half * 32 + j * 8) / 2);
+    corr[i] = offset_correction(reinterpret_cast<const float*>(buf + C::kAWords)[r], half);
+  }
+  const uint4* bq = reinterpret_cast<const uint4*>(buf + C::kAWords + kBigM);
+#pragma unroll
+  for (int mat = 0; mat < NM; ++mat) {
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const int n = wn * C::kWaveCols + ns * 32 + col;  // column inside the workgroup
+      const uint4 q = bq[(mat * 2 + half) * C::kWgCols + n];
+      const float sv = static_cast<float>(
+          __builtin_bit_cast(_Float16, sc[(mat * C::kWgCols + n) * groups + grp]));
+      bf16x8_t bw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bw[j] = dequant_word(word_of(q, j));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f32x16_t p = corr[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][j]), bw[j], p, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = fmaf(sv, p[e], acc[i][mat][ns][e]);
+      }
+    }
+  }
+}
+
+template <int NM, int NS, bool DOWN>
+__global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
+  using C = Big<NM, NS>;
+  extern __shared__ __align__(16) uint32_t lds[];
+  const int ti = blockIdx.y;
+  if (ti >= __builtin_amdgcn_readfirstlane(g.n_big[0])) return;
+  const int N = DOWN ? g.d : g.f, K = DOWN ? g.f : g.d;
+  const int n0 = blockIdx.x * C::kWgCols;
+  if (n0 >= N) return;
+  const int2 tile = g.big_tiles[ti];
+  const int slot = __builtin_amdgcn_readfirstlane(tile.x);
+  const int m0 = __builtin_amdgcn_readfirstlane(tile.y);
+  const Slot sl = resolve_slot(g, slot);
+  const int groups = K / 64;
+  const int ntv = min(C::kTilesN, (N - n0) / 64);  // packed tiles inside the matrix
+  uint32_t* buf0 = lds;
+  uint32_t* buf1 = lds + C::kBufWords;
+  uint16_t* sc = reinterpret_cast<uint16_t*>(lds + 2 * C::kBufWords);  // [NM][kWgCols][groups]
+
+  const size_t soff[2] = {DOWN ? g.s_down : g.s_gate, g.s_up};
+  const size_t qoff[2] = {DOWN ? g.q_down : g.q_gate, g.q_up};
+  const uint8_t* qbase[NM];
+#pragma unroll
+  for (int mat = 0; mat < NM; ++mat) {
+    qbase[mat] = sl.blk + qoff[mat] + static_cast<size_t>(n0 / 64) * 32 * K;
+    const uint4* src = reinterpret_cast<const uint4*>(sl.blk + soff[mat] +
+                                                      static_cast<size_t>(n0) * groups * 2);
+    uint4* dst = reinterpret_cast<uint4*>(sc + mat * C::kWgCols * groups);
+    for (int i = threadIdx.x; i < ntv * 64 * groups / 8; i += 256) dst[i] = src[i];
+  }
+  const int t = threadIdx.x, arow = t >> 1, ahalf = t & 1;
+  const int m = m0 + arow;
+  const uint16_t* rowp = nullptr;
+  if (m < sl.M) {
+    if (DOWN) {
+      rowp = g.h + static_cast<size_t>(row_of(g, sl, m)) * g.f;
+    } else {
+      const int tok = sl.shared ? m : g.perm[sl.p0 + m] / g.top_k;
+      rowp = g.x + static_cast<size_t>(tok) * g.d;
+    }
+  }
+  const int wv = t >> 6, lane = t & 63;
+  const int wm = wv & 1, wn = wv >> 1, col = lane & 31, half = lane >> 5;
+
+  uint4 ra[4], rb;
+  big_load<NM, NS>(rowp, ahalf, 0, K, ntv, qbase, ra, rb);
+  big_store<NM, NS>(buf0, arow, ahalf, ra, rb);
+  __syncthreads();
+  f32x16_t acc[2][NM][NS];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int mat = 0; mat < NM; ++mat)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = 0.0f;
+  for (int grp = 0; grp < groups; ++grp) {
+    const bool more = grp + 1 < groups;
+    if (more) big_load<NM, NS>(rowp, ahalf, grp + 1, K, ntv, qbase, ra, rb);
+    big_math<NM, NS>((grp & 1) ? buf1 : buf0, sc, groups, grp, wm, wn, col, half, acc);
+    if (more) big_store<NM, NS>((grp & 1) ? buf0 : buf1, arow, ahalf, ra, rb);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int mm = m0 + wm * 64 + i * 32 + out_row(e, half);
+      if (mm >= sl.M) continue;
+      if constexpr (DOWN) {
+        uint16_t* out = sl.shared ? g.y_shared + static_cast<size_t>(mm) * g.d
+                                  : g.y + static_cast<size_t>(sl.p0 + mm) * g.d;
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          const int n = n0 + wn * C::kWaveCols + ns * 32 + col;
+          if (n < N) out[n] = f32_to_bf16(acc[i][0][ns][e]);
+        }
+      } else {
+        const float hv = silu(acc[i][0][0][e]) * acc[i][1][0][e];
+        g.h[static_cast<size_t>(row_of(g, sl, mm)) * g.f + n0 + wn * C::kWaveCols + col] =
+            f32_to_bf16(hv);
+      }
+    }
+  }
+}
+
+// Upper bounds of the M-tiles of a launch.  Every 128-row tile holds at
+// least kBigMinRows rows; a slot leaves fewer than kBigMinRows rows to
+// 16-row tiles, so at most six of them.
+int rows_of(int T, int k, bool has_shared) { return T * k + (has_shared ? T : 0); }
+int max_small(int T, int k, int slots, bool has_shared) {
+  return std::min(rows_of(T, k, has_shared) / kBM + slots, (kBigMinRows + kBM - 1) / kBM * slots);
+}
+int max_big(int T, int k, bool has_shared) { return rows_of(T, k, has_shared) / kBigMinRows + 1; }
+
 struct PrefillLayout {
-  size_t h, tiles, n_tiles, total;
+  size_t h, tiles, big_tiles, counts, total;
 };
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 PrefillLayout prefill_layout(int T, int k, int E, int f, bool has_shared) {
   PrefillLayout l{};
   const int slots = (has_shared ? 1 : 0) + std::min(E, T * k);
-  const size_t rows = static_cast<size_t>(T) * (k + (has_shared ? 1 : 0));
+  const size_t rows = rows_of(T, k, has_shared);
   l.h = 0;
-  size_t off = (rows * f * 2 + 255) / 256 * 256;
+  size_t off = align256(rows * f * 2);
   l.tiles = off;
-  off += (static_cast<size_t>(max_tiles(T, k, slots, has_shared)) * sizeof(int2) + 255) / 256 * 256;
-  l.n_tiles = off;
+  off += align256(static_cast<size_t>(max_small(T, k, slots, has_shared)) * sizeof(int2));
+  l.big_tiles = off;
+  off += align256(static_cast<size_t>(max_big(T, k, has_shared)) * sizeof(int2));
+  l.counts = off;
   off += 256;
   l.total = off;
   return l;
+}
+
+// Dynamic LDS above 64 KB has to be enabled per kernel.
+template <typename K>
+hipError_t allow_lds(K kernel, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 }  // namespace
@@ -405,17 +718,32 @@ hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream) {
   char* ws = static_cast<char*>(p.workspace);
   g.h = reinterpret_cast<uint16_t*>(ws + l.h);
   g.tiles = reinterpret_cast<int2*>(ws + l.tiles);
-  g.n_tiles = reinterpret_cast<int*>(ws + l.n_tiles);
+  g.big_tiles = reinterpret_cast<int2*>(ws + l.big_tiles);
+  g.n_tiles = reinterpret_cast<int*>(ws + l.counts);
+  g.n_big = g.n_tiles + 1;
   g.y = static_cast<uint16_t*>(p.y);
   g.y_shared = static_cast<uint16_t*>(p.y_shared);
-  const int mt = max_tiles(p.T, p.k, g.slots, p.has_shared);
-  hipError_t err = launch(prefill_tiles, dim3(1), dim3(1024), 0, stream, g);
+  const int ms = max_small(p.T, p.k, g.slots, p.has_shared);
+  const int mb = max_big(p.T, p.k, p.has_shared);
+  using GU = Big<2, 1>;
+  using DN = Big<1, 2>;
+  const int lds_gu = GU::lds_bytes(p.d / 64), lds_dn = DN::lds_bytes(p.f / 64);
+  if (lds_gu > kMaxLds || lds_dn > kMaxLds) return hipErrorNotSupported;
+  hipError_t err;
+  if ((err = allow_lds(prefill_big<2, 1, false>, lds_gu)) != hipSuccess) return err;
+  if ((err = allow_lds(prefill_big<1, 2, true>, lds_dn)) != hipSuccess) return err;
+  if ((err = launch(prefill_tiles, dim3(1), dim3(1024), 0, stream, g)) != hipSuccess) return err;
+  err = launch(prefill_big<2, 1, false>, dim3((p.f + GU::kWgCols - 1) / GU::kWgCols, mb),
+               dim3(256), lds_gu, stream, g);
   if (err != hipSuccess) return err;
-  err = launch(prefill_gateup, dim3((p.f + kWgCols - 1) / kWgCols, mt), dim3(kWaves * kWave), 0,
-               stream, g);
+  err = launch(prefill_small<2, kSmallNSubGU, false>,
+               dim3((p.f + 64 * kSmallNSubGU - 1) / (64 * kSmallNSubGU), ms), dim3(256), 0, stream, g);
   if (err != hipSuccess) return err;
-  return launch(prefill_down, dim3((p.d + kWgCols - 1) / kWgCols, mt), dim3(kWaves * kWave), 0,
-                stream, g);
+  err = launch(prefill_big<1, 2, true>, dim3((p.d + DN::kWgCols - 1) / DN::kWgCols, mb),
+               dim3(256), lds_dn, stream, g);
+  if (err != hipSuccess) return err;
+  return launch(prefill_small<1, kSmallNSubDN, true>,
+                dim3((p.d + 64 * kSmallNSubDN - 1) / (64 * kSmallNSubDN), ms), dim3(256), 0, stream, g);
 }
 
 }  // namespace moe
