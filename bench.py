@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="only run what the HBM-traffic counter passes measure: a 1 GiB device "
+                         "copy (calibration) and 20 decode expert-FFN launches")
     return ap.parse_args()
 
 
@@ -77,6 +80,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.counters:
+        return counter_workload(args, torch, moe, synth, LayerBuffers, run_layer, dev)
 
     # ------------------------------------------------------------------ data
     t0 = time.time()
@@ -206,7 +211,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": load_traffic(),
             "algorithmic_bytes_per_launch": step_bytes,
             "avg_launch_us": round(float(ffn_ms.mean()) * 1e3, 2),
         },
@@ -284,6 +289,70 @@ def bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts,
             "avg_launch_us": round(float(ffn_ms.mean()) * 1e3, 1),
         },
     }
+
+
+def counter_workload(args, torch, moe, synth, LayerBuffers, run_layer, dev):
+    """The workload of the FETCH_SIZE / WRITE_SIZE counter passes: a plain
+    1 GiB device-to-device copy, three times (reads and writes exactly 2^30
+    bytes each: the calibration of the counters), then 20 one-token decode
+    expert-FFN launches on rotating layer copies, as in the timed run."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    L = synth.make_layer(4)
+    sh = moe.shape_of(L.shape)
+    src = torch.from_numpy(L.experts).to(dev)
+    experts = [torch.empty_like(src)]
+    moe.moe_pack_experts(sh, L.shape.n_experts, src, experts[0])
+    del src
+    src = torch.from_numpy(L.shared[None]).to(dev)
+    shared = [torch.empty_like(src)[0]]
+    moe.moe_pack_experts(sh, 1, src, shared[0])
+    del src
+    for _ in range(3):
+        experts.append(experts[0].clone())
+        shared.append(shared[0].clone())
+    w_router = torch.from_numpy(L.w_router).to(dev)
+    DEC = moe.MOE_PATH_DECODE_F32
+    xs, bufs = [], []
+    for i in range(4):
+        bits, _ = synth.make_tokens(4, 1, batch=i)
+        xs.append(torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16))
+        bufs.append(LayerBuffers.allocate(sh, 1, DEC))
+        run_layer(xs[i], w_router, None, experts[i], shared[i], bufs[i])
+    torch.cuda.synchronize()
+    for i in range(20):
+        b = bufs[i % 4]
+        moe.moe_expert_ffn(sh, xs[i % 4], experts[i % 4], shared[i % 4], b.offsets, b.perm,
+                           b.active, b.n_active, DEC, b.y, b.y_shared, b.ffn_workspace)
+    torch.cuda.synchronize()
+    active = [int(b.n_active.item()) + 1 for b in bufs]
+    log(f"counter workload done: copy 3 x {n} B; 20 decode FFN launches of {active} expert blocks")
+    return 0
+
+
+def load_traffic():
+    """HBM bytes per decode expert-FFN launch from the committed counter
+    summary, or None when the decode kernel source has changed since the
+    counters were taken (its SHA-256 is recorded with them)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_ffn_traffic.json")
+    src = os.path.join(ROOT, "int4_routed_expert_logits_amd", "csrc", "ffn_decode.hip")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+        with open(src, "rb") as fh:
+            digest = hashlib.sha256(fh.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(L, bb):
