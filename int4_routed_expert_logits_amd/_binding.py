@@ -25,8 +25,7 @@ MOE_PATH_DECODE_F32, MOE_PATH_PREFILL_BF16 = 0, 1
 
 # every function include/moe_int4.h declares
 EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_route_workspace_bytes", "moe_route",
-           "moe_union", "moe_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
-           "moe_status_str")
+           "moe_union", "moe_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_status_str")
 
 
 class Shape(ctypes.Structure):

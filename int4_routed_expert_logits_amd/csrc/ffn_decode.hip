@@ -61,6 +61,9 @@ constexpr int kDnRows = 16;    // down rows per wavefront
 constexpr int kDnParts = 4;    // lanes per down row
 constexpr int kDnWaves = 4;    // wavefronts per down workgroup (64 rows)
 constexpr int kSkewWords = 4;  // LDS skew between the parts of a row (16 bytes)
+static_assert(kGuRows * kGuParts == kWave && kDnRows * kDnParts == kWave, "lane split");
+static_assert(64 % (kGuRows * kGuWaves) == 0 && 64 % (kDnRows * kDnWaves) == 0,
+              "a workgroup's rows stay inside one packed 64-row tile");
 
 struct FfnArgs {
   const uint8_t* experts;
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g) {
   const int row0 = blockIdx.x * kGuWaves * kGuRows;  // first f-row of the workgroup
   const int tile = row0 / 64;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & (kGuRows - 1), p = lane >> 3;
+  const int r = lane % kGuRows, p = lane / kGuRows;
   const int rt = row0 % 64 + wv * kGuRows + r;  // row inside the tile
   const StageLayout L = stage_layout(g.d / 32, kGuParts, XW);
   constexpr int kRowsWg = kGuWaves * kGuRows;
@@ -403,14 +406,13 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m >= nt) break;
-      // sum over the row's 8 lanes (lane bits 3..5), fixed order
+      // sum over the row's lanes (one per part), fixed order
       float gs = acc[0][m], us = acc[1][m];
-      gs += __shfl_xor(gs, 8, kWave);
-      us += __shfl_xor(us, 8, kWave);
-      gs += __shfl_xor(gs, 16, kWave);
-      us += __shfl_xor(us, 16, kWave);
-      gs += __shfl_xor(gs, 32, kWave);
-      us += __shfl_xor(us, 32, kWave);
+#pragma unroll
+      for (int off = kGuRows; off < kWave; off <<= 1) {
+        gs += __shfl_xor(gs, off, kWave);
+        us += __shfl_xor(us, off, kWave);
+      }
       const float h = silu(gs) * us;
       const uint32_t hi = f32_to_bf16(h);
       const uint32_t lo = f32_to_bf16(h - __uint_as_float(hi << 16));
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
   const int row0 = blockIdx.x * kDnWaves * kDnRows;  // first d-row of the workgroup
   const int tile = row0 / 64;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & (kDnRows - 1), p = lane >> 4;
+  const int r = lane % kDnRows, p = lane / kDnRows;
   const int rt = row0 % 64 + wv * kDnRows + r;
   const StageLayout L = stage_layout(g.f / 32, kDnParts, 32);
   constexpr int kRowsWg = kDnWaves * kDnRows;
@@ -470,8 +472,8 @@ __global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
     for (int m = 0; m < MT; ++m) {
       if (m >= nt) break;
       float ys = acc[0][m];
-      ys += __shfl_xor(ys, 16, kWave);
-      ys += __shfl_xor(ys, 32, kWave);
+#pragma unroll
+      for (int off = kDnRows; off < kWave; off <<= 1) ys += __shfl_xor(ys, off, kWave);
       if (p == 0) {
         float* out = sl.shared ? g.y_shared + static_cast<size_t>(m0 + m) * g.d
                                : g.y + static_cast<size_t>(sl.p0 + m0 + m) * g.d;

@@ -50,6 +50,42 @@ __device__ __forceinline__ float x_at<float>(const void* x, size_t idx) {
 constexpr int kTokGroup = 8;
 constexpr int kSplitMaxT = 32;  // larger batches use the tiled kernel
 
+// Partial float64 sums of tokens t0 .. t0+kTokGroup-1 against router row e
+// over columns [i0, i1), each lane its strided share.
+template <bool XBF16>
+__device__ __forceinline__ void logits_part(const void* __restrict__ x, const float* __restrict__ w,
+                                            int T, int d, int e, int i0, int i1, int t0, int lane,
+                                            double (&acc)[kTokGroup]) {
+  const float* wr = w + static_cast<size_t>(e) * d;
+#pragma unroll
+  for (int tt = 0; tt < kTokGroup; ++tt) acc[tt] = 0.0;
+  // four 256-column steps per pass, their router loads issued together
+  for (int ib = i0 + lane * 4; ib < i1; ib += 4 * 256) {
+    float4 wv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = ib + u * 256;
+      wv[u] = i < i1 ? *reinterpret_cast<const float4*>(wr + i) : make_float4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = ib + u * 256;
+      if (i >= i1) break;
+#pragma unroll
+      for (int tt = 0; tt < kTokGroup; ++tt) {
+        if (t0 + tt < T) {
+          float xv[4];
+          load_x4<XBF16>(x, static_cast<size_t>(t0 + tt) * d + i, xv);
+          acc[tt] = fma(static_cast<double>(xv[0]), static_cast<double>(wv[u].x), acc[tt]);
+          acc[tt] = fma(static_cast<double>(xv[1]), static_cast<double>(wv[u].y), acc[tt]);
+          acc[tt] = fma(static_cast<double>(xv[2]), static_cast<double>(wv[u].z), acc[tt]);
+          acc[tt] = fma(static_cast<double>(xv[3]), static_cast<double>(wv[u].w), acc[tt]);
+        }
+      }
+    }
+  }
+}
+
 template <bool XBF16>
 __global__ __launch_bounds__(256) void logits_split(const void* __restrict__ x,
                                                      const float* __restrict__ w,
@@ -60,25 +96,9 @@ __global__ __launch_bounds__(256) void logits_split(const void* __restrict__ x,
   if (item >= E * P) return;
   const int e = item / P, p = item - e * P;
   const int i0 = p * L, i1 = min(d, i0 + L);
-  const float* wr = w + static_cast<size_t>(e) * d;
   for (int t0 = 0; t0 < T; t0 += kTokGroup) {
     double acc[kTokGroup];
-#pragma unroll
-    for (int tt = 0; tt < kTokGroup; ++tt) acc[tt] = 0.0;
-    for (int i = i0 + lane * 4; i < i1; i += 256) {
-      const float4 wv = *reinterpret_cast<const float4*>(wr + i);
-#pragma unroll
-      for (int tt = 0; tt < kTokGroup; ++tt) {
-        if (t0 + tt < T) {
-          float xv[4];
-          load_x4<XBF16>(x, static_cast<size_t>(t0 + tt) * d + i, xv);
-          acc[tt] = fma(static_cast<double>(xv[0]), static_cast<double>(wv.x), acc[tt]);
-          acc[tt] = fma(static_cast<double>(xv[1]), static_cast<double>(wv.y), acc[tt]);
-          acc[tt] = fma(static_cast<double>(xv[2]), static_cast<double>(wv.z), acc[tt]);
-          acc[tt] = fma(static_cast<double>(xv[3]), static_cast<double>(wv.w), acc[tt]);
-        }
-      }
-    }
+    logits_part<XBF16>(x, w, T, d, e, i0, i1, t0, lane, acc);
 #pragma unroll
     for (int tt = 0; tt < kTokGroup; ++tt) {
       if (t0 + tt < T) {
@@ -89,70 +109,79 @@ __global__ __launch_bounds__(256) void logits_split(const void* __restrict__ x,
   }
 }
 
-// 64 tokens x 64 experts per workgroup, 4x4 outputs per thread, K step 16.
-constexpr int kTile = 64;
+// Large batches: 128 tokens x 128 experts per workgroup over one of P parts
+// of d, 8x8 float64 outputs per thread (16 LDS reads feed 64 FMAs), K steps
+// of 16 staged in LDS.  Each thread sums its part in column order and writes
+// part[t][e][p]; the top-k kernel adds the parts in order, so the result is
+// fixed by the layer shape.
+constexpr int kTile = 128;
 constexpr int kStep = 16;
+constexpr int kLdT = kTile + 1;
 
 template <typename XT>
 __global__ __launch_bounds__(256) void logits_tiled(const void* __restrict__ x,
                                                      const float* __restrict__ w,
-                                                     const float* __restrict__ bias,
-                                                     double* __restrict__ logits, int T, int d,
-                                                     int E) {
-  __shared__ double xs[kStep][kTile + 1];
-  __shared__ double ws[kStep][kTile + 1];
+                                                     double* __restrict__ part, int T, int d,
+                                                     int E, int P, int L) {
+  __shared__ double xs[kStep][kLdT];
+  __shared__ double ws[kStep][kLdT];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int e0 = blockIdx.x * kTile, t0 = blockIdx.y * kTile;
-  double acc[4][4];
+  const int e0 = blockIdx.x * kTile, t0 = blockIdx.y * kTile, p = blockIdx.z;
+  const int k_begin = p * L, k_end = min(d, k_begin + L);
+  double acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  for (int k0 = 0; k0 < d; k0 += kStep) {
-    for (int i = threadIdx.x; i < kTile * kStep; i += 256) {
-      const int r = i / kStep, c = i % kStep;
-      const int t = t0 + r, e = e0 + r;
-      xs[c][r] = t < T ? static_cast<double>(x_at<XT>(x, static_cast<size_t>(t) * d + k0 + c)) : 0.0;
-      ws[c][r] = e < E ? static_cast<double>(w[static_cast<size_t>(e) * d + k0 + c]) : 0.0;
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+  // staging: thread -> row r (0..127), 8 consecutive columns
+  const int sr = threadIdx.x >> 1, sc = (threadIdx.x & 1) * 8;
+  const int st = t0 + sr, se = e0 + sr;
+  for (int k0 = k_begin; k0 < k_end; k0 += kStep) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int k = k0 + sc + c;
+      const bool in = k < k_end;
+      xs[sc + c][sr] = (st < T && in) ? static_cast<double>(x_at<XT>(x, static_cast<size_t>(st) * d + k)) : 0.0;
+      ws[sc + c][sr] = (se < E && in) ? static_cast<double>(w[static_cast<size_t>(se) * d + k]) : 0.0;
     }
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < kStep; ++c) {
-      double a[4], bb[4];
+      double a[8], bb[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[c][ty * 4 + i];
+      for (int i = 0; i < 8; ++i) a[i] = xs[c][ty + 16 * i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bb[j] = ws[c][tx * 4 + j];
+      for (int j = 0; j < 8; ++j) bb[j] = ws[c][tx + 16 * j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], bb[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], bb[j], acc[i][j]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
+  for (int i = 0; i < 8; ++i) {
+    const int t = t0 + ty + 16 * i;
     if (t >= T) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) logits[static_cast<size_t>(t) * E + e] = acc[i][j] + (bias ? static_cast<double>(bias[e]) : 0.0);
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + tx + 16 * j;
+      if (e < E) part[(static_cast<size_t>(t) * E + e) * P + p] = acc[i][j];
     }
   }
 }
 
-// Top-k and softmax, one wavefront per token, E <= 64*NPL.
+// Top-k and softmax of one token by one wavefront, E <= 64*NPL.
 //
 // The logit of expert e is the in-order sum of its P partial sums plus the
 // bias.  Selection is exact on the float64 logits with ties to the lower id.
 // It first narrows the field with float32 copies: rounding to float32 is
-// monotone, so the k best experts all have float32 keys at or above the k-th
-// largest float32 key tau, found by a 32-step bitwise search with ballots.
-// The (usually exactly k) candidates at or above tau are then ranked by
-// (float64 logit desc, id asc) against each other.  If more than 64
-// candidates share the cut (mass ties), k rounds of a wave-wide argmax over
-// all experts decide instead.
+// monotone, so the k best experts all have float32 keys at or above tau, the
+// k-th largest float32 key (found by k rounds of a wave-wide maximum, each
+// taking one key out).  The (usually exactly k) candidates at or above tau
+// are then ranked by (float64 logit desc, id asc) against each other.  If
+// more than 64 candidates share the cut (mass ties), k rounds of a wave-wide
+// argmax over all experts decide instead.
 constexpr int kMaxK = 32;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -160,43 +189,89 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the wavefront, in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror
+  const uint32_t a = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
+  const uint32_t b = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
+  const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
+  const uint32_t d = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+  return max(max(a, b), max(c, d));
+}
+
+// LDS scratch of one wavefront.
+struct TopkLds {
+  double cand_v[64];
+  int cand_e[64];
+  double sel_v[kMaxK];
+  int sel_e[kMaxK];
+  double sel_p[kMaxK];
+};
+
 template <int NPL>
-__global__ __launch_bounds__(256) void topk_softmax(const double* __restrict__ part, int P,
-                                                    const float* __restrict__ bias, int T, int E,
-                                                    int k, int32_t* __restrict__ topk_idx,
-                                                    float* __restrict__ topk_w) {
-  __shared__ double cand_v[4][64];
-  __shared__ int cand_e[4][64];
-  __shared__ double sel_v[4][kMaxK];
-  __shared__ int sel_e[4][kMaxK];
-  __shared__ double sel_p[4][kMaxK];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wv;
-  if (t >= T) return;
+__device__ void topk_token(const double* __restrict__ part, int P, const float* __restrict__ bias,
+                           int t, int E, int k, int32_t* __restrict__ topk_idx,
+                           float* __restrict__ topk_w, TopkLds& sh) {
+  const int lane = threadIdx.x & 63;
   const uint64_t lower = (1ull << lane) - 1ull;
   double v[NPL];
   uint32_t key[NPL];
+  // every lane's partial sums are loaded before any is added; route_parts
+  // gives P <= 2048 / E (at most 16), so E <= 64 * NPL bounds it
+  constexpr int kMaxParts = NPL <= 4 ? 16 : (NPL == 8 ? 8 : 4);
+  double pv[NPL][kMaxParts];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    const double* q = part + (static_cast<size_t>(t) * E + e) * P;
+#pragma unroll
+    for (int pp = 0; pp < kMaxParts; ++pp) pv[i][pp] = q[min(pp, P - 1)];
+  }
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
     double s = -__builtin_inf();
     if (e < E) {
-      const double* q = part + (static_cast<size_t>(t) * E + e) * P;
-      s = q[0];
-      for (int pp = 1; pp < P; ++pp) s += q[pp];
+      s = pv[i][0];
+#pragma unroll
+      for (int pp = 1; pp < kMaxParts; ++pp)
+        if (pp < P) s += pv[i][pp];
       if (bias) s += static_cast<double>(bias[e]);
       if (s != s) s = -__builtin_inf();  // NaN ranks as -inf
     }
     v[i] = s;
-    key[i] = e < E ? order_key(static_cast<float>(s)) : 0u;
+    key[i] = e < E ? order_key(static_cast<float>(s)) : 0u;  // real keys are > 0
   }
-  uint32_t tau = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = tau | (1u << bit);
-    int cnt = 0;
+  // tau: take the largest remaining key out, k times
+  uint32_t wk[NPL];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) cnt += __popcll(__ballot(key[i] >= c));
-    if (cnt >= k) tau = c;
+  for (int i = 0; i < NPL; ++i) wk[i] = key[i];
+  uint32_t tau = 0;
+  for (int j = 0; j < k; ++j) {
+    uint32_t lm = wk[0];
+#pragma unroll
+    for (int i = 1; i < NPL; ++i) lm = max(lm, wk[i]);
+    tau = wave_max_u32(lm);
+    const uint64_t who = __ballot(lm == tau);
+    if (lane == __ffsll(static_cast<unsigned long long>(who)) - 1) {
+      bool done = false;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        if (!done && wk[i] == tau) {
+          wk[i] = 0;
+          done = true;
+        }
+      }
+    }
   }
   int nc = 0;
 #pragma unroll
@@ -205,25 +280,25 @@ __global__ __launch_bounds__(256) void topk_softmax(const double* __restrict__ p
     const uint64_t m = __ballot(in);
     const int pos = nc + __popcll(m & lower);
     if (in && pos < 64) {
-      cand_v[wv][pos] = v[i];
-      cand_e[wv][pos] = lane + 64 * i;
+      sh.cand_v[pos] = v[i];
+      sh.cand_e[pos] = lane + 64 * i;
     }
     nc += __popcll(m);
   }
   __builtin_amdgcn_wave_barrier();
   if (nc <= 64) {
     if (lane < nc) {
-      const double mv = cand_v[wv][lane];
-      const int me = cand_e[wv][lane];
+      const double mv = sh.cand_v[lane];
+      const int me = sh.cand_e[lane];
       int rank = 0;
       for (int q = 0; q < nc; ++q) {
-        const double ov = cand_v[wv][q];
-        const int oe = cand_e[wv][q];
+        const double ov = sh.cand_v[q];
+        const int oe = sh.cand_e[q];
         rank += (ov > mv || (ov == mv && oe < me)) ? 1 : 0;
       }
       if (rank < k) {
-        sel_v[wv][rank] = mv;
-        sel_e[wv][rank] = me;
+        sh.sel_v[rank] = mv;
+        sh.sel_e[rank] = me;
       }
     }
   } else {
@@ -249,48 +324,68 @@ __global__ __launch_bounds__(256) void topk_softmax(const double* __restrict__ p
       }
       if ((be & 63) == lane) taken |= 1u << (be >> 6);
       if (lane == 0) {
-        sel_v[wv][j] = bv;
-        sel_e[wv][j] = be;
+        sh.sel_v[j] = bv;
+        sh.sel_e[j] = be;
       }
     }
   }
   __builtin_amdgcn_wave_barrier();
   // softmax over the chosen k in float64: p_j = exp(l_j - l_0), z summed in j order
-  const double m = sel_v[wv][0];
-  const double pj = lane < k ? exp(sel_v[wv][lane] - m) : 0.0;
-  if (lane < k) sel_p[wv][lane] = pj;
+  const double m = sh.sel_v[0];
+  const double pj = lane < k ? exp(sh.sel_v[lane] - m) : 0.0;
+  if (lane < k) sh.sel_p[lane] = pj;
   __builtin_amdgcn_wave_barrier();
   double z = 0.0;
-  for (int j = 0; j < k; ++j) z += sel_p[wv][j];
+  for (int j = 0; j < k; ++j) z += sh.sel_p[j];
   if (lane < k) {
-    topk_idx[static_cast<size_t>(t) * k + lane] = sel_e[wv][lane];
+    topk_idx[static_cast<size_t>(t) * k + lane] = sh.sel_e[lane];
     topk_w[static_cast<size_t>(t) * k + lane] = static_cast<float>(pj / z);
   }
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void topk_softmax(const double* __restrict__ part, int P,
+                                                    const float* __restrict__ bias, int T, int E,
+                                                    int k, int32_t* __restrict__ topk_idx,
+                                                    float* __restrict__ topk_w) {
+  __shared__ TopkLds sh[4];
+  const int wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  topk_token<NPL>(part, P, bias, t, E, k, topk_idx, topk_w, sh[wv]);
 }
 
 }  // namespace
 
+// Parts of d per logit, the same rule for every batch in a size class: the
+// split kernel spreads the router matrix over E*P wavefronts; the tiled
+// kernel cuts d into parts of at least 384 columns.  The top-k kernel holds
+// up to 16 parts for E <= 256, 8 for E <= 512, 4 beyond.
 int route_parts(int T, int d, int E) {
-  if (T > kSplitMaxT) return 0;
-  int P = 2048 / E;
-  P = P < 1 ? 1 : (P > 16 ? 16 : P);
-  const int by_len = d / 256;
-  if (P > by_len) P = by_len < 1 ? 1 : by_len;
-  return P;
+  const int cap = E <= 256 ? 16 : (E <= 512 ? 8 : 4);
+  int P;
+  if (T <= kSplitMaxT) {
+    P = 2048 / E;
+    const int by_len = d / 256;
+    if (P > by_len) P = by_len;
+  } else {
+    P = d / 384;
+  }
+  return P < 1 ? 1 : (P > cap ? cap : P);
 }
 
 size_t route_workspace(int T, int d, int E) {
-  const int P = route_parts(T, d, E);
-  return static_cast<size_t>(T) * E * (P > 0 ? P : 1) * sizeof(double);
+  return static_cast<size_t>(T) * E * route_parts(T, d, E) * sizeof(double);
 }
 
 hipError_t launch_route(int T, int d, int E, int k, const void* x, bool x_bf16,
                         const float* w_router, const float* bias, double* logits,
                         int32_t* topk_idx, float* topk_w, hipStream_t stream) {
   hipError_t err;
-  int P = route_parts(T, d, E);
+  const int P = route_parts(T, d, E);
   const float* topk_bias = bias;
-  if (P > 0) {
+  if (T <= kSplitMaxT) {
     const int L = ((d + P - 1) / P + 3) / 4 * 4;
     const dim3 grid((E * P + 3) / 4);
     err = x_bf16 ? launch(logits_split<true>, grid, dim3(256), 0, stream, x, w_router, logits, T,
@@ -298,13 +393,12 @@ hipError_t launch_route(int T, int d, int E, int k, const void* x, bool x_bf16,
                  : launch(logits_split<false>, grid, dim3(256), 0, stream, x, w_router, logits,
                           T, d, E, P, L);
   } else {
-    P = 1;
-    topk_bias = nullptr;  // the tiled kernel adds the bias itself
-    const dim3 grid((E + kTile - 1) / kTile, (T + kTile - 1) / kTile);
-    err = x_bf16 ? launch(logits_tiled<uint16_t>, grid, dim3(256), 0, stream, x, w_router, bias,
-                          logits, T, d, E)
-                 : launch(logits_tiled<float>, grid, dim3(256), 0, stream, x, w_router, bias,
-                          logits, T, d, E);
+    const int L = ((d + P - 1) / P + kStep - 1) / kStep * kStep;
+    const dim3 grid((E + kTile - 1) / kTile, (T + kTile - 1) / kTile, P);
+    err = x_bf16 ? launch(logits_tiled<uint16_t>, grid, dim3(256), 0, stream, x, w_router,
+                          logits, T, d, E, P, L)
+                 : launch(logits_tiled<float>, grid, dim3(256), 0, stream, x, w_router, logits,
+                          T, d, E, P, L);
   }
   if (err != hipSuccess) return err;
   const dim3 grid((T + 3) / 4);

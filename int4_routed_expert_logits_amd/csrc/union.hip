@@ -11,6 +11,7 @@
 // one regardless of the order in which hardware atomics land.
 #include "common.h"
 #include "launch.h"
+#include "union_wave.h"
 
 namespace moe {
 
@@ -134,11 +135,7 @@ __global__ __launch_bounds__(kThreads) void batch_union(const int32_t* __restric
 }
 
 // Small batches (at most 64 slots, e.g. decode up to 8 tokens at k=8): one
-// wavefront, no workgroup barriers.  Lane s holds slot s; the histogram is
-// built with LDS atomics, every lane scans a contiguous block of E/64
-// experts, and a slot's grouped position is its expert's offset plus the
-// number of lower slots with the same expert (ballot rank), which is the
-// stable order by (expert, slot).
+// wavefront, no workgroup barriers (union_wave.h).
 template <int EPL>
 __global__ __launch_bounds__(64) void batch_union_small(const int32_t* __restrict__ topk_idx,
                                                          int n, int E,
@@ -151,74 +148,8 @@ __global__ __launch_bounds__(64) void batch_union_small(const int32_t* __restric
   __shared__ int cnt[64 * EPL];
   __shared__ int first[64 * EPL];
   const int lane = threadIdx.x;
-  int e = lane < n ? topk_idx[lane] : -1;
-  const bool valid = e >= 0 && e < E;
-  if (!valid) e = -1;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) cnt[lane * EPL + i] = 0;
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  if (valid) atomicAdd(&cnt[e], 1);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  // this lane's block of experts [lane*EPL, lane*EPL + EPL)
-  int c[EPL];
-  int sum = 0, act = 0;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    c[i] = cnt[lane * EPL + i];
-    sum += c[i];
-    act += c[i] > 0 ? 1 : 0;
-  }
-  int isum = sum, iact = act;  // inclusive scans over lanes
-  for (int off = 1; off < 64; off <<= 1) {
-    const int os = __shfl_up(isum, off, 64);
-    const int oa = __shfl_up(iact, off, 64);
-    if (lane >= off) {
-      isum += os;
-      iact += oa;
-    }
-  }
-  int base = isum - sum, abase = iact - act;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int ee = lane * EPL + i;
-    if (ee < E) {
-      counts[ee] = c[i];
-      offsets[ee] = base;
-      if (c[i] > 0) active[abase++] = ee;
-    }
-    first[ee] = base;
-    base += c[i];
-  }
-  const int total = __shfl(isum, 63, 64);
-  const int n_act = __shfl(iact, 63, 64);
-  for (int i = n_act + lane; i < E; i += 64) active[i] = -1;
-  if (lane == 0) {
-    offsets[E] = total;
-    n_active[0] = n_act;
-  }
-  __builtin_amdgcn_wave_barrier();
-  // rank among lower lanes with the same expert
-  int rank = 0;
-  uint64_t pending = __ballot(valid);
-  const uint64_t lower = (1ull << lane) - 1ull;
-  while (pending) {
-    const int leader = __ffsll(static_cast<unsigned long long>(pending)) - 1;
-    const int key = __shfl(e, leader, 64);
-    const uint64_t same = __ballot(valid && e == key);
-    if (valid && e == key) rank = __popcll(same & lower);
-    pending &= ~same;
-  }
-  if (lane < n) {
-    if (valid) {
-      const int pos = first[e] + rank;
-      perm[pos] = lane;
-      inv_perm[lane] = pos;
-    } else {
-      inv_perm[lane] = -1;
-    }
-  }
+  const int e = lane < n ? topk_idx[lane] : -1;
+  union_wave<EPL>(e, n, E, counts, offsets, perm, inv_perm, active, n_active, cnt, first);
 }
 
 }  // namespace

@@ -108,29 +108,27 @@ def test_route_parity(cfg, T):
     gap = min_gap(lg, k)
     assert np.array_equal(idx.cpu().numpy(), ridx), f"top-k differs (smallest k/k+1 logit gap {gap:.3e})"
     assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-6
-    # the gpu logits themselves (float64, summation order aside); small batches
-    # leave per-part partial sums in the workspace, large ones whole logits
+    # the gpu logits themselves (float64, summation order aside): the workspace
+    # holds P partial sums per (token, expert); their in-order sum plus the
+    # bias is the logit
     P = route_parts(T, sh.d, sh.n_experts)
-    raw = ws[: T * sh.n_experts * max(P, 1) * 8].view(torch.float64).cpu().numpy()
-    if P:
-        part = raw.reshape(T, sh.n_experts, P)
-        glg = part[:, :, 0].copy()
-        for p in range(1, P):
-            glg += part[:, :, p]
-        if L.bias is not None:
-            glg += L.bias.astype(np.float64)
-    else:
-        glg = raw.reshape(T, sh.n_experts)
+    part = ws[: T * sh.n_experts * P * 8].view(torch.float64).cpu().numpy().reshape(T, sh.n_experts, P)
+    glg = part[:, :, 0].copy()
+    for p in range(1, P):
+        glg += part[:, :, p]
+    if L.bias is not None:
+        glg += L.bias.astype(np.float64)
     assert np.max(np.abs(glg - lg)) <= 1e-12 * max(1.0, np.max(np.abs(lg)))
 
 
 def route_parts(T, d, E):
-    """Parts the small-batch logit kernel splits each router row into (0 for
-    the tiled large-batch kernel); mirrors the library's host rule."""
-    if T > 32:
-        return 0
-    P = min(max(2048 // E, 1), 16)
-    return max(1, min(P, d // 256)) if P > d // 256 else P
+    """Parts of d per router logit; mirrors the library's host rule."""
+    cap = 16 if E <= 256 else (8 if E <= 512 else 4)
+    if T <= 32:
+        P = min(2048 // E, d // 256)
+    else:
+        P = d // 384
+    return max(1, min(P, cap))
 
 
 def _route_fine(E, k, T=1):
