@@ -264,14 +264,12 @@ constexpr int kSmallNSubDN = 8;  //   and down
 
 template <int NM, int NSUB>
 struct SmallCodes {
-  uint2 q[NM][NSUB];     // 2 words = 2 B fragments per subtile
-  _Float16 s[NM][NSUB];  // group scales of this lane's columns
+  uint2 q[NM][NSUB];  // 2 words = 2 B fragments per subtile
 };
 
 template <int NM, int NSUB>
 __device__ __forceinline__ void small_codes(int grp, int groups, int kq,
-                                            const __amdgpu_buffer_rsrc_t (&rq)[NM],
-                                            const uint16_t* const (&srow)[NM][NSUB], int rt0,
+                                            const __amdgpu_buffer_rsrc_t (&rq)[NM], int rt0,
                                             SmallCodes<NM, NSUB>& st) {
   const int gg = min(grp, groups - 1);
 #pragma unroll
@@ -283,9 +281,39 @@ __device__ __forceinline__ void small_codes(int grp, int groups, int kq,
           rq[mat], (rt >> 6) * 32 * (groups * 64) + (2 * gg + (kq >> 1)) * 1024 + (rt & 63) * 16 +
                        (kq & 1) * 8, 0, 0);
       st.q[mat][sb] = make_uint2(v[0], v[1]);
-      st.s[mat][sb] = __builtin_bit_cast(_Float16, srow[mat][sb][gg]);
     }
   }
+}
+
+// Group scales of one ring pass (kRing groups) for all the workgroup's output
+// rows, staged in LDS as [row][kRing] fp16.  Thread t loads rows t and
+// t + 256; groups past the matrix repeat its last group and columns past it
+// repeat its last column (both unused).
+constexpr int kScaleRows = 512;  // output rows (all matrices) of one workgroup
+static_assert(kRing == 4, "one 8-byte scale run per row and pass");
+
+struct ScaleRun {
+  uint32_t h[kScaleRows / 256][kRing];  // one fp16 per register, combined at the store
+};
+
+// 2-byte loads with no arithmetic on the loaded values until the store: a
+// value that is used at once would make the load wait on every load in
+// flight before it.
+__device__ __forceinline__ ScaleRun small_scale_load(const uint16_t* const (&srow)[2], int pass,
+                                                     int groups) {
+  ScaleRun r;
+#pragma unroll
+  for (int j = 0; j < kScaleRows / 256; ++j)
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) r.h[j][i] = srow[j][min(pass * kRing + i, groups - 1)];
+  return r;
+}
+
+__device__ __forceinline__ void small_scale_store(uint2* sbuf, const ScaleRun& r) {
+#pragma unroll
+  for (int j = 0; j < kScaleRows / 256; ++j)
+    sbuf[threadIdx.x + 256 * j] = make_uint2(r.h[j][0] | (r.h[j][1] << 16),
+                                             r.h[j][2] | (r.h[j][3] << 16));
 }
 
 __device__ __forceinline__ f32x4_t offset_correction16(float S, int kq) {
@@ -306,8 +334,11 @@ __device__ __forceinline__ f32x4_t offset_correction16(float S, int kq) {
 
 // abuf: [32 rows][kALdS] bf16 then 32 row sums (float).
 template <int NM, int NSUB>
+// sc: this lane's scale of subtile 0 of matrix 0 for this group in the LDS
+// scale buffer; subtile sb of matrix mat sits (mat * 64 * NSUB + sb * 16)
+// rows further.
 __device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCodes<NM, NSUB>& st,
-                                           int col, int kq,
+                                           const uint16_t* sc, int col, int kq,
                                            f32x4_t (&acc)[kSmallRB][NM][NSUB]) {
   uint4 a[kSmallRB][2];
   f32x4_t corr[kSmallRB];
@@ -324,7 +355,8 @@ __device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCode
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
       const bf16x8_t b0 = dequant_word(st.q[mat][sb].x), b1 = dequant_word(st.q[mat][sb].y);
-      const float sv = static_cast<float>(st.s[mat][sb]);
+      const float sv = static_cast<float>(
+          __builtin_bit_cast(_Float16, sc[(mat * 64 * NSUB + sb * 16) * kRing]));
 #pragma unroll
       for (int rb = 0; rb < kSmallRB; ++rb) {
         f32x4_t p = corr[rb];
@@ -338,13 +370,17 @@ __device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCode
 }
 
 // Staging of one group of the tile's A: thread t holds 8 columns of row
-// t / 8; the row's sum is reduced over its 8 threads (fixed order).
+// t / 8; the row's sum is reduced over its 8 threads (fixed order).  The load
+// is unconditional (rows past the slot read a valid row) and the value is
+// masked only at the store, so the load is waited for where it is stored and
+// not earlier, with the codes behind it still in flight.
 __device__ __forceinline__ uint4 small_a_load(const uint16_t* arow, int grp) {
-  return arow ? *reinterpret_cast<const uint4*>(arow + grp * 64 + (threadIdx.x & 7) * 8)
-              : make_uint4(0, 0, 0, 0);
+  return *reinterpret_cast<const uint4*>(arow + grp * 64 + (threadIdx.x & 7) * 8);
 }
 
-__device__ __forceinline__ void small_a_store(uint32_t* abuf, const uint4& v) {
+// keep: all ones for a row of the slot, zero for rows past it
+__device__ __forceinline__ void small_a_store(uint32_t* abuf, const uint4& raw, uint32_t keep) {
+  const uint4 v = make_uint4(raw.x & keep, raw.y & keep, raw.z & keep, raw.w & keep);
   const int t = threadIdx.x, r = t >> 3, c8 = t & 7;
   reinterpret_cast<uint4*>(abuf + (r * kALdS + c8 * 8) / 2)[0] = v;
   float s = frag_sum(v);
@@ -360,6 +396,7 @@ template <int NM, int NSUB, bool DOWN>
 __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
   constexpr int kWaveN = 16 * NSUB;
   __shared__ __align__(16) uint32_t abufs[2][kSmallBufWords];
+  __shared__ uint2 sbufs[2][kScaleRows];  // group scales of a ring pass, [row][kRing] fp16
   const int ti = blockIdx.y;
   if (ti >= __builtin_amdgcn_readfirstlane(g.n_tiles[0])) return;
   const int N = DOWN ? g.d : g.f, K = DOWN ? g.f : g.d;
@@ -368,17 +405,19 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
   const int m0 = __builtin_amdgcn_readfirstlane(tile.y);
   const Slot sl = resolve_slot(g, slot);
   const int groups = K / 64;
-  // A staging: thread t -> row t / 8 of the tile
-  const uint16_t* srcrow = nullptr;
+  // A staging: thread t -> row t / 8 of the tile (rows past the slot read
+  // the slot's first row and are zeroed)
+  const int am = m0 + (threadIdx.x >> 3);
+  const bool aok = am < sl.M;
+  const uint32_t akeep = aok ? 0xFFFFFFFFu : 0u;
+  const uint16_t* srcrow;
   {
-    const int m = m0 + (threadIdx.x >> 3);
-    if (m < sl.M) {
-      if (DOWN) {
-        srcrow = g.h + static_cast<size_t>(row_of(g, sl, m)) * g.f;
-      } else {
-        const int tok = sl.shared ? m : g.perm[sl.p0 + m] / g.top_k;
-        srcrow = g.x + static_cast<size_t>(tok) * g.d;
-      }
+    const int m = aok ? am : m0;
+    if (DOWN) {
+      srcrow = g.h + static_cast<size_t>(row_of(g, sl, m)) * g.f;
+    } else {
+      const int tok = sl.shared ? m : g.perm[sl.p0 + m] / g.top_k;
+      srcrow = g.x + static_cast<size_t>(tok) * g.d;
     }
   }
   // the wavefront index is uniform: keep it (and the descriptors built from
@@ -394,16 +433,21 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
   // packed tiles of this wavefront inside the matrix (reads past them give 0)
   const int ntv = min((kWaveN + 63) / 64, (N - nb) / 64);
   __amdgpu_buffer_rsrc_t rq[NM];
-  const uint16_t* srow[NM][NSUB];
 #pragma unroll
-  for (int mat = 0; mat < NM; ++mat) {
-    rq[mat] = make_rsrc(sl.blk + qoff[mat] + tq, 32u * K * ntv);
-    const uint16_t* sb = reinterpret_cast<const uint16_t*>(sl.blk + soff[mat]);
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s)
-      srow[mat][s] = sb + static_cast<size_t>(min(nb + s * 16 + col, N - 1)) * groups;
-  }
+  for (int mat = 0; mat < NM; ++mat) rq[mat] = make_rsrc(sl.blk + qoff[mat] + tq, 32u * K * ntv);
   const int rt0 = nb % 64 + col;  // this lane's row inside the packed tile (subtile 0)
+  // scale rows t and t + 256 of the workgroup (matrix-major, then column)
+  constexpr int kWgN = 4 * kWaveN;
+  static_assert(NM * kWgN == kScaleRows && kWgN % 256 == 0, "scale rows per workgroup");
+  const uint16_t* srow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int mat = 256 * j / kWgN, c = (threadIdx.x + 256 * j) % kWgN;
+    srow[j] = reinterpret_cast<const uint16_t*>(sl.blk + soff[mat]) +
+              static_cast<size_t>(min(static_cast<int>(blockIdx.x) * kWgN + c, N - 1)) * groups;
+  }
+  // this lane's scale (subtile 0 of matrix 0, first group of a pass) in scale buffer 0
+  const uint16_t* scl = reinterpret_cast<const uint16_t*>(sbufs) + (wv * kWaveN + col) * kRing;
 
   f32x4_t acc[kSmallRB][NM][NSUB];
 #pragma unroll
@@ -412,23 +456,58 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
     for (int mat = 0; mat < NM; ++mat)
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) acc[rb][mat][s] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // Loads are issued in the order they are consumed (scales of pass 0, A of
+  // groups 0..2, codes of groups 0..kRing-1, scales of pass 1), and in the
+  // loop A of group grp+3 goes out ahead of the codes of group grp+kRing.
+  // Counters drain in order, so each wait then covers exactly the data it
+  // needs and leaves the later codes in flight.
+  const ScaleRun s0 = small_scale_load(srow, 0, groups);
+  const uint4 a0 = small_a_load(srcrow, 0);
+  uint4 areg[2];  // A of group j lives in areg[j & 1] until its store
+  areg[1] = small_a_load(srcrow, min(1, groups - 1));
+  areg[0] = small_a_load(srcrow, min(2, groups - 1));
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order
   SmallCodes<NM, NSUB> ring[kRing];
 #pragma unroll
-  for (int i = 0; i < kRing; ++i) small_codes<NM, NSUB>(i, groups, kq, rq, srow, rt0, ring[i]);
-  uint4 anext = small_a_load(srcrow, 0);
-  small_a_store(abufs[0], anext);
+  for (int i = 0; i < kRing; ++i) small_codes<NM, NSUB>(i, groups, kq, rq, rt0, ring[i]);
+  __builtin_amdgcn_sched_barrier(0);
+  ScaleRun snext = small_scale_load(srow, 1, groups);
+  small_scale_store(sbufs[0], s0);
+  small_a_store(abufs[0], a0, akeep);
   __syncthreads();
-  for (int g0 = 0; g0 < groups; g0 += kRing) {
+  // Full rings first: straight-line bodies, so the compiler can count the
+  // loads in flight and wait for exactly the group it needs.
+  const int full = groups / kRing * kRing;
+  for (int g0 = 0; g0 < full; g0 += kRing) {
+    const int pb = (g0 / kRing) & 1;  // scale buffer of this pass
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       const int grp = g0 + i;
+      if (active)
+        small_math<NM, NSUB>(abufs[i & 1], ring[i], scl + pb * kScaleRows * kRing + i, col, kq,
+                             acc);
+      small_a_store(abufs[(i + 1) & 1], areg[(i + 1) & 1], akeep);
+      if (i == kRing - 1) small_scale_store(sbufs[pb ^ 1], snext);
+      __syncthreads();
+      areg[(i + 1) & 1] = small_a_load(srcrow, min(grp + 3, groups - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      small_codes<NM, NSUB>(grp + kRing, groups, kq, rq, rt0, ring[i]);
+      if (i == kRing - 1) snext = small_scale_load(srow, g0 / kRing + 2, groups);
+    }
+  }
+  {
+    const int pb = (full / kRing) & 1;
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {  // the last groups % kRing groups
+      const int grp = full + i;
       if (grp < groups) {
-        if (grp + 1 < groups) anext = small_a_load(srcrow, grp + 1);
-        if (active) small_math<NM, NSUB>(abufs[grp & 1], ring[i], col, kq, acc);
-        if (grp + 1 < groups) small_a_store(abufs[(grp + 1) & 1], anext);
+        if (active)
+          small_math<NM, NSUB>(abufs[i & 1], ring[i], scl + pb * kScaleRows * kRing + i, col, kq,
+                               acc);
+        small_a_store(abufs[(i + 1) & 1], areg[(i + 1) & 1], akeep);
         __syncthreads();
+        areg[(i + 1) & 1] = small_a_load(srcrow, min(grp + 3, groups - 1));
       }
-      small_codes<NM, NSUB>(grp + kRing, groups, kq, rq, srow, rt0, ring[i]);
     }
   }
   if (!active) return;
