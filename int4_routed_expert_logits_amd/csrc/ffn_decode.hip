@@ -332,25 +332,35 @@ __device__ void stage_x(const FfnArgs& g, const Slot& sl, int m0, int nt, const 
   }
 }
 
-// h rows of the down phase (hi/lo pairs), plus each chunk's sum.
+// h rows of the down phase (hi/lo pairs), plus each chunk's sum.  Four
+// threads share a chunk, each copying a quarter (two 16-byte pieces: hi
+// words 4q.., lo words 4q..) and summing its 16 values; the quarter sums are
+// added in a fixed order ((q0 + q1) + (q2 + q3)).
 __device__ void stage_h(const FfnArgs& g, const Slot& sl, int m0, int nt, const StageLayout& L,
                         uint32_t* xl, float* xs) {
-  for (int i = threadIdx.x; i < nt * L.chunks; i += blockDim.x) {
+  const int q = threadIdx.x & 3;
+  const int items = nt * L.chunks;
+  // every thread of a quad runs the same iterations (the shuffles need all four)
+  for (int i0 = threadIdx.x >> 2; i0 < (items + blockDim.x / 4 - 1) / (blockDim.x / 4) * (blockDim.x / 4);
+       i0 += blockDim.x / 4) {
+    const int i = min(i0, items - 1);
     const int m = i / L.chunks, c = i - m * L.chunks;
     const int p = L.part_of(c), cl = c - L.cb(p);
     const size_t row = row_of(g, sl, m0 + m);
     const uint4* src = reinterpret_cast<const uint4*>(g.hp + (row * L.chunks + c) * 32);
     uint32_t* dst = xl + m * L.tok_words + p * L.part_words + cl * 32;
+    const uint4 vh = src[q], vl = src[4 + q];
     float s = 0.0f;
+    const uint32_t w[8] = {vh.x, vh.y, vh.z, vh.w, vl.x, vl.y, vl.z, vl.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint4 v = src[j];
-      reinterpret_cast<uint4*>(dst)[j] = v;
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) s += __uint_as_float(w[q] << 16) + __uint_as_float(w[q] & 0xFFFF0000u);
+    for (int k = 0; k < 8; ++k) s += __uint_as_float(w[k] << 16) + __uint_as_float(w[k] & 0xFFFF0000u);
+    s += __shfl_xor(s, 1, kWave);
+    s += __shfl_xor(s, 2, kWave);
+    if (i0 < items) {
+      reinterpret_cast<uint4*>(dst)[q] = vh;
+      reinterpret_cast<uint4*>(dst)[4 + q] = vl;
+      if (q == 0) xs[m * L.sum_words + p * L.cpp_max + cl] = s;
     }
-    xs[m * L.sum_words + p * L.cpp_max + cl] = s;
   }
 }
 

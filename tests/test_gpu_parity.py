@@ -409,6 +409,26 @@ def test_decode_is_deterministic_and_batch_invariant():
         assert np.array_equal(b1.out.cpu().numpy()[0], out1[t])
 
 
+def test_decode_reuses_its_workspace():
+    """Back-to-back calls on one set of buffers, with another batch in
+    between, repeat bit for bit (nothing carried over in the workspace)."""
+    say("decode workspace reuse")
+    for cfg, T in ((4, 1), (2, 16)):
+        L, dev = dev_layer(cfg)
+        sh = moe.shape_of(L.shape)
+        buf = LayerBuffers.allocate(sh, T, DEC)
+        outs = []
+        for batch in (0, 1, 0, 1, 0):
+            bits, _ = synth.make_tokens(cfg, T, batch=batch)
+            run_layer(dev_x(bits), dev["w_router"], dev["bias"], dev["experts"], dev["shared"], buf)
+            torch.cuda.synchronize()
+            outs.append(buf.out.cpu().numpy().copy())
+        assert np.isfinite(outs[0]).all()
+        assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[0], outs[4])
+        assert np.array_equal(outs[1], outs[3])
+        assert not np.array_equal(outs[0], outs[1])
+
+
 def test_doubling_down_scales_doubles_y():
     say("down-scale doubling")
     L, dev = dev_layer(1)
