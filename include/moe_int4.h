@@ -114,7 +114,10 @@ size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group);
  *     q_off + t*(64*K/2) + c*1024 + l*16
  * and inside each 4-byte word (columns 8w..8w+7) the nibble of column 8w+j
  * moves to bit 4*(j/2) + 16*(j%2), where q_off is the sub-array offset of
- * the canonical block.  Scales are copied unchanged (row-major [N][K/64]).
+ * the canonical block.  Scales follow the same tiles, group-major inside a
+ * tile: the scale of row t*64+l, group g goes to
+ *     s_off + (t*(K/64)*64 + g*64 + l)*2
+ * where s_off is the scale sub-array offset of the canonical block.
  *  n_blocks  number of consecutive blocks in src (0 is a no-op)
  *  src       canonical blocks, 16-byte aligned
  *  dst       packed blocks, 16-byte aligned, must not overlap src */

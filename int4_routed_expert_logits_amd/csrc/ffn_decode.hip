@@ -61,6 +61,7 @@ constexpr int kDnRows = 16;    // down rows per wavefront
 constexpr int kDnParts = 4;    // lanes per down row
 constexpr int kDnWaves = 4;    // wavefronts per down workgroup (64 rows)
 constexpr int kSkewWords = 4;  // LDS skew between the parts of a row (16 bytes)
+constexpr int kScalePad = 8;   // LDS padding (fp16) after each group's row scales
 static_assert(kGuRows * kGuParts == kWave && kDnRows * kDnParts == kWave, "lane split");
 static_assert(64 % (kGuRows * kGuWaves) == 0 && 64 % (kDnRows * kDnWaves) == 0,
               "a workgroup's rows stay inside one packed 64-row tile");
@@ -162,10 +163,10 @@ __device__ __forceinline__ void load_step(const TileRes<NM>& res, int c, int cb,
 
 // Math of one step.  xl: this lane's activations, local chunk cl of token m
 // at xl[m * tok_words + cl * XW]; xs: chunk sums at xs[m * sum_words + cl];
-// sc[mat]: the fp16 group scales of this lane's row, indexed by local group
-// (the lane's range starts at chunk cb).  XW = 16 (bf16 pairs) or 32 (16 hi
-// pairs, then 16 lo pairs).
-template <int NM, int MT, int XW>
+// sc[mat]: the fp16 group scales of this lane's row, group j at
+// sc[mat][j * kSst] (the lane's range starts at chunk cb).  XW = 16 (bf16
+// pairs) or 32 (16 hi pairs, then 16 lo pairs).
+template <int NM, int MT, int XW, int kSst>
 __device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int cb, int nt,
                                           const uint32_t* xl, int tok_words, const float* xs,
                                           int sum_words, const _Float16* const (&sc)[NM],
@@ -215,7 +216,7 @@ __device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int
     }
 #pragma unroll
     for (int mat = 0; mat < NM; ++mat) {
-      const float sv = static_cast<float>(sc[mat][(cb + c) >> 1]);
+      const float sv = static_cast<float>(sc[mat][((cb + c) >> 1) * kSst]);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         if (m < nt)
@@ -231,7 +232,7 @@ __device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int
 //
 // `a` and `b` hold the first two steps' loads, issued by the caller before
 // it staged the activations, so their latency overlaps the staging.
-template <int NM, int MT, int XW>
+template <int NM, int MT, int XW, int kSst>
 __device__ __forceinline__ void sweep(const TileRes<NM>& res, int cb, int ce, int nmax, int rt,
                                       int nt, const uint32_t* xl, int tok_words, const float* xs,
                                       int sum_words, const _Float16* const (&sc)[NM], Step<NM>& a,
@@ -242,9 +243,9 @@ __device__ __forceinline__ void sweep(const TileRes<NM>& res, int cb, int ce, in
     for (int m = 0; m < MT; ++m) acc[mat][m] = 0.0f;
   const int nl = ce - cb;
   for (int c0 = 0; c0 < nmax; c0 += 2 * kStep) {
-    math_step<NM, MT, XW>(a, c0, nl, cb, nt, xl, tok_words, xs, sum_words, sc, acc);
+    math_step<NM, MT, XW, kSst>(a, c0, nl, cb, nt, xl, tok_words, xs, sum_words, sc, acc);
     load_step<NM>(res, cb + c0 + 2 * kStep, cb, ce, rt, a);
-    math_step<NM, MT, XW>(b, c0 + kStep, nl, cb, nt, xl, tok_words, xs, sum_words, sc, acc);
+    math_step<NM, MT, XW, kSst>(b, c0 + kStep, nl, cb, nt, xl, tok_words, xs, sum_words, sc, acc);
     load_step<NM>(res, cb + c0 + 3 * kStep, cb, ce, rt, b);
   }
 }
@@ -276,13 +277,18 @@ __device__ __forceinline__ StageLayout stage_layout(int chunks, int parts, int x
   return s;
 }
 
-// The fp16 scales of `rows` consecutive rows (row-major, `groups` per row,
-// contiguous in the block) into LDS.
-__device__ __forceinline__ void stage_scales(const uint8_t* src, int rows, int groups,
+// The fp16 scales of `rows` consecutive rows, starting at row o of a packed
+// 64-row tile (the block's scales are group-major inside a tile: group j of
+// the tile's 64 rows at tile + j * 128 bytes), into LDS as
+// [groups][rows + kScalePad].
+__device__ __forceinline__ void stage_scales(const uint8_t* tile, int o, int rows, int groups,
                                              uint32_t* dst) {
-  const int n16 = rows * groups / 8;  // 16-byte pieces (rows is a multiple of 8)
-  const uint4* s = reinterpret_cast<const uint4*>(src);
-  for (int i = threadIdx.x; i < n16; i += blockDim.x) reinterpret_cast<uint4*>(dst)[i] = s[i];
+  const int per = rows / 8;  // 16-byte pieces per group (rows is a multiple of 8)
+  for (int i = threadIdx.x; i < groups * per; i += blockDim.x) {
+    const int j = i / per, pc = i - j * per;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + (j * 64 + o) * 2 + pc * 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(dst) + (j * (rows + kScalePad) + pc * 8) * 2) = v;
+  }
 }
 
 // x rows of the gate/up phase: bf16 copied as pairs, or f32 split into hi/lo
@@ -383,8 +389,9 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g) {
   const StageLayout L = stage_layout(g.d / 32, kGuParts, XW);
   constexpr int kRowsWg = kGuWaves * kGuRows;
   const int groups = g.d / 64;
-  uint32_t* scl = lds;                                    // [2][kRowsWg][groups] fp16
-  uint32_t* xl = lds + kRowsWg * groups;                  // staged x
+  constexpr int kSst = kRowsWg + kScalePad;
+  uint32_t* scl = lds;                                    // [2][groups][kSst] fp16
+  uint32_t* xl = lds + kSst * groups;                     // staged x
   float* xs = reinterpret_cast<float*>(xl + MT * L.tok_words);
   const int cb = L.cb(p), ce = L.cb(p + 1);
 
@@ -394,11 +401,11 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g) {
   res.q[1] = make_rsrc(sl.blk + g.q_up + tq, 32u * g.d);
   const int rl = wv * kGuRows + r;  // row inside the workgroup
   const _Float16* const sc[2] = {
-      reinterpret_cast<const _Float16*>(scl) + rl * groups,
-      reinterpret_cast<const _Float16*>(scl) + (kRowsWg + rl) * groups};
-  stage_scales(sl.blk + g.s_gate + static_cast<size_t>(row0) * groups * 2, kRowsWg, groups, scl);
-  stage_scales(sl.blk + g.s_up + static_cast<size_t>(row0) * groups * 2, kRowsWg, groups,
-               scl + kRowsWg * groups / 2);
+      reinterpret_cast<const _Float16*>(scl) + rl,
+      reinterpret_cast<const _Float16*>(scl) + kSst * groups + rl};
+  const size_t ts = static_cast<size_t>(tile) * 64 * groups * 2;  // the tile's scales
+  stage_scales(sl.blk + g.s_gate + ts, row0 % 64, kRowsWg, groups, scl);
+  stage_scales(sl.blk + g.s_up + ts, row0 % 64, kRowsWg, groups, scl + kSst * groups / 2);
   const int fchunks = g.f / 32;
   const int frow = row0 + wv * kGuRows + r;
 
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g) {
     stage_x<XF32>(g, sl, m0, nt, L, xl, xs);
     __syncthreads();
     float acc[2][MT];
-    sweep<2, MT, XW>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
+    sweep<2, MT, XW, kSst>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
                      xs + p * L.cpp_max, L.sum_words, sc, first, second, acc);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -455,16 +462,18 @@ __global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
   const StageLayout L = stage_layout(g.f / 32, kDnParts, 32);
   constexpr int kRowsWg = kDnWaves * kDnRows;
   const int groups = g.f / 64;
-  uint32_t* scl = lds;                                    // [kRowsWg][groups] fp16
-  uint32_t* xl = lds + kRowsWg * groups / 2;              // staged h
+  constexpr int kSst = kRowsWg + kScalePad;
+  uint32_t* scl = lds;                                    // [groups][kSst] fp16
+  uint32_t* xl = lds + kSst * groups / 2;                 // staged h
   float* xs = reinterpret_cast<float*>(xl + MT * L.tok_words);
   const int cb = L.cb(p), ce = L.cb(p + 1);
 
   TileRes<1> res;
   res.q[0] = make_rsrc(sl.blk + g.q_down + static_cast<size_t>(tile) * 64 * (g.f / 2), 32u * g.f);
   const int rl = wv * kDnRows + r;
-  const _Float16* const sc[1] = {reinterpret_cast<const _Float16*>(scl) + rl * groups};
-  stage_scales(sl.blk + g.s_down + static_cast<size_t>(row0) * groups * 2, kRowsWg, groups, scl);
+  const _Float16* const sc[1] = {reinterpret_cast<const _Float16*>(scl) + rl};
+  stage_scales(sl.blk + g.s_down + static_cast<size_t>(tile) * 64 * groups * 2, row0 % 64,
+               kRowsWg, groups, scl);
   const int drow = row0 + wv * kDnRows + r;
 
   for (int m0 = 0; m0 < sl.M; m0 += MT) {
@@ -476,7 +485,7 @@ __global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
     stage_h(g, sl, m0, nt, L, xl, xs);
     __syncthreads();
     float acc[1][MT];
-    sweep<1, MT, 32>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
+    sweep<1, MT, 32, kSst>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
                      xs + p * L.cpp_max, L.sum_words, sc, first, second, acc);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -495,13 +504,13 @@ __global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
 
 int gu_lds_bytes(int d, int mt, bool xf32) {
   const int chunks = d / 32, cpp = (chunks + kGuParts - 1) / kGuParts, xw = xf32 ? 32 : 16;
-  const int scales = kGuWaves * kGuRows * (d / 64);  // words: two matrices of fp16
+  const int scales = (kGuWaves * kGuRows + kScalePad) * (d / 64);  // words: two matrices of fp16
   return (scales + mt * (kGuParts * (cpp * xw + kSkewWords) + kGuParts * cpp)) * 4;
 }
 
 int dn_lds_bytes(int f, int mt) {
   const int chunks = f / 32, cpp = (chunks + kDnParts - 1) / kDnParts;
-  const int scales = kDnWaves * kDnRows * (f / 64) / 2;
+  const int scales = (kDnWaves * kDnRows + kScalePad) * (f / 64) / 2;
   return (scales + mt * (kDnParts * (cpp * 32 + kSkewWords) + kDnParts * cpp)) * 4;
 }
 

@@ -255,6 +255,23 @@ __device__ __forceinline__ int out_row(int i, int half) { return (i >> 2) * 8 + 
 // kq/2), for the activations one 32-byte run.
 // ---------------------------------------------------------------------------
 
+// Work item of this workgroup on a 1-D grid.  Workgroup b runs on XCD
+// b % 8 (workgroups are dealt to the 8 XCDs in turn), as the (b / 8)-th of
+// that XCD.  The items -- (tile, column block), tile-major -- are cut into 8
+// contiguous runs, one per XCD, so every column block of a tile and the
+// neighbouring tiles of the same expert share one L2: the tile's
+// activations and the expert's weights are fetched into it once.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bool xcd_item(int ntiles, int ncols, int& tile, int& col) {
+  const int items = ntiles * ncols, per = (items + kXcds - 1) / kXcds;
+  const int b = blockIdx.x, j = b / kXcds, w = (b % kXcds) * per + j;
+  if (j >= per || w >= items) return false;
+  tile = w / ncols;
+  col = w - tile * ncols;
+  return true;
+}
+
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kRing = 4;  // groups of codes in flight per wavefront
 constexpr int kSmallRB = 2;  // 16-row blocks per small tile
@@ -286,34 +303,23 @@ __device__ __forceinline__ void small_codes(int grp, int groups, int kq,
 }
 
 // Group scales of one ring pass (kRing groups) for all the workgroup's output
-// rows, staged in LDS as [row][kRing] fp16.  Thread t loads rows t and
-// t + 256; groups past the matrix repeat its last group and columns past it
-// repeat its last column (both unused).
+// rows, staged in LDS as [kRing][row] fp16.  The workgroup's 512 rows are 8
+// packed 64-row tiles, whose scales are group-major: one group of one tile
+// is a 128-byte run, so a pass is 8 x 4 such runs, one 16-byte piece per
+// thread (tile t / 32, group (t / 8) % 4, rows 8 * (t % 8) ..).  Groups past
+// the matrix repeat its last group (unused).
 constexpr int kScaleRows = 512;  // output rows (all matrices) of one workgroup
-static_assert(kRing == 4, "one 8-byte scale run per row and pass");
+static_assert(kRing == 4 && kScaleRows / 64 * kRing * 8 == 256, "one scale piece per thread");
 
-struct ScaleRun {
-  uint32_t h[kScaleRows / 256][kRing];  // one fp16 per register, combined at the store
-};
-
-// 2-byte loads with no arithmetic on the loaded values until the store: a
-// value that is used at once would make the load wait on every load in
-// flight before it.
-__device__ __forceinline__ ScaleRun small_scale_load(const uint16_t* const (&srow)[2], int pass,
-                                                     int groups) {
-  ScaleRun r;
-#pragma unroll
-  for (int j = 0; j < kScaleRows / 256; ++j)
-#pragma unroll
-    for (int i = 0; i < kRing; ++i) r.h[j][i] = srow[j][min(pass * kRing + i, groups - 1)];
-  return r;
+// src: this thread's run at group 0 of its tile
+__device__ __forceinline__ uint4 small_scale_load(const uint8_t* src, int pass, int groups) {
+  const int j = min(pass * kRing + ((threadIdx.x >> 3) & 3), groups - 1);
+  return *reinterpret_cast<const uint4*>(src + j * 128);
 }
 
-__device__ __forceinline__ void small_scale_store(uint2* sbuf, const ScaleRun& r) {
-#pragma unroll
-  for (int j = 0; j < kScaleRows / 256; ++j)
-    sbuf[threadIdx.x + 256 * j] = make_uint2(r.h[j][0] | (r.h[j][1] << 16),
-                                             r.h[j][2] | (r.h[j][3] << 16));
+__device__ __forceinline__ void small_scale_store(uint16_t* sbuf, const uint4& v) {
+  const int t = threadIdx.x;
+  reinterpret_cast<uint4*>(sbuf + ((t >> 3) & 3) * kScaleRows + (t >> 5) * 64 + (t & 7) * 8)[0] = v;
 }
 
 __device__ __forceinline__ f32x4_t offset_correction16(float S, int kq) {
@@ -356,7 +362,7 @@ __device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCode
     for (int sb = 0; sb < NSUB; ++sb) {
       const bf16x8_t b0 = dequant_word(st.q[mat][sb].x), b1 = dequant_word(st.q[mat][sb].y);
       const float sv = static_cast<float>(
-          __builtin_bit_cast(_Float16, sc[(mat * 64 * NSUB + sb * 16) * kRing]));
+          __builtin_bit_cast(_Float16, sc[mat * 64 * NSUB + sb * 16]));
 #pragma unroll
       for (int rb = 0; rb < kSmallRB; ++rb) {
         f32x4_t p = corr[rb];
@@ -396,10 +402,12 @@ template <int NM, int NSUB, bool DOWN>
 __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
   constexpr int kWaveN = 16 * NSUB;
   __shared__ __align__(16) uint32_t abufs[2][kSmallBufWords];
-  __shared__ uint2 sbufs[2][kScaleRows];  // group scales of a ring pass, [row][kRing] fp16
-  const int ti = blockIdx.y;
-  if (ti >= __builtin_amdgcn_readfirstlane(g.n_tiles[0])) return;
+  __shared__ __align__(16) uint16_t sbufs[2][kRing * kScaleRows];  // scales of a ring pass
   const int N = DOWN ? g.d : g.f, K = DOWN ? g.f : g.d;
+  int ti, cblk;
+  if (!xcd_item(__builtin_amdgcn_readfirstlane(g.n_tiles[0]), (N + 4 * kWaveN - 1) / (4 * kWaveN),
+                ti, cblk))
+    return;
   const int2 tile = g.tiles[ti];
   const int slot = __builtin_amdgcn_readfirstlane(tile.x);
   const int m0 = __builtin_amdgcn_readfirstlane(tile.y);
@@ -423,7 +431,7 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
   // the wavefront index is uniform: keep it (and the descriptors built from
   // it) in scalar registers
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int n0 = (blockIdx.x * 4 + wv) * kWaveN;  // first output column of this wavefront
+  const int n0 = (cblk * 4 + wv) * kWaveN;  // first output column of this wavefront
   const bool active = n0 < N;                     // (barriers below need every wavefront)
   const int col = lane & 15, kq = lane >> 4;
   const int nb = active ? n0 : 0;
@@ -436,18 +444,19 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
 #pragma unroll
   for (int mat = 0; mat < NM; ++mat) rq[mat] = make_rsrc(sl.blk + qoff[mat] + tq, 32u * K * ntv);
   const int rt0 = nb % 64 + col;  // this lane's row inside the packed tile (subtile 0)
-  // scale rows t and t + 256 of the workgroup (matrix-major, then column)
+  // this thread's scale piece: tile t / 32 of the workgroup's rows
+  // (matrix-major, then column), rows 8 * (t % 8) .. of the tile
   constexpr int kWgN = 4 * kWaveN;
-  static_assert(NM * kWgN == kScaleRows && kWgN % 256 == 0, "scale rows per workgroup");
-  const uint16_t* srow[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int mat = 256 * j / kWgN, c = (threadIdx.x + 256 * j) % kWgN;
-    srow[j] = reinterpret_cast<const uint16_t*>(sl.blk + soff[mat]) +
-              static_cast<size_t>(min(static_cast<int>(blockIdx.x) * kWgN + c, N - 1)) * groups;
+  static_assert(NM * kWgN == kScaleRows && kWgN % 64 == 0, "scale rows per workgroup");
+  const uint8_t* ssrc;
+  {
+    const int ti8 = threadIdx.x >> 5, mat = ti8 * 64 / kWgN;
+    const int pt = min((cblk * kWgN + ti8 * 64 % kWgN) / 64, N / 64 - 1);  // packed tile
+    ssrc = sl.blk + (mat == 0 ? soff[0] : soff[NM - 1]) +
+           (static_cast<size_t>(pt) * groups * 64 + (threadIdx.x & 7) * 8) * 2;
   }
   // this lane's scale (subtile 0 of matrix 0, first group of a pass) in scale buffer 0
-  const uint16_t* scl = reinterpret_cast<const uint16_t*>(sbufs) + (wv * kWaveN + col) * kRing;
+  const uint16_t* scl = reinterpret_cast<const uint16_t*>(sbufs) + wv * kWaveN + col;
 
   f32x4_t acc[kSmallRB][NM][NSUB];
 #pragma unroll
@@ -461,7 +470,7 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
   // loop A of group grp+3 goes out ahead of the codes of group grp+kRing.
   // Counters drain in order, so each wait then covers exactly the data it
   // needs and leaves the later codes in flight.
-  const ScaleRun s0 = small_scale_load(srow, 0, groups);
+  const uint4 s0 = small_scale_load(ssrc, 0, groups);
   const uint4 a0 = small_a_load(srcrow, 0);
   uint4 areg[2];  // A of group j lives in areg[j & 1] until its store
   areg[1] = small_a_load(srcrow, min(1, groups - 1));
@@ -471,7 +480,7 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
 #pragma unroll
   for (int i = 0; i < kRing; ++i) small_codes<NM, NSUB>(i, groups, kq, rq, rt0, ring[i]);
   __builtin_amdgcn_sched_barrier(0);
-  ScaleRun snext = small_scale_load(srow, 1, groups);
+  uint4 snext = small_scale_load(ssrc, 1, groups);
   small_scale_store(sbufs[0], s0);
   small_a_store(abufs[0], a0, akeep);
   __syncthreads();
@@ -484,15 +493,15 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
     for (int i = 0; i < kRing; ++i) {
       const int grp = g0 + i;
       if (active)
-        small_math<NM, NSUB>(abufs[i & 1], ring[i], scl + pb * kScaleRows * kRing + i, col, kq,
-                             acc);
+        small_math<NM, NSUB>(abufs[i & 1], ring[i], scl + (pb * kRing + i) * kScaleRows, col,
+                             kq, acc);
       small_a_store(abufs[(i + 1) & 1], areg[(i + 1) & 1], akeep);
       if (i == kRing - 1) small_scale_store(sbufs[pb ^ 1], snext);
       __syncthreads();
       areg[(i + 1) & 1] = small_a_load(srcrow, min(grp + 3, groups - 1));
       __builtin_amdgcn_sched_barrier(0);
       small_codes<NM, NSUB>(grp + kRing, groups, kq, rq, rt0, ring[i]);
-      if (i == kRing - 1) snext = small_scale_load(srow, g0 / kRing + 2, groups);
+      if (i == kRing - 1) snext = small_scale_load(ssrc, g0 / kRing + 2, groups);
     }
   }
   {
@@ -502,8 +511,8 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
       const int grp = full + i;
       if (grp < groups) {
         if (active)
-          small_math<NM, NSUB>(abufs[i & 1], ring[i], scl + pb * kScaleRows * kRing + i, col, kq,
-                               acc);
+          small_math<NM, NSUB>(abufs[i & 1], ring[i], scl + (pb * kRing + i) * kScaleRows, col,
+                               kq, acc);
         small_a_store(abufs[(i + 1) & 1], areg[(i + 1) & 1], akeep);
         __syncthreads();
         areg[(i + 1) & 1] = small_a_load(srcrow, min(grp + 3, groups - 1));
@@ -623,7 +632,8 @@ __device__ __forceinline__ void big_math(const uint32_t* buf, const uint16_t* sc
       const int n = wn * C::kWaveCols + ns * 32 + col;  // column inside the workgroup
       const uint4 q = bq[(mat * 2 + half) * C::kWgCols + n];
       const float sv = static_cast<float>(
-          __builtin_bit_cast(_Float16, sc[(mat * C::kWgCols + n) * groups + grp]));
+          __builtin_bit_cast(_Float16, sc[mat * C::kWgCols * groups + (n >> 6) * 64 * groups +
+                                          grp * 64 + (n & 63)]));
       bf16x8_t bw[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bw[j] = dequant_word(word_of(q, j));
@@ -644,11 +654,12 @@ template <int NM, int NS, bool DOWN>
 __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   using C = Big<NM, NS>;
   extern __shared__ __align__(16) uint32_t lds[];
-  const int ti = blockIdx.y;
-  if (ti >= __builtin_amdgcn_readfirstlane(g.n_big[0])) return;
   const int N = DOWN ? g.d : g.f, K = DOWN ? g.f : g.d;
-  const int n0 = blockIdx.x * C::kWgCols;
-  if (n0 >= N) return;
+  int ti, cblk;
+  if (!xcd_item(__builtin_amdgcn_readfirstlane(g.n_big[0]), (N + C::kWgCols - 1) / C::kWgCols, ti,
+                cblk))
+    return;
+  const int n0 = cblk * C::kWgCols;
   const int2 tile = g.big_tiles[ti];
   const int slot = __builtin_amdgcn_readfirstlane(tile.x);
   const int m0 = __builtin_amdgcn_readfirstlane(tile.y);
@@ -657,7 +668,8 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   const int ntv = min(C::kTilesN, (N - n0) / 64);  // packed tiles inside the matrix
   uint32_t* buf0 = lds;
   uint32_t* buf1 = lds + C::kBufWords;
-  uint16_t* sc = reinterpret_cast<uint16_t*>(lds + 2 * C::kBufWords);  // [NM][kWgCols][groups]
+  // scales as packed: [NM][64-row tile][groups][64] fp16
+  uint16_t* sc = reinterpret_cast<uint16_t*>(lds + 2 * C::kBufWords);
 
   const size_t soff[2] = {DOWN ? g.s_down : g.s_gate, g.s_up};
   const size_t qoff[2] = {DOWN ? g.q_down : g.q_gate, g.q_up};
@@ -812,17 +824,21 @@ hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream) {
   if ((err = allow_lds(prefill_big<2, 1, false>, lds_gu)) != hipSuccess) return err;
   if ((err = allow_lds(prefill_big<1, 2, true>, lds_dn)) != hipSuccess) return err;
   if ((err = launch(prefill_tiles, dim3(1), dim3(1024), 0, stream, g)) != hipSuccess) return err;
-  err = launch(prefill_big<2, 1, false>, dim3((p.f + GU::kWgCols - 1) / GU::kWgCols, mb),
-               dim3(256), lds_gu, stream, g);
+  // 1-D grids: enough workgroups for the largest possible tile lists, in
+  // whole rounds of the XCDs
+  auto grid = [](int tiles, int cols) {
+    return dim3((static_cast<unsigned>(tiles) * cols + kXcds - 1) / kXcds * kXcds);
+  };
+  const int cgu = (p.f + GU::kWgCols - 1) / GU::kWgCols, cdn = (p.d + DN::kWgCols - 1) / DN::kWgCols;
+  const int sgu = (p.f + 64 * kSmallNSubGU - 1) / (64 * kSmallNSubGU);
+  const int sdn = (p.d + 64 * kSmallNSubDN - 1) / (64 * kSmallNSubDN);
+  err = launch(prefill_big<2, 1, false>, grid(mb, cgu), dim3(256), lds_gu, stream, g);
   if (err != hipSuccess) return err;
-  err = launch(prefill_small<2, kSmallNSubGU, false>,
-               dim3((p.f + 64 * kSmallNSubGU - 1) / (64 * kSmallNSubGU), ms), dim3(256), 0, stream, g);
+  err = launch(prefill_small<2, kSmallNSubGU, false>, grid(ms, sgu), dim3(256), 0, stream, g);
   if (err != hipSuccess) return err;
-  err = launch(prefill_big<1, 2, true>, dim3((p.d + DN::kWgCols - 1) / DN::kWgCols, mb),
-               dim3(256), lds_dn, stream, g);
+  err = launch(prefill_big<1, 2, true>, grid(mb, cdn), dim3(256), lds_dn, stream, g);
   if (err != hipSuccess) return err;
-  return launch(prefill_small<1, kSmallNSubDN, true>,
-                dim3((p.d + 64 * kSmallNSubDN - 1) / (64 * kSmallNSubDN), ms), dim3(256), 0, stream, g);
+  return launch(prefill_small<1, kSmallNSubDN, true>, grid(ms, sdn), dim3(256), 0, stream, g);
 }
 
 }  // namespace moe

@@ -11,9 +11,13 @@
 // one contiguous kilobyte.  Inside each 4-byte word (8 columns 8w..8w+7) the
 // nibble of column 8w+j moves to bit 4*(j/2) + 16*(j%2), so that
 // (word >> 4i) & 0x000F000F holds columns (8w+2i, 8w+2i+1) in its two
-// 16-bit halves.  Scales keep the canonical row-major order [N][K/64]: a
-// kernel stages the scales of its rows (contiguous) once.  The offsets
-// q_off / s_off of the six sub-arrays are those of the canonical block.
+// 16-bit halves.  Scales follow the same 64-row tiles, group-major inside a
+// tile: row t*64+l, group g goes to
+//     s_off + (t*(K/64)*64 + g*64 + l)*2
+// so the scales of one group for a whole tile are one 128-byte run (a
+// kernel that walks the groups reads whole lines), and a tile's scales are
+// still one contiguous piece.  The offsets q_off / s_off of the six
+// sub-arrays are those of the canonical block.
 #include <algorithm>
 
 #include "common.h"
@@ -100,7 +104,9 @@ __global__ __launch_bounds__(256) void pack_scales(PackArgs a) {
     }
     const uint16_t* s = reinterpret_cast<const uint16_t*>(a.src + b * a.block_bytes + g.s_off);
     uint16_t* d = reinterpret_cast<uint16_t*>(a.dst + b * a.block_bytes + g.s_off);
-    d[u] = s[u];
+    const int G = g.K / 64;
+    const long long r = u / G, grp = u - r * G;
+    d[(r / 64) * G * 64 + grp * 64 + r % 64] = s[u];
   }
 }
 

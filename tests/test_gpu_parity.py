@@ -462,7 +462,7 @@ def test_empty_batch_is_a_no_op():
 def np_pack_block(blk, d, f):
     """The packed layout, restated with numpy reshapes: 64-row tiles, 32-column
     chunks of 16 bytes per row, nibble j of each 4-byte word moved to bit
-    4*(j//2) + 16*(j%2); scales unchanged."""
+    4*(j//2) + 16*(j%2); scales in the same 64-row tiles, group-major."""
     blk = np.asarray(blk, dtype=np.uint8)
     out = np.empty_like(blk)
     s0 = 3 * d * f // 2
@@ -477,7 +477,8 @@ def np_pack_block(blk, d, f):
         tiled = new.astype("<u4").transpose(0, 2, 1, 3)          # [tile][chunk][row][word]
         out[qo:qo + nq] = np.ascontiguousarray(tiled).view(np.uint8).reshape(-1)
         ns = N * (K // 64) * 2
-        out[so:so + ns] = blk[so:so + ns]
+        sc = blk[so:so + ns].view("<u2").reshape(N // 64, 64, K // 64).transpose(0, 2, 1)
+        out[so:so + ns] = np.ascontiguousarray(sc).view(np.uint8).reshape(-1)
     return out
 
 
