@@ -72,6 +72,9 @@ __global__ __launch_bounds__(64) void combine_kernel(const void* __restrict__ y,
   float acc[V];
 #pragma unroll
   for (int q = 0; q < V; ++q) acc[q] = 0.0f;
+  // the shared expert's row needs no index: it goes out first
+  float vs[V];
+  if (y_shared) load_row8<YBF16>(y_shared, static_cast<size_t>(t) * d + c0, vs);
   for (int j0 = 0; j0 < k; j0 += KU) {
     int p[KU];
     float w[KU];
@@ -96,10 +99,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const void* __restrict__ y,
     }
   }
   if (y_shared) {
-    float v[V];
-    load_row8<YBF16>(y_shared, static_cast<size_t>(t) * d + c0, v);
 #pragma unroll
-    for (int q = 0; q < V; ++q) acc[q] += v[q];
+    for (int q = 0; q < V; ++q) acc[q] += vs[q];
   }
   if constexpr (OBF16) {
     uint32_t w[4];

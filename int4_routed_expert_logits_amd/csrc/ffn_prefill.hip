@@ -29,11 +29,13 @@
 // the bf16 pair (136 + q) of columns 2i, 2i+1 -- exact -- so one word is one
 // 8-element B operand.  Per 64-column scale group g the MFMAs accumulate
 // P = sum_k x[m,k] (136 + q[k,n]) on top of a correction C = -136 S_g[m]
-// (S_g the row's activation sum over the group, split into three bf16 parts
-// and multiplied by -136 in one extra MFMA), and the group scale is applied
-// once: acc += s[n,g] * P.  The weights therefore enter the products
-// exactly; only the float32 accumulation and the bf16 rounding of H and Y
-// round.  Activations are bf16 (an f32 x is rejected by the C ABI).
+// (S_g the row's activation sum over the group), and the group scale is
+// applied once: acc += s[n,g] * P.  C comes from the same MFMA with a B
+// operand that is -136 everywhere; it is the same for every column, so it is
+// formed once per row block and group and shared by every column tile.
+// The weights enter the products exactly (so do x * 136); only the float32
+// accumulation and the bf16 rounding of H and Y round.  Activations are
+// bf16 (an f32 x is rejected by the C ABI).
 #include <algorithm>
 
 #include "common.h"
@@ -196,32 +198,11 @@ __device__ __forceinline__ uint32_t word_of(const uint4& q, int j) {
   return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
 }
 
-// Sum of the 8 bf16 values of a fragment, in order.
-__device__ __forceinline__ float frag_sum(const uint4& v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) s += __uint_as_float(w[i] << 16) + __uint_as_float(w[i] & 0xFFFF0000u);
-  return s;
-}
-
-// -136 * S for the 32 rows of the tile, replicated over every column, as an
-// MFMA result: A holds S split into three bf16 parts in k = 0..2 (lanes of
-// the first half), B holds -136 there.
-__device__ __forceinline__ f32x16_t offset_correction(float S, int half) {
-  const uint32_t s_hi = f32_to_bf16(S);
-  const float r1 = S - __uint_as_float(s_hi << 16);
-  const uint32_t s_mid = f32_to_bf16(r1);
-  const float r2 = r1 - __uint_as_float(s_mid << 16);
-  const uint32_t s_lo = f32_to_bf16(r2);
-  const uint32_t m136 = f32_to_bf16(-136.0f);
-  uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-  if (half == 0) {
-    a = make_uint4(s_hi | (s_mid << 16), s_lo, 0, 0);
-    b = make_uint4(m136 | (m136 << 16), m136, 0, 0);
-  }
-  f32x16_t z = {};
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), z, 0, 0, 0);
+// B operand holding -136 in every element (bf16 0xC308).  With codes dequantised
+// to 136 + q, the product with it gives the -136 * sum(A) that turns
+// A * (136 + q) into A * q, for every column of the tile at once.
+__device__ __forceinline__ bf16x8_t minus136() {
+  return as_bf16x8(make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));
 }
 
 // Buffer descriptor for `bytes` bytes at `base`.  The base is the same in
@@ -322,23 +303,7 @@ __device__ __forceinline__ void small_scale_store(uint16_t* sbuf, const uint4& v
   reinterpret_cast<uint4*>(sbuf + ((t >> 3) & 3) * kScaleRows + (t >> 5) * 64 + (t & 7) * 8)[0] = v;
 }
 
-__device__ __forceinline__ f32x4_t offset_correction16(float S, int kq) {
-  const uint32_t s_hi = f32_to_bf16(S);
-  const float r1 = S - __uint_as_float(s_hi << 16);
-  const uint32_t s_mid = f32_to_bf16(r1);
-  const float r2 = r1 - __uint_as_float(s_mid << 16);
-  const uint32_t s_lo = f32_to_bf16(r2);
-  const uint32_t m136 = f32_to_bf16(-136.0f);
-  uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-  if (kq == 0) {
-    a = make_uint4(s_hi | (s_mid << 16), s_lo, 0, 0);
-    b = make_uint4(m136 | (m136 << 16), m136, 0, 0);
-  }
-  f32x4_t z = {};
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), z, 0, 0, 0);
-}
-
-// abuf: [32 rows][kALdS] bf16 then 32 row sums (float).
+// abuf: [32 rows][kALdS] bf16.
 template <int NM, int NSUB>
 // sc: this lane's scale of subtile 0 of matrix 0 for this group in the LDS
 // scale buffer; subtile sb of matrix mat sits (mat * 64 * NSUB + sb * 16)
@@ -354,7 +319,11 @@ __device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCode
     const uint4* ap = reinterpret_cast<const uint4*>(abuf + (r * kALdS + kq * 16) / 2);
     a[rb][0] = ap[0];
     a[rb][1] = ap[1];
-    corr[rb] = offset_correction16(reinterpret_cast<const float*>(abuf + 32 * kALdS / 2)[r], kq);
+    // -136 * (row sums of the group), the same for every column
+    corr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][0]), minus136(),
+                                                       f32x4_t{}, 0, 0, 0);
+    corr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][1]), minus136(), corr[rb],
+                                                       0, 0, 0);
   }
 #pragma unroll
   for (int mat = 0; mat < NM; ++mat) {
@@ -376,7 +345,7 @@ __device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCode
 }
 
 // Staging of one group of the tile's A: thread t holds 8 columns of row
-// t / 8; the row's sum is reduced over its 8 threads (fixed order).  The load
+// t / 8.  The load
 // is unconditional (rows past the slot read a valid row) and the value is
 // masked only at the store, so the load is waited for where it is stored and
 // not earlier, with the codes behind it still in flight.
@@ -389,14 +358,9 @@ __device__ __forceinline__ void small_a_store(uint32_t* abuf, const uint4& raw, 
   const uint4 v = make_uint4(raw.x & keep, raw.y & keep, raw.z & keep, raw.w & keep);
   const int t = threadIdx.x, r = t >> 3, c8 = t & 7;
   reinterpret_cast<uint4*>(abuf + (r * kALdS + c8 * 8) / 2)[0] = v;
-  float s = frag_sum(v);
-  s += __shfl_xor(s, 1, kWave);
-  s += __shfl_xor(s, 2, kWave);
-  s += __shfl_xor(s, 4, kWave);
-  if (c8 == 0) reinterpret_cast<float*>(abuf + 32 * kALdS / 2)[r] = s;
 }
 
-constexpr int kSmallBufWords = 32 * kALdS / 2 + 32;
+constexpr int kSmallBufWords = 32 * kALdS / 2;
 
 template <int NM, int NSUB, bool DOWN>
 __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
@@ -558,55 +522,57 @@ struct Big {
   static constexpr int kTilesN = kWgCols / 64;            // packed 64-row tiles per matrix
   static constexpr int kAWords = kBigM * kALd / 2;        // A buffer (32-bit words)
   static constexpr int kBWords = NM * kWgCols * 32 / 4;   // codes of one group
-  static constexpr int kBufWords = kAWords + kBigM + kBWords;
+  static constexpr int kBufWords = kAWords + kBWords;
   static int lds_bytes(int groups) {
     return (2 * kBufWords + NM * kWgCols * groups / 2) * 4;
   }
 };
 
-// Global loads of one group: this thread's 32 A columns of its row (rowp,
-// null past the slot's rows) and one 16-byte piece of the codes.
-// Packed tiles at or past ntv (the matrix ends there) read as zero.
+// Global loads of group grp (clamped to the last group): this thread's 32 A
+// columns of its row and one 16-byte piece of the codes.  Every address is
+// valid -- rows past the slot read a row of the slot, tiles past the end of
+// the matrix read its last tile -- and big_store masks those, so the loads
+// are unconditional and a wait for one group's loads leaves the next group's
+// in flight.
 template <int NM, int NS>
-__device__ __forceinline__ void big_load(const uint16_t* rowp, int ahalf, int grp, int K, int ntv,
-                                         const uint8_t* const (&qbase)[NM], uint4 (&ra)[4],
-                                         uint4& rb) {
+__device__ __forceinline__ void big_load(const uint16_t* rowp, int ahalf, int grp, int groups,
+                                         int K, int ntv, const uint8_t* const (&qbase)[NM],
+                                         uint4 (&ra)[4], uint4& rb) {
+  grp = min(grp, groups - 1);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    ra[j] = rowp ? *reinterpret_cast<const uint4*>(rowp + grp * 64 + ahalf * 32 + j * 8)
-                 : make_uint4(0, 0, 0, 0);
+    ra[j] = *reinterpret_cast<const uint4*>(rowp + grp * 64 + ahalf * 32 + j * 8);
   constexpr int kPer = 256 / NM;  // threads per matrix
   const int t = threadIdx.x;
   const int mat = t / kPer, r = t % kPer;
-  const int tt = r / 128, h = (r / 64) & 1, row = r & 63;
+  const int tt = min(r / 128, ntv - 1), h = (r / 64) & 1, row = r & 63;
   const uint8_t* src = qbase[0];
 #pragma unroll
   for (int mm = 1; mm < NM; ++mm)
     if (mat == mm) src = qbase[mm];
-  rb = tt < ntv ? *reinterpret_cast<const uint4*>(src + static_cast<size_t>(tt) * 32 * K +
-                                                  static_cast<size_t>(2 * grp + h) * 1024 + row * 16)
-                : make_uint4(0, 0, 0, 0);
+  rb = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(tt) * 32 * K +
+                                       static_cast<size_t>(2 * grp + h) * 1024 + row * 16);
 }
 
-// The loaded group into LDS buffer `buf`: A rows, their sums, the codes.
+__device__ __forceinline__ uint4 masked(const uint4& v, uint32_t keep) {
+  return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+}
+
+// The loaded group into LDS buffer `buf`: A rows (zero past the slot), then
+// the codes (zero past the matrix).
 template <int NM, int NS>
 __device__ __forceinline__ void big_store(uint32_t* buf, int arow, int ahalf, const uint4 (&ra)[4],
-                                          const uint4& rb) {
+                                          const uint4& rb, uint32_t akeep, uint32_t bkeep) {
   using C = Big<NM, NS>;
   uint4* a = reinterpret_cast<uint4*>(buf + (arow * kALd + ahalf * 32) / 2);
-  float part = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    a[j] = ra[j];
-    part += frag_sum(ra[j]);
-  }
-  const float other = __shfl_xor(part, 1, kWave);
-  if (ahalf == 0) reinterpret_cast<float*>(buf + C::kAWords)[arow] = part + other;
+  for (int j = 0; j < 4; ++j) a[j] = masked(ra[j], akeep);
   constexpr int kPer = 256 / NM;
   const int t = threadIdx.x;
   const int mat = t / kPer, r = t % kPer;
   const int tt = r / 128, h = (r / 64) & 1, row = r & 63;
-  reinterpret_cast<uint4*>(buf + C::kAWords + kBigM)[(mat * 2 + h) * C::kWgCols + tt * 64 + row] = rb;
+  reinterpret_cast<uint4*>(buf + C::kAWords)[(mat * 2 + h) * C::kWgCols + tt * 64 + row] =
+      masked(rb, bkeep);
 }
 
 template <int NM, int NS>
@@ -622,9 +588,15 @@ __device__ __forceinline__ void big_math(const uint32_t* buf, const uint16_t* sc
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       a[i][j] = *reinterpret_cast<const uint4*>(buf + (r * kALd + half * 32 + j * 8) / 2);
-    corr[i] = offset_correction(reinterpret_cast<const float*>(buf + C::kAWords)[r], half);
+    // -136 * (row sums of the group), the same for every column: once per
+    // row block, shared by every matrix and column tile
+    corr[i] = f32x16_t{};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][j]), minus136(), corr[i],
+                                                        0, 0, 0);
   }
-  const uint4* bq = reinterpret_cast<const uint4*>(buf + C::kAWords + kBigM);
+  const uint4* bq = reinterpret_cast<const uint4*>(buf + C::kAWords);
 #pragma unroll
   for (int mat = 0; mat < NM; ++mat) {
 #pragma unroll
@@ -684,21 +656,27 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   }
   const int t = threadIdx.x, arow = t >> 1, ahalf = t & 1;
   const int m = m0 + arow;
-  const uint16_t* rowp = nullptr;
-  if (m < sl.M) {
+  const uint32_t akeep = m < sl.M ? 0xFFFFFFFFu : 0u;
+  const uint32_t bkeep = (t % (256 / NM)) / 128 < ntv ? 0xFFFFFFFFu : 0u;
+  const uint16_t* rowp;
+  {
+    const int mr = m < sl.M ? m : m0;  // rows past the slot read the first row (masked)
     if (DOWN) {
-      rowp = g.h + static_cast<size_t>(row_of(g, sl, m)) * g.f;
+      rowp = g.h + static_cast<size_t>(row_of(g, sl, mr)) * g.f;
     } else {
-      const int tok = sl.shared ? m : g.perm[sl.p0 + m] / g.top_k;
+      const int tok = sl.shared ? mr : g.perm[sl.p0 + mr] / g.top_k;
       rowp = g.x + static_cast<size_t>(tok) * g.d;
     }
   }
   const int wv = t >> 6, lane = t & 63;
   const int wm = wv & 1, wn = wv >> 1, col = lane & 31, half = lane >> 5;
 
-  uint4 ra[4], rb;
-  big_load<NM, NS>(rowp, ahalf, 0, K, ntv, qbase, ra, rb);
-  big_store<NM, NS>(buf0, arow, ahalf, ra, rb);
+  // Two register sets: group g+1 is stored to LDS while g+2 is in flight,
+  // so every group's loads have two groups of math to land.
+  uint4 ra[2][4], rb[2];
+  big_load<NM, NS>(rowp, ahalf, 0, groups, K, ntv, qbase, ra[0], rb[0]);
+  big_load<NM, NS>(rowp, ahalf, 1, groups, K, ntv, qbase, ra[1], rb[1]);
+  big_store<NM, NS>(buf0, arow, ahalf, ra[0], rb[0], akeep, bkeep);
   __syncthreads();
   f32x16_t acc[2][NM][NS];
 #pragma unroll
@@ -709,12 +687,18 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
       for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = 0.0f;
-  for (int grp = 0; grp < groups; ++grp) {
-    const bool more = grp + 1 < groups;
-    if (more) big_load<NM, NS>(rowp, ahalf, grp + 1, K, ntv, qbase, ra, rb);
-    big_math<NM, NS>((grp & 1) ? buf1 : buf0, sc, groups, grp, wm, wn, col, half, acc);
-    if (more) big_store<NM, NS>((grp & 1) ? buf0 : buf1, arow, ahalf, ra, rb);
+  for (int g0 = 0; g0 < groups; g0 += 2) {
+    // group g0 is in buf0, group g0 + 1 in register set 1
+    big_load<NM, NS>(rowp, ahalf, g0 + 2, groups, K, ntv, qbase, ra[0], rb[0]);
+    big_math<NM, NS>(buf0, sc, groups, g0, wm, wn, col, half, acc);
+    big_store<NM, NS>(buf1, arow, ahalf, ra[1], rb[1], akeep, bkeep);
     __syncthreads();
+    if (g0 + 1 < groups) {
+      big_load<NM, NS>(rowp, ahalf, g0 + 3, groups, K, ntv, qbase, ra[1], rb[1]);
+      big_math<NM, NS>(buf1, sc, groups, g0 + 1, wm, wn, col, half, acc);
+      big_store<NM, NS>(buf0, arow, ahalf, ra[0], rb[0], akeep, bkeep);
+      __syncthreads();
+    }
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
