@@ -16,6 +16,8 @@
  *                   expert in the union, plus the always-active shared expert
  *   moe_combine     gate-weighted sum of each token's k expert outputs plus
  *                   the shared expert's output
+ *   moe_route_union moe_route and moe_union in one call (one launch fewer
+ *                   for decode batches)
  *   moe_pack_experts one-time byte permutation of the expert blocks into the
  *                   tiled layout the FFN kernels stream
  *
@@ -167,6 +169,18 @@ moe_status moe_route(const moe_shape* shape, int32_t T, const void* x, moe_dtype
 moe_status moe_union(const moe_shape* shape, int32_t T, const int32_t* topk_idx,
                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                      int32_t* active, int32_t* n_active, void* stream);
+
+/* moe_route followed by moe_union, in one call: the same outputs, bit for
+ * bit, as the two calls in sequence (arguments as there; the workspace is
+ * moe_route's).  Batches with T <= 8 and T*top_k <= 64 (and E <= 256) run
+ * the top-k and the grouping in a single kernel, one launch fewer per
+ * decode step; larger batches run exactly the two calls' kernels.
+ * T == 0 writes the empty grouping, as moe_union does. */
+moe_status moe_route_union(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
+                           const float* w_router, const float* bias, int32_t* topk_idx,
+                           float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int32_t* inv_perm, int32_t* active, int32_t* n_active,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Scratch bytes moe_expert_ffn needs for T tokens on `path`. */
 size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path);

@@ -25,7 +25,8 @@ MOE_PATH_DECODE_F32, MOE_PATH_PREFILL_BF16 = 0, 1
 
 # every function include/moe_int4.h declares
 EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_route_workspace_bytes", "moe_route",
-           "moe_union", "moe_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_status_str")
+           "moe_union", "moe_route_union", "moe_ffn_workspace_bytes", "moe_expert_ffn",
+           "moe_combine", "moe_status_str")
 
 
 class Shape(ctypes.Structure):
@@ -68,6 +69,10 @@ def load():
     lib.moe_union.argtypes = [sp, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_void_p]
     lib.moe_union.restype = c_int32
+    lib.moe_route_union.argtypes = [sp, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.moe_route_union.restype = c_int32
     lib.moe_expert_ffn.argtypes = [sp, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                    c_void_p, c_size_t, c_void_p]
@@ -173,6 +178,17 @@ def moe_union(shape, T, topk_idx, counts, offsets, perm, inv_perm, active, n_act
     _check("moe_union", load().moe_union(
         ctypes.byref(sh), T, _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
         _ptr(inv_perm), _ptr(active), _ptr(n_active), _stream(stream)))
+
+
+def moe_route_union(shape, x, w_router, bias, topk_idx, topk_w, counts, offsets, perm, inv_perm,
+                    active, n_active, workspace, stream=None):
+    """moe_route then moe_union in one call (same outputs)."""
+    sh = _shape(shape)
+    _check("moe_route_union", load().moe_route_union(
+        ctypes.byref(sh), x.shape[0], _ptr(x), _dtype(x), _ptr(w_router), _ptr(bias),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv_perm),
+        _ptr(active), _ptr(n_active), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def moe_expert_ffn(shape, x, experts, shared, offsets, perm, active, n_active, path, y, y_shared,

@@ -114,6 +114,36 @@ moe_status moe_union(const moe_shape* shape, int32_t T, const int32_t* topk_idx,
                                       static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_route_union(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
+                           const float* w_router, const float* bias, int32_t* topk_idx,
+                           float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int32_t* inv_perm, int32_t* active, int32_t* n_active,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(shape, T)) != MOE_OK) return st;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!counts || !offsets || !active || !n_active) return MOE_ERR_NULL;
+  if (!aligned(counts, 4) || !aligned(offsets, 4) || !aligned(active, 4) || !aligned(n_active, 4))
+    return MOE_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0)  // an empty batch: the empty grouping, as moe_union writes it
+    return hip_status(moe::launch_union(0, shape->n_experts, nullptr, counts, offsets, nullptr,
+                                        nullptr, active, n_active, s));
+  if (!x || !w_router || !topk_idx || !topk_w || !workspace || !perm || !inv_perm)
+    return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(workspace, kWorkspaceAlign) ||
+      !aligned(topk_idx, 4) || !aligned(topk_w, 4) || (bias && !aligned(bias, 4)) ||
+      !aligned(perm, 4) || !aligned(inv_perm, 4))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_route_workspace_bytes(shape, T)) return MOE_ERR_WORKSPACE;
+  const moe::UnionOut u{counts, offsets, perm, inv_perm, active, n_active};
+  return hip_status(moe::launch_route_union(T, shape->d, shape->n_experts, shape->top_k, x,
+                                            x_dt == MOE_BF16, w_router, bias,
+                                            static_cast<double*>(workspace), topk_idx, topk_w, u,
+                                            s));
+}
+
 size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path) {
   if (check_shape(shape) != MOE_OK || T < 0) return 0;
   const bool sh = shape->f_shared != 0;

@@ -41,6 +41,18 @@ hipError_t launch_union(int n_slots, int E, const int32_t* topk_idx, int32_t* co
                         int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* active,
                         int32_t* n_active, hipStream_t stream);
 
+// The batch-union outputs (moe_union's arrays).
+struct UnionOut {
+  int32_t *counts, *offsets, *perm, *inv_perm, *active, *n_active;
+};
+
+// route.hip: the router and the batch-union of its result; small batches run
+// top-k and union in one kernel, the rest as launch_route + launch_union.
+hipError_t launch_route_union(int T, int d, int E, int k, const void* x, bool x_bf16,
+                              const float* w_router, const float* bias, double* logits,
+                              int32_t* topk_idx, float* topk_w, const UnionOut& u,
+                              hipStream_t stream);
+
 struct FfnProblem {
   int T, d, f, E, k;
   bool has_shared;

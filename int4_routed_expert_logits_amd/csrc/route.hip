@@ -13,6 +13,7 @@
 // float64 evaluation, and that order is fixed for a given batch-size class.
 #include "common.h"
 #include "launch.h"
+#include "union_wave.h"
 
 namespace moe {
 
@@ -217,17 +218,18 @@ struct TopkLds {
   double sel_p[kMaxK];
 };
 
-template <int NPL>
-__device__ void topk_token(const double* __restrict__ part, int P, const float* __restrict__ bias,
-                           int t, int E, int k, int32_t* __restrict__ topk_idx,
-                           float* __restrict__ topk_w, TopkLds& sh) {
+// MP: parts loaded per logit (P <= MP); every lane's partial sums are
+// loaded before any is added.
+template <int NPL, int MP>
+__device__ __forceinline__ void topk_token(const double* __restrict__ part, int P,
+                                           const float* __restrict__ bias, int t, int E, int k,
+                                           int32_t* __restrict__ topk_idx,
+                                           float* __restrict__ topk_w, TopkLds& sh) {
   const int lane = threadIdx.x & 63;
   const uint64_t lower = (1ull << lane) - 1ull;
   double v[NPL];
   uint32_t key[NPL];
-  // every lane's partial sums are loaded before any is added; route_parts
-  // gives P <= 2048 / E (at most 16), so E <= 64 * NPL bounds it
-  constexpr int kMaxParts = NPL <= 4 ? 16 : (NPL == 8 ? 8 : 4);
+  constexpr int kMaxParts = MP;
   double pv[NPL][kMaxParts];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
@@ -344,7 +346,7 @@ __device__ void topk_token(const double* __restrict__ part, int P, const float* 
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int NPL>
+template <int NPL, int MP>
 __global__ __launch_bounds__(256) void topk_softmax(const double* __restrict__ part, int P,
                                                     const float* __restrict__ bias, int T, int E,
                                                     int k, int32_t* __restrict__ topk_idx,
@@ -353,7 +355,32 @@ __global__ __launch_bounds__(256) void topk_softmax(const double* __restrict__ p
   const int wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
-  topk_token<NPL>(part, P, bias, t, E, k, topk_idx, topk_w, sh[wv]);
+  topk_token<NPL, MP>(part, P, bias, t, E, k, topk_idx, topk_w, sh[wv]);
+}
+
+// Top-k and batch-union in one workgroup, for batches whose T * k slots one
+// wavefront can group (T <= kFusedMaxT, T * k <= 64): wavefront t runs the
+// top-k of token t exactly as topk_softmax does, then wavefront 0 groups the
+// chosen ids, read back from LDS, exactly as the stand-alone union kernel
+// does.  One launch less per decode step.
+constexpr int kFusedMaxT = 8;
+
+template <int NPL, int MP, int EPL>
+__global__ __launch_bounds__(64 * kFusedMaxT) void topk_union(
+    const double* __restrict__ part, int P, const float* __restrict__ bias, int T, int E, int k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+  __shared__ TopkLds sh[kFusedMaxT];
+  __shared__ int cnt[64 * EPL];
+  __shared__ int first[64 * EPL];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wv < T) topk_token<NPL, MP>(part, P, bias, wv, E, k, topk_idx, topk_w, sh[wv]);
+  __syncthreads();
+  if (wv != 0) return;
+  const int n = T * k;
+  const int e = lane < n ? sh[lane / k].sel_e[lane % k] : -1;
+  union_wave<EPL>(e, n, E, counts, offsets, perm, inv_perm, active, n_active, cnt, first);
 }
 
 }  // namespace
@@ -379,44 +406,94 @@ size_t route_workspace(int T, int d, int E) {
   return static_cast<size_t>(T) * E * route_parts(T, d, E) * sizeof(double);
 }
 
-hipError_t launch_route(int T, int d, int E, int k, const void* x, bool x_bf16,
-                        const float* w_router, const float* bias, double* logits,
-                        int32_t* topk_idx, float* topk_w, hipStream_t stream) {
-  hipError_t err;
-  const int P = route_parts(T, d, E);
-  const float* topk_bias = bias;
+namespace {
+
+hipError_t launch_logits(int T, int d, int E, int P, const void* x, bool x_bf16,
+                         const float* w_router, double* logits, hipStream_t stream) {
   if (T <= kSplitMaxT) {
     const int L = ((d + P - 1) / P + 3) / 4 * 4;
     const dim3 grid((E * P + 3) / 4);
-    err = x_bf16 ? launch(logits_split<true>, grid, dim3(256), 0, stream, x, w_router, logits, T,
+    return x_bf16 ? launch(logits_split<true>, grid, dim3(256), 0, stream, x, w_router, logits, T,
                           d, E, P, L)
-                 : launch(logits_split<false>, grid, dim3(256), 0, stream, x, w_router, logits,
-                          T, d, E, P, L);
-  } else {
-    const int L = ((d + P - 1) / P + kStep - 1) / kStep * kStep;
-    const dim3 grid((E + kTile - 1) / kTile, (T + kTile - 1) / kTile, P);
-    err = x_bf16 ? launch(logits_tiled<uint16_t>, grid, dim3(256), 0, stream, x, w_router,
-                          logits, T, d, E, P, L)
-                 : launch(logits_tiled<float>, grid, dim3(256), 0, stream, x, w_router, logits,
-                          T, d, E, P, L);
+                  : launch(logits_split<false>, grid, dim3(256), 0, stream, x, w_router, logits,
+                           T, d, E, P, L);
   }
+  const int L = ((d + P - 1) / P + kStep - 1) / kStep * kStep;
+  const dim3 grid((E + kTile - 1) / kTile, (T + kTile - 1) / kTile, P);
+  return x_bf16 ? launch(logits_tiled<uint16_t>, grid, dim3(256), 0, stream, x, w_router, logits,
+                         T, d, E, P, L)
+                : launch(logits_tiled<float>, grid, dim3(256), 0, stream, x, w_router, logits, T,
+                         d, E, P, L);
+}
+
+// Parts held per logit by the top-k kernels: the next of 4, 8, 16 at or
+// above P (route_parts caps P at 16 for E <= 256, 8 for E <= 512, 4 beyond).
+template <int NPL>
+hipError_t launch_topk(int T, int E, int k, int P, const double* part, const float* bias,
+                       int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  constexpr int kCap = NPL <= 4 ? 16 : (NPL == 8 ? 8 : 4);
+  const dim3 grid((T + 3) / 4), block(256);
+  if (P <= 4)
+    return launch(topk_softmax<NPL, 4>, grid, block, 0, stream, part, P, bias, T, E, k, topk_idx,
+                  topk_w);
+  if (P <= 8 || kCap == 8)
+    return launch(topk_softmax<NPL, (kCap < 8 ? kCap : 8)>, grid, block, 0, stream, part, P, bias,
+                  T, E, k, topk_idx, topk_w);
+  return launch(topk_softmax<NPL, kCap>, grid, block, 0, stream, part, P, bias, T, E, k, topk_idx,
+                topk_w);
+}
+
+hipError_t launch_topk_any(int T, int E, int k, int P, const double* part, const float* bias,
+                           int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  if (E <= 64) return launch_topk<1>(T, E, k, P, part, bias, topk_idx, topk_w, stream);
+  if (E <= 128) return launch_topk<2>(T, E, k, P, part, bias, topk_idx, topk_w, stream);
+  if (E <= 256) return launch_topk<4>(T, E, k, P, part, bias, topk_idx, topk_w, stream);
+  if (E <= 512) return launch_topk<8>(T, E, k, P, part, bias, topk_idx, topk_w, stream);
+  return launch_topk<16>(T, E, k, P, part, bias, topk_idx, topk_w, stream);
+}
+
+template <int NPL, int EPL>
+hipError_t launch_topk_union(int T, int E, int k, int P, const double* part, const float* bias,
+                             int32_t* topk_idx, float* topk_w, const UnionOut& u,
+                             hipStream_t stream) {
+  const dim3 grid(1), block(64 * kFusedMaxT);
+  if (P <= 8)
+    return launch(topk_union<NPL, 8, EPL>, grid, block, 0, stream, part, P, bias, T, E, k,
+                  topk_idx, topk_w, u.counts, u.offsets, u.perm, u.inv_perm, u.active,
+                  u.n_active);
+  return launch(topk_union<NPL, 16, EPL>, grid, block, 0, stream, part, P, bias, T, E, k, topk_idx,
+                topk_w, u.counts, u.offsets, u.perm, u.inv_perm, u.active, u.n_active);
+}
+
+}  // namespace
+
+hipError_t launch_route(int T, int d, int E, int k, const void* x, bool x_bf16,
+                        const float* w_router, const float* bias, double* logits,
+                        int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  const int P = route_parts(T, d, E);
+  const hipError_t err = launch_logits(T, d, E, P, x, x_bf16, w_router, logits, stream);
   if (err != hipSuccess) return err;
-  const dim3 grid((T + 3) / 4);
-  const double* part = logits;
-  if (E <= 64)
-    return launch(topk_softmax<1>, grid, dim3(256), 0, stream, part, P, topk_bias, T, E, k,
-                  topk_idx, topk_w);
-  if (E <= 128)
-    return launch(topk_softmax<2>, grid, dim3(256), 0, stream, part, P, topk_bias, T, E, k,
-                  topk_idx, topk_w);
-  if (E <= 256)
-    return launch(topk_softmax<4>, grid, dim3(256), 0, stream, part, P, topk_bias, T, E, k,
-                  topk_idx, topk_w);
-  if (E <= 512)
-    return launch(topk_softmax<8>, grid, dim3(256), 0, stream, part, P, topk_bias, T, E, k,
-                  topk_idx, topk_w);
-  return launch(topk_softmax<16>, grid, dim3(256), 0, stream, part, P, topk_bias, T, E, k,
-                topk_idx, topk_w);
+  return launch_topk_any(T, E, k, P, logits, bias, topk_idx, topk_w, stream);
+}
+
+hipError_t launch_route_union(int T, int d, int E, int k, const void* x, bool x_bf16,
+                              const float* w_router, const float* bias, double* logits,
+                              int32_t* topk_idx, float* topk_w, const UnionOut& u,
+                              hipStream_t stream) {
+  const int P = route_parts(T, d, E);
+  hipError_t err = launch_logits(T, d, E, P, x, x_bf16, w_router, logits, stream);
+  if (err != hipSuccess) return err;
+  if (T <= kFusedMaxT && T * k <= 64 && E <= 256) {
+    if (E <= 64)
+      return launch_topk_union<1, 4>(T, E, k, P, logits, bias, topk_idx, topk_w, u, stream);
+    if (E <= 128)
+      return launch_topk_union<2, 4>(T, E, k, P, logits, bias, topk_idx, topk_w, u, stream);
+    return launch_topk_union<4, 4>(T, E, k, P, logits, bias, topk_idx, topk_w, u, stream);
+  }
+  err = launch_topk_any(T, E, k, P, logits, bias, topk_idx, topk_w, stream);
+  if (err != hipSuccess) return err;
+  return launch_union(T * k, E, topk_idx, u.counts, u.offsets, u.perm, u.inv_perm, u.active,
+                      u.n_active, stream);
 }
 
 }  // namespace moe

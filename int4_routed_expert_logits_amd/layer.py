@@ -61,11 +61,11 @@ class LayerBuffers:
 
 
 def run_layer(x, w_router, bias, experts, shared, buf: LayerBuffers, stream=None):
-    """All four steps of the layer for the batch x [T, d]."""
+    """All four steps of the layer for the batch x [T, d]: route and union in
+    one call (moe_route_union), then the expert FFN and the combine."""
     sh = buf.shape
-    B.moe_route(sh, x, w_router, bias, buf.topk_idx, buf.topk_w, buf.workspace, stream)
-    B.moe_union(sh, buf.T, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.inv_perm,
-                buf.active, buf.n_active, stream)
+    B.moe_route_union(sh, x, w_router, bias, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets,
+                      buf.perm, buf.inv_perm, buf.active, buf.n_active, buf.workspace, stream)
     B.moe_expert_ffn(sh, x, experts, shared, buf.offsets, buf.perm, buf.active, buf.n_active,
                      buf.path, buf.y, buf.y_shared, buf.ffn_workspace, stream)
     B.moe_combine(sh, buf.y, buf.y_shared, buf.inv_perm, buf.topk_w, buf.out, stream)

@@ -87,6 +87,8 @@ def test_bad_shapes_are_rejected_by_every_call(lib, shape, status):
     assert lib.moe_union(s, 4, P, P, P, P, P, P, P, None) == status
     assert lib.moe_expert_ffn(s, 4, P, 0, P, None, P, P, P, P, 0, P, None, P, 1 << 30, None) == status
     assert lib.moe_combine(s, 4, P, None, 0, P, P, P, 0, None) == status
+    assert lib.moe_route_union(s, 4, P, 0, P, None, P, P, P, P, P, P, P, P, P, 1 << 20,
+                               None) == status
 
 
 def test_null_shape(lib):
@@ -106,6 +108,30 @@ def test_route_argument_checks(lib):
     assert lib.moe_route(s, 4, P, 0, P, None, P, P, P, ws - 1, None) == B.MOE_ERR_WORKSPACE
     # an empty batch is a no-op
     assert lib.moe_route(s, 0, None, 0, None, None, None, None, None, 0, None) == B.MOE_OK
+
+
+def test_route_union_argument_checks(lib):
+    s = ctypes.byref(shp())
+    ws = 4 * 8 * 8
+
+    def call(T=4, x=P, dt=0, w=P, topk_idx=P, counts=P, perm=P, n_active=P, ws_ptr=P, nbytes=ws):
+        return lib.moe_route_union(s, T, x, dt, w, None, topk_idx, P, counts, P, perm, P, P,
+                                   n_active, ws_ptr, nbytes, None)
+
+    assert call(T=-1) == B.MOE_ERR_SHAPE
+    assert call(dt=7) == B.MOE_ERR_DTYPE
+    assert call(x=None) == B.MOE_ERR_NULL
+    assert call(w=None) == B.MOE_ERR_NULL
+    assert call(topk_idx=None) == B.MOE_ERR_NULL
+    assert call(counts=None) == B.MOE_ERR_NULL
+    assert call(perm=None) == B.MOE_ERR_NULL
+    assert call(n_active=None) == B.MOE_ERR_NULL
+    assert call(ws_ptr=None) == B.MOE_ERR_NULL
+    assert call(x=MIS) == B.MOE_ERR_ALIGN
+    assert call(ws_ptr=P + 16) == B.MOE_ERR_ALIGN
+    assert call(counts=P + 2) == B.MOE_ERR_ALIGN
+    assert call(nbytes=ws - 1) == B.MOE_ERR_WORKSPACE
+    assert call(T=1 << 24) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_union_argument_checks(lib):

@@ -242,6 +242,43 @@ def test_union_parity_random(T, k, E, seed):
     check_union(topk, E)
 
 
+@pytest.mark.parametrize("cfg,T", [(1, 4), (2, 1), (2, 8), (2, 9), (2, 16), (3, 64), (4, 1),
+                                   (4, 8)])
+def test_route_union_equals_route_then_union(cfg, T):
+    """moe_route_union (one kernel for top-k + grouping up to 8 tokens) gives
+    exactly moe_route's and moe_union's outputs."""
+    say(f"route_union cfg={cfg} T={T}")
+    L, dev = dev_layer(cfg, router_only=True)
+    x, _ = tokens(cfg, T, 1)
+    sh = moe.shape_of(L.shape)
+    a = LayerBuffers.allocate(sh, T, DEC)
+    b = LayerBuffers.allocate(sh, T, DEC)
+    moe.moe_route(sh, x, dev["w_router"], dev["bias"], a.topk_idx, a.topk_w, a.workspace)
+    moe.moe_union(sh, T, a.topk_idx, a.counts, a.offsets, a.perm, a.inv_perm, a.active,
+                  a.n_active)
+    moe.moe_route_union(sh, x, dev["w_router"], dev["bias"], b.topk_idx, b.topk_w, b.counts,
+                        b.offsets, b.perm, b.inv_perm, b.active, b.n_active, b.workspace)
+    torch.cuda.synchronize()
+    n = T * sh.top_k
+    for name in ("topk_idx", "topk_w", "counts", "offsets", "active", "n_active"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    assert torch.equal(a.perm[:n], b.perm[:n]) and torch.equal(a.inv_perm[:n], b.inv_perm[:n])
+
+
+def test_route_union_empty_batch():
+    say("route_union empty batch")
+    L, dev = dev_layer(1, router_only=True)
+    sh = moe.shape_of(L.shape)
+    b = LayerBuffers.allocate(sh, 0, DEC)
+    b.counts.fill_(7)
+    b.n_active.fill_(7)
+    x = torch.empty((0, sh.d), dtype=torch.float32, device="cuda")
+    moe.moe_route_union(sh, x, dev["w_router"], None, b.topk_idx, b.topk_w, b.counts, b.offsets,
+                        b.perm, b.inv_perm, b.active, b.n_active, b.workspace)
+    torch.cuda.synchronize()
+    assert not b.counts.any() and int(b.n_active.item()) == 0
+
+
 def test_union_all_slots_to_one_expert():
     say("union single expert")
     check_union(np.full((4096, 1), 5, dtype=np.int32), 8)
