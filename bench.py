@@ -295,7 +295,8 @@ def counter_workload(args, torch, moe, synth, LayerBuffers, run_layer, dev):
     """The workload of the FETCH_SIZE / WRITE_SIZE counter passes: a plain
     1 GiB device-to-device copy, three times (reads and writes exactly 2^30
     bytes each: the calibration of the counters), then 20 one-token decode
-    expert-FFN launches on rotating layer copies, as in the timed run."""
+    expert-FFN launches on rotating layer copies, as in the timed run, then
+    three 2048-token prefill expert-FFN launches (Zipf-biased routing)."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
@@ -332,7 +333,19 @@ def counter_workload(args, torch, moe, synth, LayerBuffers, run_layer, dev):
                            b.active, b.n_active, DEC, b.y, b.y_shared, b.ffn_workspace)
     torch.cuda.synchronize()
     active = [int(b.n_active.item()) + 1 for b in bufs]
-    log(f"counter workload done: copy 3 x {n} B; 20 decode FFN launches of {active} expert blocks")
+    del bufs
+    L5 = synth.make_layer(5, experts=[])
+    bits, _ = synth.make_tokens(5, 2048)
+    x5 = torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+    PRE = moe.MOE_PATH_PREFILL_BF16
+    pb = LayerBuffers.allocate(sh, 2048, PRE)
+    run_layer(x5, w_router, torch.from_numpy(L5.bias).to(dev), experts[0], shared[0], pb)
+    for _ in range(3):
+        moe.moe_expert_ffn(sh, x5, experts[0], shared[0], pb.offsets, pb.perm, pb.active,
+                           pb.n_active, PRE, pb.y, pb.y_shared, pb.ffn_workspace)
+    torch.cuda.synchronize()
+    log(f"counter workload done: copy 3 x {n} B; 20 decode FFN launches of {active} expert blocks; "
+        f"3 prefill FFN launches ({int(pb.n_active.item())} active experts)")
     return 0
 
 

@@ -381,7 +381,13 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g) {
   constexpr int XW = XF32 ? 32 : 16;
   const Slot sl = resolve_slot(g, blockIdx.y);
   if (!sl.live) return;
-  const int row0 = blockIdx.x * kGuWaves * kGuRows;  // first f-row of the workgroup
+  // The two 32-row halves of a 64-row tile go to workgroups x and x + 8,
+  // which run on the same XCD (workgroups are dealt to the 8 XCDs in turn),
+  // so the tile's 128-byte scale runs are fetched into one L2 once.
+  static_assert(kGuWaves * kGuRows == 32, "two workgroups per 64-row tile");
+  const int xb = blockIdx.x, nb = g.f / 32;  // workgroups along f
+  const int row0 = (nb % 16 == 0 ? (xb / 16) * 512 + (xb % 8) * 64 + ((xb / 8) & 1) * 32
+                                 : xb * 32);  // first f-row of the workgroup
   const int tile = row0 / 64;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane % kGuRows, p = lane / kGuRows;
