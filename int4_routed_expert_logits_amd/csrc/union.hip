@@ -2,10 +2,10 @@
 // expert needed by several positions of one batch is read once; "capability
 // 3" -- a worker receives one layer's routed batch-union and runs the FFN).
 //
-// One workgroup of 512 threads does the whole grouping in LDS: a histogram of
-// the T*k routing slots per expert, an exclusive scan into offsets, the
+// One workgroup of 1024 threads does the whole grouping in LDS: a histogram
+// of the T*k routing slots per expert, an exclusive scan into offsets, the
 // active-expert list, then a stable counting sort of the slots.  Slots are
-// taken in chunks of 512 in id order; inside a chunk each wavefront ranks its
+// taken in chunks of 1024 in id order; inside a chunk each wavefront ranks its
 // lanes among equal keys with ballots, and wavefronts are ordered by a
 // per-chunk table of per-wave key counts, so the permutation is the stable
 // one regardless of the order in which hardware atomics land.
@@ -17,11 +17,12 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxE = 1024;
 
-// Exclusive scan of n <= 1024 ints in LDS (in place), returns the total.
+// Exclusive scan of n <= 2 * kThreads ints in LDS (in place), returns the
+// total.
 __device__ int block_exclusive_scan(int* a, int n, int* tmp) {
   // each thread owns two consecutive entries
   const int tid = threadIdx.x;
@@ -29,7 +30,7 @@ __device__ int block_exclusive_scan(int* a, int n, int* tmp) {
   const int v0 = i0 < n ? a[i0] : 0;
   const int v1 = i1 < n ? a[i1] : 0;
   int s = v0 + v1;
-  // inclusive scan of s over the 512 threads: wave scan then wave totals
+  // inclusive scan of s over the threads: wave scan then wave totals
   const int lane = tid & 63, wv = tid >> 6;
   int incl = s;
   for (int off = 1; off < 64; off <<= 1) {
@@ -50,6 +51,12 @@ __device__ int block_exclusive_scan(int* a, int n, int* tmp) {
   return total;
 }
 
+__device__ __forceinline__ int key_of(const int32_t* __restrict__ topk_idx, int s, int n, int E) {
+  const int e = s < n ? topk_idx[s] : -1;
+  return (e >= 0 && e < E) ? e : -1;
+}
+
+// Dynamic LDS: wave_cnt and wave_pre, kWaves * E ints each.
 __global__ __launch_bounds__(kThreads) void batch_union(const int32_t* __restrict__ topk_idx,
                                                         int n, int E, int32_t* __restrict__ counts,
                                                         int32_t* __restrict__ offsets,
@@ -60,17 +67,24 @@ __global__ __launch_bounds__(kThreads) void batch_union(const int32_t* __restric
   __shared__ int cnt[kMaxE];
   __shared__ int start[kMaxE];    // next free grouped position per expert
   __shared__ int flag[kMaxE];
-  __shared__ int wave_cnt[kWaves][kMaxE];
   __shared__ int scan_tmp[kWaves];
+  extern __shared__ int dyn[];
+  int* wave_cnt = dyn;            // [kWaves][E] slots of the chunk per wave and expert
+  int* wave_pre = dyn + kWaves * E;  // [kWaves][E] first grouped position of each
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
 
   for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
-  for (int i = tid; i < kWaves * E; i += kThreads) wave_cnt[i / E][i % E] = 0;
+  for (int i = tid; i < kWaves * E; i += kThreads) wave_cnt[i] = 0;
   __syncthreads();
-  for (int s = tid; s < n; s += kThreads) {
-    const int e = topk_idx[s];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  // histogram: four keys per thread in flight at a time
+  for (int s0 = tid; s0 < n; s0 += 4 * kThreads) {
+    int e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) e[u] = key_of(topk_idx, s0 + u * kThreads, n, E);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (e[u] >= 0) atomicAdd(&cnt[e[u]], 1);
   }
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) {
@@ -92,44 +106,47 @@ __global__ __launch_bounds__(kThreads) void batch_union(const int32_t* __restric
   }
   __syncthreads();
 
-  // Stable placement, one chunk of kThreads slots at a time.
+  // Stable placement, one chunk of kThreads slots at a time (the next
+  // chunk's keys are loaded while this one is placed).  A slot's position is
+  // its expert's next free position, plus the expert's slots in lower
+  // wavefronts of the chunk, plus its rank among the lower lanes of its own
+  // wavefront with the same expert.
+  const int nbits = key_bits(E);
+  int e_next = key_of(topk_idx, tid, n, E);
   for (int c0 = 0; c0 < n; c0 += kThreads) {
     const int s = c0 + tid;
-    int e = s < n ? topk_idx[s] : -1;
-    const bool valid = e >= 0 && e < E;
-    if (!valid) e = -1;
-    int rank = 0;
-    // rank among lower lanes of this wave with the same key
-    uint64_t pending = __ballot(valid);
-    const uint64_t lower = (1ull << lane) - 1ull;
-    while (pending) {
-      const int leader = __ffsll(static_cast<unsigned long long>(pending)) - 1;
-      const int key = __shfl(e, leader, 64);
-      const uint64_t same = __ballot(valid && e == key);
-      if (valid && e == key) rank = __popcll(same & lower);
-      if (lane == leader) wave_cnt[wv][key] = __popcll(same);
-      pending &= ~same;
+    const int e = e_next;
+    e_next = key_of(topk_idx, s + kThreads, n, E);
+    const bool valid = e >= 0;
+    const uint64_t same = match_key(e, valid, nbits);
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
+    // the expert's lowest lane in the wavefront writes its count
+    if (valid && rank == 0) wave_cnt[wv * E + e] = __popcll(same);
+    __syncthreads();
+    // per expert: exclusive prefix over the wavefronts, from its next free
+    // position
+    for (int ee = tid; ee < E; ee += kThreads) {
+      int run = start[ee];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        wave_pre[w * E + ee] = run;
+        run += wave_cnt[w * E + ee];
+      }
+      start[ee] = run;
     }
     __syncthreads();
     if (s < n) {
       if (valid) {
-        int pos = start[e] + rank;
-        for (int w = 0; w < wv; ++w) pos += wave_cnt[w][e];
+        const int pos = wave_pre[wv * E + e] + rank;
         perm[pos] = s;
         inv_perm[s] = pos;
       } else {
         inv_perm[s] = -1;
       }
     }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += kThreads) {
-      int add = 0;
-      for (int w = 0; w < kWaves; ++w) {
-        add += wave_cnt[w][ee];
-        wave_cnt[w][ee] = 0;
-      }
-      start[ee] += add;
-    }
+    // the lane of rank 0 of each expert in a wavefront is the one that wrote
+    // its count: it clears it for the next chunk
+    if (valid && rank == 0) wave_cnt[wv * E + e] = 0;
     __syncthreads();
   }
 }
@@ -164,7 +181,13 @@ hipError_t launch_union(int n_slots, int E, const int32_t* topk_idx, int32_t* co
     return launch(batch_union_small<16>, dim3(1), dim3(64), 0, stream, topk_idx, n_slots, E,
                   counts, offsets, perm, inv_perm, active, n_active);
   }
-  return launch(batch_union, dim3(1), dim3(kThreads), 0, stream, topk_idx, n_slots, E, counts,
+  const int lds = 2 * kWaves * E * static_cast<int>(sizeof(int));
+  if (lds > 48 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(batch_union),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  return launch(batch_union, dim3(1), dim3(kThreads), lds, stream, topk_idx, n_slots, E, counts,
                 offsets, perm, inv_perm, active, n_active);
 }
 

@@ -6,13 +6,30 @@
 // Lane s holds slot s; the histogram is built with LDS atomics, every lane
 // scans a contiguous block of EPL experts, and a slot's grouped position is
 // its expert's offset plus the number of lower slots with the same expert
-// (ballot rank), which is the stable order by (expert, slot).  Ids outside
+// (match_key rank), which is the stable order by (expert, slot).  Ids outside
 // [0, E) are not grouped (inv_perm = -1).
 #pragma once
 
 #include "common.h"
 
 namespace moe {
+
+// Mask of the lanes of this wavefront whose key equals this lane's, among
+// the lanes with valid set: one ballot per key bit (keys < 2^nbits), each
+// lane keeping the lanes that agree with it on that bit.  No loop over the
+// distinct keys.
+__device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    same &= bit ? m : ~m;
+  }
+  return same;
+}
+
+// Bits of an expert id below E.
+__device__ __forceinline__ int key_bits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
 
 // cnt, first: LDS scratch of 64 * EPL ints each.  e: this lane's slot's
 // expert id (any value for lanes >= n).
@@ -70,16 +87,8 @@ __device__ __forceinline__ void union_wave(int e, int n, int E, int32_t* __restr
     n_active[0] = n_act;
   }
   __builtin_amdgcn_wave_barrier();
-  int rank = 0;
-  uint64_t pending = __ballot(valid);
   const uint64_t lower = (1ull << lane) - 1ull;
-  while (pending) {
-    const int leader = __ffsll(static_cast<unsigned long long>(pending)) - 1;
-    const int key = __shfl(e, leader, 64);
-    const uint64_t same = __ballot(valid && e == key);
-    if (valid && e == key) rank = __popcll(same & lower);
-    pending &= ~same;
-  }
+  const int rank = __popcll(match_key(e, valid, key_bits(E)) & lower);
   if (lane < n) {
     if (valid) {
       const int pos = first[e] + rank;
