@@ -29,7 +29,7 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
 
 // route.hip: float64 logits then top-k + renormalised softmax.  The
 // workspace holds float64 logits, split into route_parts() partial sums per
-// (token, expert) for small batches (0 parts = the tiled kernel, one logit).
+// (token, expert) and part of d.
 int route_parts(int T, int d, int E);
 size_t route_workspace(int T, int d, int E);
 hipError_t launch_route(int T, int d, int E, int k, const void* x, bool x_bf16,

@@ -7,8 +7,8 @@
 // Two logit kernels: for small batches each router row is split into P
 // parts and one wavefront per (expert, part) streams it once for all tokens,
 // so the router matrix (6.3 MB at d=6144/E=256) is read by E*P wavefronts at
-// HBM rate; for large batches a tiled float64 product reuses each router row
-// across 64 tokens.  Every product x*w is exact in float64 (bf16 or fp32
+// HBM rate; large batches run the product on the float64 matrix cores in
+// 64-token x 128-expert tiles.  Every product x*w is exact in float64 (bf16 or fp32
 // times fp32), so only the summation order can differ from any other
 // float64 evaluation, and that order is fixed for a given batch-size class.
 #include "common.h"
@@ -33,23 +33,12 @@ __device__ __forceinline__ void load_x4(const void* x, size_t idx, float (&v)[4]
   }
 }
 
-template <typename T>
-__device__ __forceinline__ float x_at(const void* x, size_t idx);
-template <>
-__device__ __forceinline__ float x_at<uint16_t>(const void* x, size_t idx) {
-  return bf16_to_f32(static_cast<const uint16_t*>(x)[idx]);
-}
-template <>
-__device__ __forceinline__ float x_at<float>(const void* x, size_t idx) {
-  return static_cast<const float*>(x)[idx];
-}
-
 // Small batches: one wavefront per (expert, part of d).  Spreading each
 // router row over P parts puts E*P wavefronts in flight, enough to stream the
 // router matrix at HBM rate; every wavefront keeps up to 8 tokens' float64
 // sums and writes part[t][e][p] (tree-summed over its lanes).
 constexpr int kTokGroup = 8;
-constexpr int kSplitMaxT = 32;  // larger batches use the tiled kernel
+constexpr int kSplitMaxT = 32;  // larger batches use the matrix-core kernel
 
 // Partial float64 sums of tokens t0 .. t0+kTokGroup-1 against router row e
 // over columns [i0, i1), each lane its strided share.
@@ -110,64 +99,118 @@ __global__ __launch_bounds__(256) void logits_split(const void* __restrict__ x,
   }
 }
 
-// Large batches: 128 tokens x 128 experts per workgroup over one of P parts
-// of d, 8x8 float64 outputs per thread (16 LDS reads feed 64 FMAs), K steps
-// of 16 staged in LDS.  Each thread sums its part in column order and writes
-// part[t][e][p]; the top-k kernel adds the parts in order, so the result is
-// fixed by the layer shape.
-constexpr int kTile = 128;
-constexpr int kStep = 16;
-constexpr int kLdT = kTile + 1;
+// Large batches on the float64 matrix cores (v_mfma_f64_16x16x4_f64): a
+// workgroup computes 64 tokens x 128 experts over one of P parts of d, each
+// wavefront 64 tokens x 32 experts as 4 x 2 tiles of 16 x 16.  x and w are
+// staged in LDS in their own types, 32 columns at a time (the next chunk's
+// loads in flight during the current one's MFMAs), and widened to float64 --
+// exactly -- as each operand is read.  Operand layout of the 16x16x4 f64
+// MFMA: lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]; it receives
+// D[l / 16 + 4 * v][l % 16], v = 0..3.  Parts are multiples of 32 columns.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int kMT = 64, kME = 128, kMK = 32;
+constexpr int kXPad = 8, kWPad = 4;  // LDS row padding (elements)
 
 template <typename XT>
-__global__ __launch_bounds__(256) void logits_tiled(const void* __restrict__ x,
-                                                     const float* __restrict__ w,
-                                                     double* __restrict__ part, int T, int d,
-                                                     int E, int P, int L) {
-  __shared__ double xs[kStep][kLdT];
-  __shared__ double ws[kStep][kLdT];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int e0 = blockIdx.x * kTile, t0 = blockIdx.y * kTile, p = blockIdx.z;
+struct MfmaLogitsLds {
+  static constexpr int kXLd = kMK + kXPad * (4 / static_cast<int>(sizeof(XT)));  // x row stride
+  static constexpr int kWLd = kMK + kWPad;
+  XT x[2][kMT][kXLd];
+  float w[2][kME][kWLd];
+};
+
+template <typename XT>
+__global__ __launch_bounds__(256) void logits_mfma(const void* __restrict__ x,
+                                                    const float* __restrict__ w,
+                                                    double* __restrict__ part, int T, int d,
+                                                    int E, int P, int L) {
+  using S = MfmaLogitsLds<XT>;
+  __shared__ __align__(16) S sh;
+  const int e0 = blockIdx.x * kME, t0 = blockIdx.y * kMT, p = blockIdx.z;
   const int k_begin = p * L, k_end = min(d, k_begin + L);
-  double acc[8][8];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  // staging: x rows as 16-byte pieces (XP per row), w rows as 8 pieces
+  constexpr int XP = kMK * static_cast<int>(sizeof(XT)) / 16;  // 4 (bf16) or 8 (f32)
+  constexpr int XN = kMT * XP / 256;                             // pieces per thread: 1 or 2
+  const XT* xb = static_cast<const XT*>(x);
+  uint4 rx[XN], rw[4];
+  auto load = [&](int k0) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
-  // staging: thread -> row r (0..127), 8 consecutive columns
-  const int sr = threadIdx.x >> 1, sc = (threadIdx.x & 1) * 8;
-  const int st = t0 + sr, se = e0 + sr;
-  for (int k0 = k_begin; k0 < k_end; k0 += kStep) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int k = k0 + sc + c;
-      const bool in = k < k_end;
-      xs[sc + c][sr] = (st < T && in) ? static_cast<double>(x_at<XT>(x, static_cast<size_t>(st) * d + k)) : 0.0;
-      ws[sc + c][sr] = (se < E && in) ? static_cast<double>(w[static_cast<size_t>(se) * d + k]) : 0.0;
+    for (int u = 0; u < XN; ++u) {
+      const int i = tid + 256 * u, r = i / XP, c = i % XP;
+      const int t = min(t0 + r, T - 1);  // rows past T are zeroed at the store
+      rx[u] = *reinterpret_cast<const uint4*>(xb + static_cast<size_t>(t) * d + k0 +
+                                               c * (16 / static_cast<int>(sizeof(XT))));
     }
-    __syncthreads();
 #pragma unroll
-    for (int c = 0; c < kStep; ++c) {
-      double a[8], bb[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] = xs[c][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bb[j] = ws[c][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], bb[j], acc[i][j]);
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u, r = i / 8, c = i % 8;
+      const int e = min(e0 + r, E - 1);
+      rw[u] = *reinterpret_cast<const uint4*>(w + static_cast<size_t>(e) * d + k0 + c * 4);
     }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < XN; ++u) {
+      const int i = tid + 256 * u, r = i / XP, c = i % XP;
+      const uint4 v = t0 + r < T ? rx[u] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sh.x[buf][r][c * (16 / static_cast<int>(sizeof(XT)))]) = v;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u, r = i / 8, c = i % 8;
+      const uint4 v = e0 + r < E ? rw[u] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sh.w[buf][r][c * 4]) = v;
+    }
+  };
+  f64x4_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  const int fr = lane & 15, fk = lane >> 4;  // fragment row / column of this lane
+  if (k_begin < k_end) {
+    load(k_begin);
+    store(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = k_begin; k0 < k_end; k0 += kMK) {
+    const bool more = k0 + kMK < k_end;
+    if (more) load(k0 + kMK);
+#pragma unroll
+    for (int kk = 0; kk < kMK; kk += 4) {
+      double a[4], b[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (sizeof(XT) == 2)
+          a[i] = static_cast<double>(bf16_to_f32(sh.x[buf][i * 16 + fr][kk + fk]));
+        else
+          a[i] = static_cast<double>(sh.x[buf][i * 16 + fr][kk + fk]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = static_cast<double>(sh.w[buf][wv * 32 + j * 16 + fr][kk + fk]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = t0 + ty + 16 * i;
-    if (t >= T) continue;
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = e0 + tx + 16 * j;
-      if (e < E) part[(static_cast<size_t>(t) * E + e) * P + p] = acc[i][j];
+    for (int v = 0; v < 4; ++v) {
+      const int t = t0 + i * 16 + fk + 4 * v;
+      if (t >= T) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = e0 + wv * 32 + j * 16 + fr;
+        if (e < E) part[(static_cast<size_t>(t) * E + e) * P + p] = acc[i][j][v];
+      }
     }
   }
 }
@@ -386,7 +429,7 @@ __global__ __launch_bounds__(64 * kFusedMaxT) void topk_union(
 }  // namespace
 
 // Parts of d per logit, the same rule for every batch in a size class: the
-// split kernel spreads the router matrix over E*P wavefronts; the tiled
+// split kernel spreads the router matrix over E*P wavefronts; the matrix-core
 // kernel cuts d into parts of at least 384 columns.  The top-k kernel holds
 // up to 16 parts for E <= 256, 8 for E <= 512, 4 beyond.
 int route_parts(int T, int d, int E) {
@@ -418,11 +461,11 @@ hipError_t launch_logits(int T, int d, int E, int P, const void* x, bool x_bf16,
                   : launch(logits_split<false>, grid, dim3(256), 0, stream, x, w_router, logits,
                            T, d, E, P, L);
   }
-  const int L = ((d + P - 1) / P + kStep - 1) / kStep * kStep;
-  const dim3 grid((E + kTile - 1) / kTile, (T + kTile - 1) / kTile, P);
-  return x_bf16 ? launch(logits_tiled<uint16_t>, grid, dim3(256), 0, stream, x, w_router, logits,
+  const int L = ((d + P - 1) / P + kMK - 1) / kMK * kMK;
+  const dim3 grid((E + kME - 1) / kME, (T + kMT - 1) / kMT, P);
+  return x_bf16 ? launch(logits_mfma<uint16_t>, grid, dim3(256), 0, stream, x, w_router, logits,
                          T, d, E, P, L)
-                : launch(logits_tiled<float>, grid, dim3(256), 0, stream, x, w_router, logits, T,
+                : launch(logits_mfma<float>, grid, dim3(256), 0, stream, x, w_router, logits, T,
                          d, E, P, L);
 }
 
