@@ -284,7 +284,7 @@ def bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts,
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": load_traffic("prefill"),
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": round(float(ffn_ms.mean()) * 1e3, 1),
         },
@@ -349,13 +349,13 @@ def counter_workload(args, torch, moe, synth, LayerBuffers, run_layer, dev):
     return 0
 
 
-def load_traffic():
-    """HBM bytes per decode expert-FFN launch from the committed counter
-    summary, or None when the decode kernel source has changed since the
-    counters were taken (its SHA-256 is recorded with them)."""
+def load_traffic(which="decode"):
+    """HBM bytes per expert-FFN launch (decode or prefill) from the committed
+    counter summary, or None when that path's kernel source has changed since
+    the counters were taken (its SHA-256 is recorded with them)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "decode_ffn_traffic.json")
-    src = os.path.join(ROOT, "int4_routed_expert_logits_amd", "csrc", "ffn_decode.hip")
+    path = os.path.join(ROOT, "profiles", f"{which}_ffn_traffic.json")
+    src = os.path.join(ROOT, "int4_routed_expert_logits_amd", "csrc", f"ffn_{which}.hip")
     try:
         with open(path) as fh:
             rec = json.load(fh)
