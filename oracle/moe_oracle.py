@@ -22,6 +22,8 @@ the order the pages describe the layer, in float64 throughout:
   O6 expert FFN      SwiGLU: y = W_down (silu(W_gate x) * (W_up x))
   O7 shared expert   the same FFN applied to every token
   O8 combine         out[t] = sum_j w[t,j] y[slot(t,j)] + y_shared[t]
+  O9 quantiser       float weights -> int4 codes and float16 scales, per
+                     64-column group or per row (the one-time conversion)
 
 Sources (the pages, by title and section):
 
@@ -121,6 +123,61 @@ def quantize_with_scales(w: np.ndarray, scales: np.ndarray, group: int = GROUP) 
     q = np.clip(np.rint(np.asarray(w, dtype=np.float64) / s), -8, 7).astype(np.int64)
     nib = (q & 0x0F).astype(np.uint8)
     return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------
+# Quantiser (O9): float weights -> int4 codes + float16 scales
+# ----------------------------------------------------------------------------
+# The step the pages' engine runs once on a checkpoint before serving (ssnai.com
+# digest, first command; P1 "capability 4": int4 experts with gs64 scales,
+# compared there against one scale per row).  The pages give no rounding rule;
+# the reading here is the plain symmetric one:
+#   s = float16(float32(absmax) / float32(7))   (absmax over the group or row)
+#   q = the integer nearest to w / s, ties to even, clipped to [-8, 7];
+#       a group of zeros has s = 0 and q = 0.
+
+def quant_scale(absmax) -> np.ndarray:
+    """float16 scale(s) for the given absolute maxima (float32 division by 7,
+    then rounding to float16, both round-to-nearest-even)."""
+    a = np.asarray(absmax, dtype=np.float32)
+    return (a / np.float32(7.0)).astype(np.float16)
+
+
+def quant_codes(w: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Signed codes (int64): nearest integer to w / s, ties to even, clipped
+    to [-8, 7]; 0 where s == 0.  w / s is evaluated in float64, where it is
+    never rounded onto a half-integer it is not exactly equal to."""
+    w = np.asarray(w, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint(np.where(s != 0.0, w / np.where(s != 0.0, s, 1.0), 0.0))
+    return np.clip(q, -8, 7).astype(np.int64)
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Signed codes [rows, cols] -> bytes [rows, cols/2], element 2j in the low
+    nibble of byte j (the inverse of ``unpack_int4``)."""
+    nib = (np.asarray(q, dtype=np.int64) & 0x0F).astype(np.uint8)
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+
+
+def quantize_gs64(w: np.ndarray, group: int = GROUP):
+    """O9, group mode: w [N, K] (float32 or bf16 values) -> (codes [N, K/2]
+    uint8, scales [N, K/group] float16)."""
+    w = np.asarray(w, dtype=np.float64)
+    n, k = w.shape
+    g = w.reshape(n, k // group, group)
+    s = quant_scale(np.max(np.abs(g), axis=2))
+    q = quant_codes(g, s[:, :, None].astype(np.float64)).reshape(n, k)
+    return pack_int4(q), s
+
+
+def quantize_rows(w: np.ndarray):
+    """O9, per-row mode: one scale per row -> (codes [N, K/2], scales [N])."""
+    w = np.asarray(w, dtype=np.float64)
+    s = quant_scale(np.max(np.abs(w), axis=1))
+    q = quant_codes(w, s[:, None].astype(np.float64))
+    return pack_int4(q), s
 
 
 # ----------------------------------------------------------------------------

@@ -477,3 +477,105 @@ def test_union_skips_out_of_range_ids():
     assert inv.tolist() == [2, -1, -1, 0, 3, 1]
     out = oracle.combine(np.arange(12.0).reshape(6, 2), None, inv, np.ones((3, 2)), 2)
     assert out.tolist() == [[4.0, 5.0], [0.0, 1.0], [6.0 + 2.0, 7.0 + 3.0]]
+
+
+# ----------------------------------------------------------------------------
+# Quantiser (O9)
+# ----------------------------------------------------------------------------
+
+def _round_frac(x: Fraction, mant_bits: int, min_exp: int) -> Fraction:
+    """Round a positive Fraction to the nearest binary float with mant_bits
+    bits of mantissa (implicit one included), ties to even; min_exp is the
+    exponent of the smallest normal (subnormals keep that exponent)."""
+    if x == 0:
+        return Fraction(0)
+    e = x.numerator.bit_length() - x.denominator.bit_length()
+    if Fraction(2) ** e > x:
+        e -= 1
+    e = max(e, min_exp)
+    ulp = Fraction(2) ** (e - mant_bits + 1)
+    n = x / ulp
+    lo = math.floor(n)
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return lo * ulp
+
+
+def test_scale_rule_by_exact_rounding():
+    # s = float16(float32(absmax / 7)): two round-to-nearest-even steps, here
+    # done on exact fractions, independently of numpy's casts
+    rng = np.random.default_rng(9)
+    a = np.concatenate([rng.uniform(0, 3, 300), rng.uniform(0, 0.02, 300), [1.0, 7.0, 0.0, 3.5]])
+    a = a.astype(np.float32)
+    got = oracle.quant_scale(a)
+    for ai, gi in zip(a, got):
+        f32 = _round_frac(Fraction(float(ai)) / 7, 24, -126)
+        f16 = _round_frac(f32, 11, -14)
+        assert Fraction(float(gi)) == f16, (ai, gi)
+
+
+def test_quant_codes_brute_force_nearest_with_ties_to_even():
+    # every code is the q in [-8, 7] minimising |w - q*s| (exact fractions),
+    # ties to the even q -- including exact half-way points
+    rng = np.random.default_rng(10)
+    s = np.float16(0.013671875)
+    halfway = (np.arange(-8, 7) + 0.5) * float(s)
+    w = np.concatenate([rng.uniform(-0.11, 0.11, 400), halfway, [0.0, -0.0]])
+    q = oracle.quant_codes(w, float(s))
+    for wi, qi in zip(w, q):
+        best = None
+        for c in range(-8, 8):
+            err = abs(Fraction(float(wi)) - c * Fraction(float(s)))
+            if best is None or err < best[0] or (err == best[0] and c % 2 == 0):
+                best = (err, c)
+        assert qi == best[1], (wi, qi, best)
+
+
+def test_quantise_exact_grid_round_trips():
+    # weights already on the grid q*s, with a +-7 in every group: quantising
+    # gives back the same scales and codes
+    rng = np.random.default_rng(11)
+    n, k = 6, 256
+    q = rng.integers(-7, 8, size=(n, k))
+    q[:, ::64] = rng.choice([-7, 7], size=(n, k // 64))
+    s = rng.uniform(0.004, 0.03, size=(n, k // 64)).astype(np.float16)
+    w = q * np.repeat(s.astype(np.float64), 64, axis=1)
+    codes, scales = oracle.quantize_gs64(w)
+    assert np.array_equal(scales, s)
+    assert np.array_equal(oracle.unpack_int4(codes), q)
+
+
+def test_quantise_error_bound_and_zero_groups():
+    rng = np.random.default_rng(12)
+    w = synth.bf16_to_f32(synth.bf16_round(rng.standard_normal((8, 512)).astype(np.float32)))
+    w[3, 64:128] = 0.0
+    codes, scales = oracle.quantize_gs64(w)
+    assert scales[3, 1] == 0 and not oracle.unpack_int4(codes)[3, 64:128].any()
+    back = oracle.dequant(codes, scales)
+    bound = np.repeat(scales.astype(np.float64), 64, axis=1) / 2
+    assert np.all(np.abs(back - w) <= bound)
+    # a group's largest magnitude maps to +-7
+    q = oracle.unpack_int4(codes).reshape(8, 8, 64)
+    assert np.all(np.max(np.abs(q), axis=2)[scales != 0] == 7)
+
+
+def test_row_mode_is_group_mode_for_one_group_per_row():
+    rng = np.random.default_rng(13)
+    w = rng.standard_normal((5, 64)).astype(np.float32)
+    c1, s1 = oracle.quantize_rows(w)
+    c2, s2 = oracle.quantize_gs64(w)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2[:, 0])
+
+
+def test_group_scales_beat_one_scale_per_row_on_gaussian_weights():
+    # the kind of comparison the pages make (yunpan.plus, "capability 4";
+    # ssnai.com digest, caveats): gs64 keeps more of a Gaussian matrix than one
+    # scale per row
+    rng = np.random.default_rng(14)
+    w = rng.standard_normal((64, 2048))
+    cg, sg = oracle.quantize_gs64(w)
+    cr, sr = oracle.quantize_rows(w)
+    eg = np.linalg.norm(oracle.dequant(cg, sg) - w)
+    er = np.linalg.norm(oracle.unpack_int4(cr) * sr.astype(np.float64)[:, None] - w)
+    assert eg < er
