@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="only run what the HBM-traffic counter passes measure: a 1 GiB device "
                          "copy (calibration) and 20 decode expert-FFN launches")
@@ -222,12 +223,59 @@ def main():
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts[0], shared[0], w_router, dev)
 
+    # ------------------------------------------------------------ quantiser
+    if not args.no_quantizer:
+        result["quantizer"] = bench_quantizer(torch, moe, dev)
+
     # ----------------------------------------------------------- CPU oracle
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(L, bb)
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_quantizer(torch, moe, dev, reps=20):
+    """The one-time conversion: the three bf16 matrices of one ~19 MB expert
+    (W_gate, W_up [2048, 6144], W_down [6144, 2048]) quantised to int4 gs64,
+    timed with HIP events on the current stream.  Algorithmic bytes: 2 per
+    weight read, 0.5 + 2/64 per weight written."""
+    d, f = 6144, 2048
+    g = torch.Generator(device=dev).manual_seed(20261205)
+    mats = [torch.randn((f, d), generator=g, device=dev).to(torch.bfloat16),
+            torch.randn((f, d), generator=g, device=dev).to(torch.bfloat16),
+            torch.randn((d, f), generator=g, device=dev).to(torch.bfloat16)]
+    outs = [(torch.empty((m.shape[0], m.shape[1] // 2), dtype=torch.uint8, device=dev),
+             torch.empty((m.shape[0], m.shape[1] // 64), dtype=torch.float16, device=dev)) for m in mats]
+
+    def run():
+        for m, (c, sc) in zip(mats, outs):
+            moe.moe_quantize(m, moe.MOE_QUANT_GS64, c, sc)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    n_w = 3 * d * f
+    alg = n_w * 2 + n_w // 2 + n_w // 64 * 2
+    gbps = alg / (float(np.median(us)) * 1e-6) / 1e9
+    log(f"quantiser: one expert (3 x {f}x{d} bf16) in {np.median(us):.1f} us = {gbps:.0f} GB/s")
+    return {
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "workload": "int4 gs64 quantisation of one expert's three bf16 matrices (d=6144, f=2048)",
+        "us_per_expert": round(float(np.median(us)), 2),
+        "roofline": {"bound": "hbm", "kernel": "moe_quantize (gs64)", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": alg},
+    }
 
 
 def bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts, shared, w_router, dev):

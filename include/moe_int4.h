@@ -18,6 +18,8 @@
  *                   the shared expert's output
  *   moe_route_union moe_route and moe_union in one call (one launch fewer
  *                   for decode batches)
+ *   moe_quantize    float weights -> int4 codes + float16 scales (the
+ *                   one-time conversion of a checkpoint)
  *   moe_pack_experts one-time byte permutation of the expert blocks into the
  *                   tiled layout the FFN kernels stream
  *
@@ -72,6 +74,11 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *                accumulation).  An f32 x is rejected, never rounded. */
 typedef enum { MOE_PATH_DECODE_F32 = 0, MOE_PATH_PREFILL_BF16 = 1 } moe_path;
 
+/* Scale granularity of moe_quantize: one float16 scale per 64 consecutive
+ * input columns of a row (the layout every other call reads), or one per row
+ * (for comparison only). */
+typedef enum { MOE_QUANT_GS64 = 0, MOE_QUANT_ROW = 1 } moe_quant_mode;
+
 /* Layer geometry.
  *  d          hidden size; multiple of 64, 64..8192
  *  f          routed-expert intermediate size; multiple of 64, 64..8192
@@ -125,6 +132,28 @@ size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group);
  *  dst       packed blocks, 16-byte aligned, must not overlap src */
 moe_status moe_pack_experts(const moe_shape* shape, int64_t n_blocks, const uint8_t* src,
                             uint8_t* dst, void* stream);
+
+/* int4 quantiser: float weights W [N][K] -> codes and float16 scales, the
+ * one-time conversion of a checkpoint (pages: ssnai.com digest, first-command
+ * section -- the engine converts the weights once; yunpan.plus article,
+ * "capability 4" -- int4 experts with gs64 scales, compared with one scale per
+ * row).  The rule is not on the pages; this library's reading:
+ *   s = float16(float32(absmax) / 7)   absmax over the 64-column group
+ *                                      (GS64) or over the row (ROW), both
+ *                                      roundings to nearest even
+ *   q = the integer nearest to w / s, ties to even, in [-8, 7]; s == 0 gives
+ *       q = 0 (a group of zeros)
+ * Every code is decided exactly (no rounding of w / s can move it).
+ *  N, K      rows and columns; K a positive multiple of 64, K <= 65536
+ *  w         [N][K] bf16 or f32 (w_dt), row-major, 16-byte aligned
+ *  codes     out [N][K/2] bytes, element 2j of a row in the low nibble of
+ *            byte j (the canonical expert-block layout), 4-byte aligned
+ *  scales    out float16: [N][K/64] (GS64) or [N] (ROW), 2-byte aligned
+ * To build a canonical expert block, call it for W_gate, W_up and W_down with
+ * the block's sub-array pointers (moe_expert_bytes gives the layout).
+ * N == 0 is a no-op.  Non-finite weights give unspecified codes. */
+moe_status moe_quantize(int32_t N, int32_t K, const void* w, moe_dtype w_dt, moe_quant_mode mode,
+                        uint8_t* codes, void* scales, void* stream);
 
 /* Scratch bytes moe_route needs for T tokens (router logits, float64). */
 size_t moe_route_workspace_bytes(const moe_shape* shape, int32_t T);

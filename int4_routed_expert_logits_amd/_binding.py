@@ -22,11 +22,12 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
                 7: "MOE_ERR_HIP"}
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_DECODE_F32, MOE_PATH_PREFILL_BF16 = 0, 1
+MOE_QUANT_GS64, MOE_QUANT_ROW = 0, 1
 
 # every function include/moe_int4.h declares
-EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_route_workspace_bytes", "moe_route",
-           "moe_union", "moe_route_union", "moe_ffn_workspace_bytes", "moe_expert_ffn",
-           "moe_combine", "moe_status_str")
+EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_quantize", "moe_route_workspace_bytes",
+           "moe_route", "moe_union", "moe_route_union", "moe_ffn_workspace_bytes",
+           "moe_expert_ffn", "moe_combine", "moe_status_str")
 
 
 class Shape(ctypes.Structure):
@@ -82,6 +83,9 @@ def load():
     lib.moe_combine.restype = c_int32
     lib.moe_pack_experts.argtypes = [sp, ctypes.c_int64, c_void_p, c_void_p, c_void_p]
     lib.moe_pack_experts.restype = c_int32
+    lib.moe_quantize.argtypes = [c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                 c_void_p]
+    lib.moe_quantize.restype = c_int32
     lib.moe_status_str.argtypes = [c_int32]
     lib.moe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -150,6 +154,14 @@ def moe_pack_experts(shape, n_blocks: int, src, dst, stream=None):
     sh = _shape(shape)
     _check("moe_pack_experts", load().moe_pack_experts(ctypes.byref(sh), n_blocks, _ptr(src),
                                                        _ptr(dst), _stream(stream)))
+
+
+def moe_quantize(w, mode, codes, scales, stream=None):
+    """w [N, K] bf16/f32 -> codes [N, K/2] uint8 and float16 scales
+    ([N, K/64] for MOE_QUANT_GS64, [N] for MOE_QUANT_ROW)."""
+    n, k = w.shape
+    _check("moe_quantize", load().moe_quantize(n, k, _ptr(w), _dtype(w), mode, _ptr(codes),
+                                               _ptr(scales), _stream(stream)))
 
 
 def moe_route_workspace_bytes(shape, T: int) -> int:

@@ -15,6 +15,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int64_t kMaxSlots = int64_t(1) << 24;  // T * top_k
 constexpr size_t kWorkspaceAlign = 256;
+constexpr int kMaxQuantK = 65536;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -71,6 +72,19 @@ moe_status moe_pack_experts(const moe_shape* shape, int64_t n_blocks, const uint
   if (s0 < d0 + len && d0 < s0 + len) return MOE_ERR_SHAPE;  // overlapping buffers
   return hip_status(moe::launch_pack(shape->d, shape->f, n_blocks, bb, src, dst,
                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_quantize(int32_t N, int32_t K, const void* w, moe_dtype w_dt, moe_quant_mode mode,
+                        uint8_t* codes, void* scales, void* stream) {
+  if (N < 0 || K <= 0 || K % 64 != 0) return MOE_ERR_SHAPE;
+  if (K > kMaxQuantK) return MOE_ERR_UNSUPPORTED;
+  if (mode != MOE_QUANT_GS64 && mode != MOE_QUANT_ROW) return MOE_ERR_UNSUPPORTED;
+  if (w_dt != MOE_F32 && w_dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (N == 0) return MOE_OK;
+  if (!w || !codes || !scales) return MOE_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(codes, 4) || !aligned(scales, 2)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_quantize(N, K, w, w_dt == MOE_F32, mode == MOE_QUANT_ROW, codes,
+                                         scales, static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_route_workspace_bytes(const moe_shape* shape, int32_t T) {

@@ -53,6 +53,11 @@ hipError_t launch_route_union(int T, int d, int E, int k, const void* x, bool x_
                               int32_t* topk_idx, float* topk_w, const UnionOut& u,
                               hipStream_t stream);
 
+// quant.hip: float weights -> int4 codes + float16 scales (per 64-column
+// group, or per row).
+hipError_t launch_quantize(int N, int K, const void* w, bool f32, bool per_row, uint8_t* codes,
+                           void* scales, hipStream_t stream);
+
 struct FfnProblem {
   int T, d, f, E, k;
   bool has_shared;

@@ -134,6 +134,23 @@ def test_route_union_argument_checks(lib):
     assert call(T=1 << 24) == B.MOE_ERR_UNSUPPORTED
 
 
+def test_quantize_argument_checks(lib):
+    q = lambda N=4, K=128, w=P, dt=1, mode=0, c=P, sc=P: lib.moe_quantize(N, K, w, dt, mode, c, sc, None)
+    assert q(N=-1) == B.MOE_ERR_SHAPE
+    assert q(K=0) == B.MOE_ERR_SHAPE
+    assert q(K=96) == B.MOE_ERR_SHAPE
+    assert q(K=1 << 17) == B.MOE_ERR_UNSUPPORTED
+    assert q(mode=2) == B.MOE_ERR_UNSUPPORTED
+    assert q(dt=5) == B.MOE_ERR_DTYPE
+    assert q(w=None) == B.MOE_ERR_NULL
+    assert q(c=None) == B.MOE_ERR_NULL
+    assert q(sc=None) == B.MOE_ERR_NULL
+    assert q(w=MIS) == B.MOE_ERR_ALIGN
+    assert q(c=P + 2) == B.MOE_ERR_ALIGN
+    assert q(sc=P + 1) == B.MOE_ERR_ALIGN
+    assert q(N=0, w=None, c=None, sc=None) == B.MOE_OK
+
+
 def test_union_argument_checks(lib):
     s = ctypes.byref(shp())
     assert lib.moe_union(s, 4, None, P, P, P, P, P, P, None) == B.MOE_ERR_NULL

@@ -601,3 +601,102 @@ def test_prefill_empty_batch():
     moe.moe_expert_ffn(sh, x, dev["experts"], None, buf.offsets, buf.perm, buf.active,
                        buf.n_active, PRE, buf.y, None, buf.ffn_workspace)
     torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# quantiser (the one-time conversion of a checkpoint)
+# ----------------------------------------------------------------------------
+
+def gpu_quantize(w_np, dt, mode):
+    """Quantise w_np (float32 values; bf16-rounded first when dt is bf16) on
+    the GPU; returns (codes, scales, the exact input values)."""
+    if dt == "bf16":
+        bits = synth.bf16_round(np.asarray(w_np, dtype=np.float32))
+        vals = synth.bf16_to_f32(bits)
+        w = torch.from_numpy(bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+    else:
+        vals = np.asarray(w_np, dtype=np.float32)
+        w = torch.from_numpy(vals.copy()).cuda()
+    n, k = vals.shape
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda")
+    ns = k // 64 if mode == moe.MOE_QUANT_GS64 else 1
+    scales = torch.empty((n, ns), dtype=torch.float16, device="cuda")
+    moe.moe_quantize(w, mode, codes, scales)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy(), vals
+
+
+@pytest.mark.parametrize("n,k", [(1, 64), (3, 192), (17, 1024), (64, 2048)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_quantize_parity(n, k, dt, mode):
+    say(f"quantize n={n} k={k} {dt} mode={mode}")
+    rng = np.random.default_rng(n * 7 + k)
+    w = (rng.standard_normal((n, k)) * rng.uniform(0.001, 3.0, size=(n, 1))).astype(np.float32)
+    w[0, :64] = 0.0  # a group (and, at k = 64, a row) of zeros
+    codes, scales, vals = gpu_quantize(w, dt, mode)
+    if mode == moe.MOE_QUANT_GS64:
+        rc, rs = oracle.quantize_gs64(vals)
+    else:
+        rc, rs = oracle.quantize_rows(vals)
+        rs = rs[:, None]
+    assert np.array_equal(scales.view(np.uint16), rs.view(np.uint16))
+    assert np.array_equal(codes, rc)
+
+
+def test_quantize_exact_ties_go_to_even():
+    say("quantize ties")
+    # groups whose absmax is 7 * s exactly, the rest at half-way points (q + 1/2) * s
+    s = np.float16(0.013671875)
+    base = (np.arange(-7, 7) + 0.5) * float(s)
+    row = np.concatenate([[7 * float(s)], np.tile(base, 5)[:63]])
+    w = np.stack([row, -row, row[::-1].copy()]).astype(np.float32)
+    codes, scales, vals = gpu_quantize(w, "f32", moe.MOE_QUANT_GS64)
+    rc, rs = oracle.quantize_gs64(vals)
+    assert np.all(scales == s)
+    assert np.array_equal(codes, rc)
+    q = oracle.unpack_int4(codes)
+    assert np.all(q[np.abs(vals) < 7 * float(s)] % 2 == 0)
+
+
+def test_quantize_full_expert_matrix_and_round_trip_through_the_ffn():
+    """A 6144 x 2048 matrix (the down projection of the ~19 MB experts) is
+    bit-exact with the oracle; and a whole block quantised on the GPU from
+    float weights runs through the decode FFN like the oracle's block."""
+    say("quantize full matrix")
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((6144, 2048)) * 0.05).astype(np.float32)
+    codes, scales, vals = gpu_quantize(w, "bf16", moe.MOE_QUANT_GS64)
+    rc, rs = oracle.quantize_gs64(vals)
+    assert np.array_equal(scales.view(np.uint16), rs.view(np.uint16))
+    assert np.array_equal(codes, rc)
+    # small layer: quantise gate, up, down of 8 experts into canonical blocks
+    d, f, E, k = 512, 256, 8, 2
+    sh = moe.Shape(d, f, E, k, 64, 0)
+    bb = oracle.expert_block_bytes(d, f)
+    mats = [(f, d), (f, d), (d, f)]
+    blocks = torch.zeros((E, bb), dtype=torch.uint8, device="cuda")
+    ref_blocks = np.zeros((E, bb), dtype=np.uint8)
+    s0 = 3 * d * f // 2
+    for e in range(E):
+        qo, so = 0, s0
+        for (rows, cols) in mats:
+            wm = (rng.standard_normal((rows, cols)) * 0.03).astype(np.float32)
+            c_gpu = blocks[e, qo:qo + rows * cols // 2].view(rows, cols // 2)
+            s_gpu = blocks[e, so:so + rows * cols // 64 * 2].view(torch.float16).view(rows, cols // 64)
+            moe.moe_quantize(torch.from_numpy(wm).cuda(), moe.MOE_QUANT_GS64, c_gpu, s_gpu)
+            rc, rs = oracle.quantize_gs64(wm)
+            ref_blocks[e, qo:qo + rows * cols // 2] = rc.reshape(-1)
+            ref_blocks[e, so:so + rows * cols // 64 * 2] = rs.view(np.uint8).reshape(-1)
+            qo += rows * cols // 2
+            so += rows * cols // 64 * 2
+    torch.cuda.synchronize()
+    assert np.array_equal(blocks.cpu().numpy(), ref_blocks)
+    x = rng.standard_normal((4, d)).astype(np.float32)
+    wr = (rng.standard_normal((E, d)) * 0.02).astype(np.float32)
+    buf = LayerBuffers.allocate(sh, 4, DEC)
+    run_layer(torch.from_numpy(x).cuda(), torch.from_numpy(wr).cuda(), None, packed(sh, ref_blocks),
+              None, buf)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(x, wr, None, ref_blocks, None, d, f, E, k)
+    assert rel_err(buf.out.cpu().numpy(), ref["out"]) <= TOL_DECODE
