@@ -1,7 +1,7 @@
 """Device buffers for one layer call and the four-call sequence.
 
 Plumbing only: torch allocates the caller-owned device memory the C ABI
-expects, and ``run_layer`` issues moe_route -> moe_union -> moe_expert_ffn ->
+expects, and ``run_layer`` issues moe_route_union -> moe_expert_ffn ->
 moe_combine on one stream with no host synchronisation in between.
 """
 from __future__ import annotations
