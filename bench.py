@@ -12,7 +12,10 @@ block): effective expert-weight GB/s = (active experts + shared) * block bytes
 per step / step time.  Consecutive steps run on different copies of the layer
 (``--layers``, default 8, ~41 GB of HBM) and different token batches, the way
 consecutive layers of a model follow each other, so no step finds the
-previous step's experts in the 256 MB Infinity Cache.
+previous step's experts in the 256 MB Infinity Cache.  Batches of at most 8
+tokens run the layer as the one call moe_layer_decode (four launches); the
+same step through the separate calls (moe_route_union, moe_expert_ffn,
+moe_combine: five launches) is timed too and reported beside it.
 
 The same run also reports the 2048-token prefill step of that layer (Zipf
 router bias, bf16 MFMA path) as tokens/s, the roofline of the dominant
@@ -72,7 +75,7 @@ def main():
     import torch
     import synth
     import int4_routed_expert_logits_amd as moe
-    from int4_routed_expert_logits_amd.layer import LayerBuffers, run_layer
+    from int4_routed_expert_logits_amd.layer import LayerBuffers, run_layer, run_layer_decode
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -115,9 +118,17 @@ def main():
     DEC = moe.MOE_PATH_DECODE_F32
     bufs = [LayerBuffers.allocate(sh, T, DEC) for _ in range(nb)]
 
-    def step(i):
+    def step_calls(i):  # moe_route_union, moe_expert_ffn, moe_combine
         j = i % nb
         run_layer(xs[j], w_router, None, experts[j % args.layers], shared[j % args.layers], bufs[j])
+
+    def step_one_call(i):  # moe_layer_decode
+        j = i % nb
+        run_layer_decode(xs[j], w_router, None, experts[j % args.layers], shared[j % args.layers],
+                         bufs[j])
+
+    one_call = T <= 8
+    step = step_one_call if one_call else step_calls
 
     # --------------------------------------------------- per-kernel timing (events)
     for i in range(args.warmup):
@@ -145,43 +156,55 @@ def main():
         f"{kern_gbps:.0f} GB/s over {n_kt} launches")
 
     # --------------------------------------------------------- timed region
-    steps = args.steps
-    graph = None
-    if not args.no_graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(stream)
-        with torch.cuda.stream(s):
-            for i in range(nb):       # warm the capture stream
+    def timed(step):
+        """ms per step over the timed region, and the number of steps timed."""
+        steps = args.steps
+        graph = None
+        if not args.no_graph:
+            s = torch.cuda.Stream()
+            s.wait_stream(stream)
+            with torch.cuda.stream(s):
+                for i in range(nb):       # warm the capture stream
+                    step(i)
+            stream.wait_stream(s)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(nb):
+                    step(i)
+            reps = max(1, (steps + nb - 1) // nb)
+            steps = reps * nb
+            for _ in range(max(1, args.warmup // nb)):
+                graph.replay()
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            for _ in range(reps):
+                graph.replay()
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t_start
+        else:
+            for i in range(args.warmup):
                 step(i)
-        stream.wait_stream(s)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(nb):
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            for i in range(steps):
                 step(i)
-        reps = max(1, (steps + nb - 1) // nb)
-        steps = reps * nb
-        for _ in range(max(1, args.warmup // nb)):
-            graph.replay()
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for _ in range(reps):
-            graph.replay()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t_start
-    else:
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for i in range(steps):
-            step(i)
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t_start
-    ms_per_step = elapsed * 1e3 / steps
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t_start
+        del graph
+        return elapsed * 1e3 / steps, steps
+
     step_bytes = float(np.mean(bytes_per_batch))
+    graph = not args.no_graph
+    ms_calls, steps = timed(step_calls)
+    log(f"decode step, separate calls: {ms_calls * 1e3:.1f} us, "
+        f"{step_bytes / (ms_calls * 1e-3) / 1e9:.0f} GB/s ({'graph' if graph else 'eager'})")
+    ms_per_step = ms_calls
+    if one_call:
+        ms_per_step, steps = timed(step_one_call)
+        log(f"decode step, moe_layer_decode: {ms_per_step * 1e3:.1f} us, "
+            f"{step_bytes / (ms_per_step * 1e-3) / 1e9:.0f} GB/s")
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"decode step: {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s ({'graph' if graph else 'eager'})")
 
     result = {
         "metric": METRIC,
@@ -201,7 +224,10 @@ def main():
                         f"top-8 + 1 shared, int4 gs64 fp16 scales (20,054,016 B per expert)",
             "tokens_per_step": T,
             "layer_copies_rotated": args.layers,
-            "launch": "hip graph" if graph else "eager",
+            "launch": ("hip graph" if graph else "eager") +
+                      (", moe_layer_decode (4 launches)" if one_call
+                       else ", moe_route_union + moe_expert_ffn + moe_combine (5 launches)"),
+            "separate_calls_us_per_step": round(ms_calls * 1e3, 2),
             "expert_blocks_per_step": round(step_bytes / bb, 3),
             "hbm_pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         },
@@ -217,7 +243,6 @@ def main():
             "avg_launch_us": round(float(ffn_ms.mean()) * 1e3, 2),
         },
     }
-    del graph
 
     # --------------------------------------------------------------- prefill
     if not args.no_prefill:

@@ -18,6 +18,8 @@
  *                   the shared expert's output
  *   moe_route_union moe_route and moe_union in one call (one launch fewer
  *                   for decode batches)
+ *   moe_layer_decode the whole layer (route, union, expert FFN, combine) for
+ *                   a decode batch of at most 8 tokens, in four launches
  *   moe_quantize    float weights -> int4 codes + float16 scales (the
  *                   one-time conversion of a checkpoint)
  *   moe_pack_experts one-time byte permutation of the expert blocks into the
@@ -256,6 +258,35 @@ moe_status moe_expert_ffn(const moe_shape* shape, int32_t T, const void* x, moe_
 moe_status moe_combine(const moe_shape* shape, int32_t T, const void* y, const void* y_shared,
                        moe_dtype y_dt, const int32_t* inv_perm, const float* topk_w, void* out,
                        moe_dtype out_dt, void* stream);
+
+/* Scratch bytes moe_layer_decode needs for T tokens (0 if the shape is
+ * invalid). */
+size_t moe_layer_decode_workspace_bytes(const moe_shape* shape, int32_t T);
+
+/* The whole layer for a small decode batch -- moe_route_union, then
+ * moe_expert_ffn on the DECODE path, then moe_combine -- in one call with
+ * the same outputs, bit for bit, as those three calls in sequence (pages:
+ * zhichai.net, section on MTP speculative decoding -- the main model checks
+ * 2-3 drafted tokens per forward pass, and draft and check must compute the
+ * same function).  The gate/up kernel derives the top-k and the grouping of
+ * the batch itself from the router's float64 partial sums, so a step is four
+ * launches (router logits, gate/up, down, combine) instead of five.
+ *  arguments as in the three calls; every output of theirs is written:
+ *  topk_idx, topk_w, counts, offsets, perm, inv_perm, active, n_active, y and
+ *  y_shared (float32), and out (out_dt).
+ *  workspace >= moe_layer_decode_workspace_bytes(shape, T), 256-byte
+ *            aligned, no initial contents required; never shared between
+ *            calls that may run at the same time.
+ * Supported: 1 <= T <= 8, T*top_k <= 64, n_experts <= 256 (anything else is
+ * MOE_ERR_UNSUPPORTED; larger batches use the separate calls).  T == 0 writes
+ * the empty grouping, as moe_route_union does. */
+moe_status moe_layer_decode(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
+                            const float* w_router, const float* bias, const uint8_t* experts,
+                            const uint8_t* shared, int32_t* topk_idx, float* topk_w,
+                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                            int32_t* active, int32_t* n_active, void* y, void* y_shared,
+                            void* out, moe_dtype out_dt, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Static text for a status code. */
 const char* moe_status_str(moe_status status);

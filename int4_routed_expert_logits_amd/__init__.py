@@ -7,7 +7,8 @@ helpers that allocate the caller-owned device buffers with PyTorch.
 from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, MOE_BF16, MOE_F32, MOE_OK, MOE_PATH_DECODE_F32, MOE_PATH_PREFILL_BF16,
     MOE_QUANT_GS64, MOE_QUANT_ROW, MoeError, Shape, STATUS_NAMES, load, moe_combine,
-    moe_expert_bytes, moe_expert_ffn, moe_ffn_workspace_bytes, moe_pack_experts, moe_quantize,
+    moe_expert_bytes, moe_expert_ffn, moe_ffn_workspace_bytes, moe_layer_decode,
+    moe_layer_decode_workspace_bytes, moe_pack_experts, moe_quantize,
     moe_route, moe_route_union, moe_route_workspace_bytes, moe_status_str, moe_union,
 )
 

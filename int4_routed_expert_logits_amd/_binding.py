@@ -27,7 +27,8 @@ MOE_QUANT_GS64, MOE_QUANT_ROW = 0, 1
 # every function include/moe_int4.h declares
 EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_quantize", "moe_route_workspace_bytes",
            "moe_route", "moe_union", "moe_route_union", "moe_ffn_workspace_bytes",
-           "moe_expert_ffn", "moe_combine", "moe_status_str")
+           "moe_expert_ffn", "moe_combine", "moe_layer_decode_workspace_bytes",
+           "moe_layer_decode", "moe_status_str")
 
 
 class Shape(ctypes.Structure):
@@ -81,6 +82,12 @@ def load():
     lib.moe_combine.argtypes = [sp, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                 c_void_p, c_int32, c_void_p]
     lib.moe_combine.restype = c_int32
+    lib.moe_layer_decode_workspace_bytes.argtypes = [sp, c_int32]
+    lib.moe_layer_decode_workspace_bytes.restype = c_size_t
+    lib.moe_layer_decode.argtypes = ([sp, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                      c_void_p] + [c_void_p] * 11 + [c_int32, c_void_p, c_size_t,
+                                                                     c_void_p])
+    lib.moe_layer_decode.restype = c_int32
     lib.moe_pack_experts.argtypes = [sp, ctypes.c_int64, c_void_p, c_void_p, c_void_p]
     lib.moe_pack_experts.restype = c_int32
     lib.moe_quantize.argtypes = [c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
@@ -172,6 +179,10 @@ def moe_ffn_workspace_bytes(shape, T: int, path: int) -> int:
     return load().moe_ffn_workspace_bytes(ctypes.byref(_shape(shape)), T, path)
 
 
+def moe_layer_decode_workspace_bytes(shape, T: int) -> int:
+    return load().moe_layer_decode_workspace_bytes(ctypes.byref(_shape(shape)), T)
+
+
 def moe_status_str(status: int) -> str:
     return load().moe_status_str(status).decode()
 
@@ -217,3 +228,16 @@ def moe_combine(shape, y, y_shared, inv_perm, topk_w, out, stream=None):
     _check("moe_combine", load().moe_combine(
         ctypes.byref(sh), out.shape[0], _ptr(y), _ptr(y_shared), _dtype(y), _ptr(inv_perm),
         _ptr(topk_w), _ptr(out), _dtype(out), _stream(stream)))
+
+
+def moe_layer_decode(shape, x, w_router, bias, experts, shared, topk_idx, topk_w, counts, offsets,
+                     perm, inv_perm, active, n_active, y, y_shared, out, workspace, stream=None):
+    """The whole layer for a decode batch of T <= 8 tokens (route, union,
+    expert FFN, combine): the same outputs as the separate calls."""
+    sh = _shape(shape)
+    _check("moe_layer_decode", load().moe_layer_decode(
+        ctypes.byref(sh), x.shape[0], _ptr(x), _dtype(x), _ptr(w_router), _ptr(bias),
+        _ptr(experts), _ptr(shared), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+        _ptr(perm), _ptr(inv_perm), _ptr(active), _ptr(n_active), _ptr(y), _ptr(y_shared),
+        _ptr(out), _dtype(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))

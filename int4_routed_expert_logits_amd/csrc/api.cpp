@@ -235,6 +235,78 @@ moe_status moe_combine(const moe_shape* shape, int32_t T, const void* y, const v
                                         out_dt == MOE_BF16, static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_layer_decode_workspace_bytes(const moe_shape* shape, int32_t T) {
+  if (check_shape(shape) != MOE_OK || T < 0) return 0;
+  return moe_route_workspace_bytes(shape, T) + moe_ffn_workspace_bytes(shape, T, MOE_PATH_DECODE_F32);
+}
+
+moe_status moe_layer_decode(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
+                            const float* w_router, const float* bias, const uint8_t* experts,
+                            const uint8_t* shared, int32_t* topk_idx, float* topk_w,
+                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                            int32_t* active, int32_t* n_active, void* y, void* y_shared,
+                            void* out, moe_dtype out_dt, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(shape, T)) != MOE_OK) return st;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (out_dt != MOE_F32 && out_dt != MOE_BF16) return MOE_ERR_DTYPE;
+  const int E = shape->n_experts, k = shape->top_k, d = shape->d;
+  const bool has_shared = shape->f_shared != 0;
+  moe::FfnProblem p{};
+  p.T = T;
+  p.d = d;
+  p.f = shape->f;
+  p.E = E;
+  p.k = k;
+  p.has_shared = has_shared;
+  p.x_bf16 = x_dt == MOE_BF16;
+  p.block_bytes = moe_expert_bytes(shape->d, shape->f, shape->group);
+  if (T > 0 && !moe::ffn_decode_groups_batch(p, moe::route_parts(T, d, E)))
+    return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets || !active || !n_active) return MOE_ERR_NULL;
+  if (!aligned(counts, 4) || !aligned(offsets, 4) || !aligned(active, 4) || !aligned(n_active, 4))
+    return MOE_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0)
+    return hip_status(moe::launch_union(0, E, nullptr, counts, offsets, nullptr, nullptr, active,
+                                        n_active, s));
+  if (!x || !w_router || !experts || !topk_idx || !topk_w || !perm || !inv_perm || !y || !out ||
+      !workspace)
+    return MOE_ERR_NULL;
+  if (has_shared != (shared != nullptr) || has_shared != (y_shared != nullptr))
+    return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || (bias && !aligned(bias, 4)) ||
+      !aligned(experts, 16) || (shared && !aligned(shared, 16)) || !aligned(topk_idx, 4) ||
+      !aligned(topk_w, 4) || !aligned(perm, 4) || !aligned(inv_perm, 4) || !aligned(y, 16) ||
+      (y_shared && !aligned(y_shared, 16)) || !aligned(out, 16) ||
+      !aligned(workspace, kWorkspaceAlign))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_layer_decode_workspace_bytes(shape, T)) return MOE_ERR_WORKSPACE;
+  // workspace: the router's partial sums, then the FFN's intermediate h
+  const size_t route_bytes = moe_route_workspace_bytes(shape, T);
+  double* part = static_cast<double*>(workspace);
+  p.x = x;
+  p.experts = experts;
+  p.shared = shared;
+  p.offsets = offsets;
+  p.perm = perm;
+  p.active = active;
+  p.n_active = n_active;
+  p.y = y;
+  p.y_shared = y_shared;
+  p.workspace = static_cast<uint8_t*>(workspace) + route_bytes;
+  const moe::RouteGroup rg{part, moe::route_parts(T, d, E), bias, topk_idx, topk_w,
+                           moe::UnionOut{counts, offsets, perm, inv_perm, active, n_active}};
+  hipError_t err = moe::launch_router_logits(T, d, E, x, x_dt == MOE_BF16, w_router, part, s);
+  if (err == hipSuccess) err = moe::launch_ffn_decode_grouping(p, rg, s);
+  if (err == hipSuccess)
+    err = moe::launch_combine(T, d, k, y, y_shared, false, inv_perm, topk_w, out,
+                              out_dt == MOE_BF16, s);
+  return hip_status(err);
+}
+
 const char* moe_status_str(moe_status status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -40,6 +40,8 @@
 
 #include "common.h"
 #include "launch.h"
+#include "topk_wave.h"
+#include "union_wave.h"
 
 // Every fused multiply-add below is written out; no other contraction, so a
 // token's arithmetic is the same however many tokens share a sweep.
@@ -85,6 +87,33 @@ struct FfnArgs {
   float* y_shared;  // [T][d]
 };
 
+// The router half of a small decode batch that the gate/up kernel groups
+// itself: float64 logit partial sums from the router kernel, and where the
+// top-k and the grouping go.
+struct RouteArgs {
+  const double* part;  // [T][E][P]
+  const float* bias;   // [E] or null
+  int P, E;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t *counts, *offsets, *perm, *inv_perm, *active, *n_active;
+};
+
+constexpr int kRouteMaxT = 8;     // tokens a grouping workgroup takes (2 per wavefront)
+constexpr int kRouteMaxE = 256;   // experts (4 per lane in the grouping wavefront)
+constexpr int kRouteEpl = kRouteMaxE / kWave;
+
+// LDS of the grouping prologue: one top-k scratch per wavefront, the chosen
+// ids of every token, and the grouping itself.
+struct RouteLds {
+  TopkLds tk[kGuWaves];
+  int sel[kRouteMaxT][kMaxK];
+  int cnt[kRouteMaxE], first[kRouteMaxE];
+  int counts[kRouteMaxE], offsets[kRouteMaxE + 4], active[kRouteMaxE];
+  int perm[kWave], inv_perm[kWave];
+  int n_active[4];
+};
+
 struct Slot {
   const uint8_t* blk;
   int M;   // tokens
@@ -96,7 +125,10 @@ struct Slot {
 // Expert slot s of the launch: the shared expert first (if any), then
 // active[0 ..].  Everything here is the same for every lane; keeping it in
 // scalar registers keeps the buffer descriptors built from it scalar.
-__device__ __forceinline__ Slot resolve_slot(const FfnArgs& g, int slot) {
+// active / offsets: the grouping, in global memory or (when the gate/up
+// kernel grouped the batch itself) in LDS.
+__device__ __forceinline__ Slot resolve_slot(const FfnArgs& g, int slot,
+                                             const int32_t* active, const int32_t* offsets) {
   Slot s{nullptr, 0, 0, false, false};
   if (slot < g.has_shared) {
     s.blk = g.shared;
@@ -107,11 +139,11 @@ __device__ __forceinline__ Slot resolve_slot(const FfnArgs& g, int slot) {
   }
   // active[] is -1 past the n_active experts of the batch, so one load tells
   // both whether the slot is live and which expert it holds
-  const int e = __builtin_amdgcn_readfirstlane(g.active[slot - g.has_shared]);
+  const int e = __builtin_amdgcn_readfirstlane(active[slot - g.has_shared]);
   if (e < 0) return s;
   s.blk = g.experts + static_cast<size_t>(e) * g.block_bytes;
-  s.p0 = __builtin_amdgcn_readfirstlane(g.offsets[e]);
-  s.M = __builtin_amdgcn_readfirstlane(g.offsets[e + 1]) - s.p0;
+  s.p0 = __builtin_amdgcn_readfirstlane(offsets[e]);
+  s.M = __builtin_amdgcn_readfirstlane(offsets[e + 1]) - s.p0;
   s.live = true;
   return s;
 }
@@ -294,12 +326,12 @@ __device__ __forceinline__ void stage_scales(const uint8_t* tile, int o, int row
 // x rows of the gate/up phase: bf16 copied as pairs, or f32 split into hi/lo
 // bf16; plus each chunk's sum of the values the dot products see.
 template <bool XF32>
-__device__ void stage_x(const FfnArgs& g, const Slot& sl, int m0, int nt, const StageLayout& L,
-                        uint32_t* xl, float* xs) {
+__device__ void stage_x(const FfnArgs& g, const Slot& sl, const int32_t* perm, int m0, int nt,
+                        const StageLayout& L, uint32_t* xl, float* xs) {
   for (int i = threadIdx.x; i < nt * L.chunks; i += blockDim.x) {
     const int m = i / L.chunks, c = i - m * L.chunks;
     const int p = L.part_of(c), cl = c - L.cb(p);
-    const int tok = sl.shared ? m0 + m : (g.T == 1 ? 0 : g.perm[sl.p0 + m0 + m] / g.top_k);
+    const int tok = sl.shared ? m0 + m : (g.T == 1 ? 0 : perm[sl.p0 + m0 + m] / g.top_k);
     uint32_t* dst = xl + m * L.tok_words + p * L.part_words + cl * L.xw;
     float s = 0.0f;
     if constexpr (!XF32) {
@@ -375,11 +407,74 @@ __device__ void stage_h(const FfnArgs& g, const Slot& sl, int m0, int nt, const 
 // of 8 rows; lane = 8 * part + row
 // ---------------------------------------------------------------------------
 
-template <int MT, bool XF32>
-__global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g) {
+// Words of a gate/up workgroup's LDS before the grouping prologue's region
+// (a multiple of 4, so the region is 16-byte aligned).
+__host__ __device__ constexpr int gu_words(int d, int mt, bool xf32) {
+  return ((kGuWaves * kGuRows + kScalePad) * (d / 64) +
+          mt * (kGuParts * (((d / 32 + kGuParts - 1) / kGuParts) * (xf32 ? 32 : 16) + kSkewWords) +
+                kGuParts * ((d / 32 + kGuParts - 1) / kGuParts)) +
+          3) / 4 * 4;
+}
+
+// The grouping prologue (RMP > 0, small batches): the routed workgroups take
+// the top-k of every token from the router's partial sums (RMP = parts held
+// per logit) and group the batch in LDS, each for itself, with the same
+// device code as the route + union kernel, so every workgroup derives the same
+// grouping.  One of them also writes the top-k and the grouping out for the
+// down and combine kernels.  The shared expert's workgroups need no grouping
+// and go straight to their weights.
+template <int RMP>
+__device__ __forceinline__ void group_batch(const FfnArgs& g, const RouteArgs& r, RouteLds& rl) {
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int k = g.top_k, n = g.T * k;
+  const bool writer = blockIdx.x == 0 && blockIdx.y == static_cast<unsigned>(g.has_shared);
+  for (int t = wv; t < g.T; t += kGuWaves) {
+    topk_token<kRouteEpl, RMP>(r.part, r.P, r.bias, t, r.E, k, writer ? r.topk_idx : nullptr,
+                               r.topk_w, rl.tk[wv]);
+    if (lane < k) rl.sel[t][lane] = rl.tk[wv].sel_e[lane];
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const int e = lane < n ? rl.sel[lane / k][lane % k] : -1;
+    union_wave<kRouteEpl>(e, n, r.E, rl.counts, rl.offsets, rl.perm, rl.inv_perm, rl.active,
+                          rl.n_active, rl.cnt, rl.first);
+  }
+  __syncthreads();
+  if (writer) {
+    for (int i = threadIdx.x; i < r.E; i += blockDim.x) {
+      r.counts[i] = rl.counts[i];
+      r.offsets[i] = rl.offsets[i];
+      r.active[i] = rl.active[i];
+    }
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      r.perm[i] = rl.perm[i];
+      r.inv_perm[i] = rl.inv_perm[i];
+    }
+    if (threadIdx.x == 0) {
+      r.offsets[r.E] = rl.offsets[r.E];
+      r.n_active[0] = rl.n_active[0];
+    }
+  }
+}
+
+template <int MT, bool XF32, int RMP>
+__global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g, RouteArgs rt_args) {
   extern __shared__ __align__(16) uint32_t lds[];
   constexpr int XW = XF32 ? 32 : 16;
-  const Slot sl = resolve_slot(g, blockIdx.y);
+  const int32_t* perm = g.perm;
+  const int32_t* active = g.active;
+  const int32_t* offsets = g.offsets;
+  if constexpr (RMP > 0) {
+    if (blockIdx.y >= static_cast<unsigned>(g.has_shared)) {
+      RouteLds& rl = *reinterpret_cast<RouteLds*>(lds + gu_words(g.d, MT, XF32));
+      group_batch<RMP>(g, rt_args, rl);
+      perm = rl.perm;
+      active = rl.active;
+      offsets = rl.offsets;
+    }
+  }
+  const Slot sl = resolve_slot(g, blockIdx.y, active, offsets);
   if (!sl.live) return;
   // The two 32-row halves of a 64-row tile go to workgroups x and x + 8,
   // which run on the same XCD (workgroups are dealt to the 8 XCDs in turn),
@@ -421,7 +516,7 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g) {
     load_step<2>(res, cb, cb, ce, rt, first);
     load_step<2>(res, cb + kStep, cb, ce, rt, second);
     __syncthreads();
-    stage_x<XF32>(g, sl, m0, nt, L, xl, xs);
+    stage_x<XF32>(g, sl, perm, m0, nt, L, xl, xs);
     __syncthreads();
     float acc[2][MT];
     sweep<2, MT, XW, kSst>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
@@ -458,7 +553,7 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g) {
 template <int MT>
 __global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
   extern __shared__ __align__(16) uint32_t lds[];
-  const Slot sl = resolve_slot(g, blockIdx.y);
+  const Slot sl = resolve_slot(g, blockIdx.y, g.active, g.offsets);
   if (!sl.live) return;
   const int row0 = blockIdx.x * kDnWaves * kDnRows;  // first d-row of the workgroup
   const int tile = row0 / 64;
@@ -522,23 +617,36 @@ int dn_lds_bytes(int f, int mt) {
 
 constexpr int kMaxLds = 64 * 1024;
 
-template <int MT, bool XF32>
-hipError_t launch_mt(const FfnArgs& g, int slots, hipStream_t s) {
+int gu_route_lds_bytes(int d, int mt, bool xf32) {
+  return gu_words(d, mt, xf32) * 4 + static_cast<int>(sizeof(RouteLds));
+}
+
+// RMP = 0: the grouping comes from global memory; 8 or 16: the gate/up
+// kernel groups the batch (RouteArgs) and writes the grouping for the down
+// kernel.
+template <int MT, bool XF32, int RMP>
+hipError_t launch_mt(const FfnArgs& g, const RouteArgs& r, int slots, hipStream_t s) {
   const dim3 g1(g.f / (kGuWaves * kGuRows), slots), g2(g.d / (kDnWaves * kDnRows), slots);
-  hipError_t err = launch(decode_gateup<MT, XF32>, g1, dim3(kGuWaves * kWave),
-                          gu_lds_bytes(g.d, MT, XF32), s, g);
+  const int gu_lds = RMP > 0 ? gu_route_lds_bytes(g.d, MT, XF32) : gu_lds_bytes(g.d, MT, XF32);
+  hipError_t err = launch(decode_gateup<MT, XF32, RMP>, g1, dim3(kGuWaves * kWave), gu_lds, s, g, r);
   if (err != hipSuccess) return err;
   return launch(decode_down<MT>, g2, dim3(kDnWaves * kWave), dn_lds_bytes(g.f, MT), s, g);
 }
 
-}  // namespace
-
-size_t ffn_decode_workspace(int T, int k, int /*E*/, int /*d*/, int f, bool has_shared) {
-  const size_t rows = static_cast<size_t>(T) * (k + (has_shared ? 1 : 0));
-  return rows * f * 4;  // h as bf16 hi/lo pairs
+template <int RMP>
+hipError_t launch_any_mt(const FfnArgs& g, const RouteArgs& r, int slots, int mt, bool xf32,
+                         hipStream_t s) {
+  if (xf32) {
+    if (mt == 4) return launch_mt<4, true, RMP>(g, r, slots, s);
+    if (mt == 2) return launch_mt<2, true, RMP>(g, r, slots, s);
+    return launch_mt<1, true, RMP>(g, r, slots, s);
+  }
+  if (mt == 4) return launch_mt<4, false, RMP>(g, r, slots, s);
+  if (mt == 2) return launch_mt<2, false, RMP>(g, r, slots, s);
+  return launch_mt<1, false, RMP>(g, r, slots, s);
 }
 
-hipError_t launch_ffn_decode(const FfnProblem& p, hipStream_t stream) {
+FfnArgs ffn_args(const FfnProblem& p) {
   const size_t dd = p.d, ff = p.f;
   FfnArgs g{};
   g.experts = p.experts;
@@ -563,22 +671,64 @@ hipError_t launch_ffn_decode(const FfnProblem& p, hipStream_t stream) {
   g.hp = static_cast<uint32_t*>(p.workspace);
   g.y = static_cast<float*>(p.y);
   g.y_shared = static_cast<float*>(p.y_shared);
-  const int slots = g.has_shared + std::min(p.E, p.T * p.k);
+  return g;
+}
+
+// Tokens per sweep: as many as the batch offers, up to 4, LDS permitting
+// (gu_extra: bytes the gate/up kernel needs beyond its staging); 0 if even
+// one token does not fit.
+int pick_mt(const FfnProblem& p, int gu_extra) {
   const bool xf32 = !p.x_bf16;
-  // tokens per sweep: as many as the batch offers, up to 4, LDS permitting
   int mt = p.T >= 4 ? 4 : (p.T >= 2 ? 2 : 1);
-  while (mt > 1 && (gu_lds_bytes(p.d, mt, xf32) > kMaxLds || dn_lds_bytes(p.f, mt) > kMaxLds))
-    mt /= 2;
-  if (gu_lds_bytes(p.d, mt, xf32) > kMaxLds || dn_lds_bytes(p.f, mt) > kMaxLds)
-    return hipErrorNotSupported;
-  if (xf32) {
-    if (mt == 4) return launch_mt<4, true>(g, slots, stream);
-    if (mt == 2) return launch_mt<2, true>(g, slots, stream);
-    return launch_mt<1, true>(g, slots, stream);
-  }
-  if (mt == 4) return launch_mt<4, false>(g, slots, stream);
-  if (mt == 2) return launch_mt<2, false>(g, slots, stream);
-  return launch_mt<1, false>(g, slots, stream);
+  auto fits = [&](int m) {
+    return gu_words(p.d, m, xf32) * 4 + gu_extra <= kMaxLds && dn_lds_bytes(p.f, m) <= kMaxLds;
+  };
+  while (mt > 1 && !fits(mt)) mt /= 2;
+  return fits(mt) ? mt : 0;
+}
+
+}  // namespace
+
+size_t ffn_decode_workspace(int T, int k, int /*E*/, int /*d*/, int f, bool has_shared) {
+  const size_t rows = static_cast<size_t>(T) * (k + (has_shared ? 1 : 0));
+  return rows * f * 4;  // h as bf16 hi/lo pairs
+}
+
+hipError_t launch_ffn_decode(const FfnProblem& p, hipStream_t stream) {
+  const FfnArgs g = ffn_args(p);
+  const int slots = g.has_shared + std::min(p.E, p.T * p.k);
+  const int mt = pick_mt(p, 0);
+  if (mt == 0) return hipErrorNotSupported;
+  return launch_any_mt<0>(g, RouteArgs{}, slots, mt, !p.x_bf16, stream);
+}
+
+bool ffn_decode_groups_batch(const FfnProblem& p, int P) {
+  return p.T >= 1 && p.T <= kRouteMaxT && p.T * p.k <= kWave && p.E <= kRouteMaxE &&
+         p.k <= kMaxK && P <= 16 && pick_mt(p, static_cast<int>(sizeof(RouteLds))) > 0;
+}
+
+hipError_t launch_ffn_decode_grouping(const FfnProblem& p, const RouteGroup& rg,
+                                      hipStream_t stream) {
+  if (!ffn_decode_groups_batch(p, rg.P)) return hipErrorNotSupported;
+  const FfnArgs g = ffn_args(p);
+  RouteArgs r{};
+  r.part = rg.part;
+  r.bias = rg.bias;
+  r.P = rg.P;
+  r.E = p.E;
+  r.topk_idx = rg.topk_idx;
+  r.topk_w = rg.topk_w;
+  r.counts = rg.u.counts;
+  r.offsets = rg.u.offsets;
+  r.perm = rg.u.perm;
+  r.inv_perm = rg.u.inv_perm;
+  r.active = rg.u.active;
+  r.n_active = rg.u.n_active;
+  const int slots = g.has_shared + std::min(p.E, p.T * p.k);
+  const int mt = pick_mt(p, static_cast<int>(sizeof(RouteLds)));
+  if (mt == 0) return hipErrorNotSupported;
+  if (rg.P <= 8) return launch_any_mt<8>(g, r, slots, mt, !p.x_bf16, stream);
+  return launch_any_mt<16>(g, r, slots, mt, !p.x_bf16, stream);
 }
 
 }  // namespace moe

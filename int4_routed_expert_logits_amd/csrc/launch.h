@@ -53,6 +53,11 @@ hipError_t launch_route_union(int T, int d, int E, int k, const void* x, bool x_
                               int32_t* topk_idx, float* topk_w, const UnionOut& u,
                               hipStream_t stream);
 
+// route.hip: only the float64 logit partial sums of launch_route (the
+// workspace's [T][E][route_parts()] doubles).
+hipError_t launch_router_logits(int T, int d, int E, const void* x, bool x_bf16,
+                                const float* w_router, double* part, hipStream_t stream);
+
 // quant.hip: float weights -> int4 codes + float16 scales (per 64-column
 // group, or per row).
 hipError_t launch_quantize(int N, int K, const void* w, bool f32, bool per_row, uint8_t* codes,
@@ -78,6 +83,24 @@ struct FfnProblem {
 // ffn_decode.hip: int4 GEMV, float32 intermediate and outputs.
 size_t ffn_decode_workspace(int T, int k, int E, int d, int f, bool has_shared);
 hipError_t launch_ffn_decode(const FfnProblem& p, hipStream_t stream);
+
+// ffn_decode.hip: the same FFN for a small batch whose top-k and grouping
+// the gate/up kernel derives itself from the router's partial sums (part,
+// P parts per logit), writing them to topk_idx / topk_w and u (p.offsets,
+// p.perm, p.active and p.n_active must be u's arrays).
+struct RouteGroup {
+  const double* part;
+  int P;
+  const float* bias;
+  int32_t* topk_idx;
+  float* topk_w;
+  UnionOut u;
+};
+// Whether launch_ffn_decode_grouping takes this problem (batch size, experts,
+// parts per logit, LDS).
+bool ffn_decode_groups_batch(const FfnProblem& p, int P);
+hipError_t launch_ffn_decode_grouping(const FfnProblem& p, const RouteGroup& rg,
+                                      hipStream_t stream);
 
 // ffn_prefill.hip: grouped GEMM on bf16 MFMA, bf16 intermediate and outputs.
 size_t ffn_prefill_workspace(int T, int k, int E, int f, bool has_shared);

@@ -2,7 +2,9 @@
 
 Plumbing only: torch allocates the caller-owned device memory the C ABI
 expects, and ``run_layer`` issues moe_route_union -> moe_expert_ffn ->
-moe_combine on one stream with no host synchronisation in between.
+moe_combine on one stream with no host synchronisation in between;
+``run_layer_decode`` makes the single moe_layer_decode call instead (decode
+batches of at most 8 tokens).
 """
 from __future__ import annotations
 
@@ -32,6 +34,7 @@ class LayerBuffers:
     out: torch.Tensor
     workspace: torch.Tensor       # moe_route scratch
     ffn_workspace: torch.Tensor   # moe_expert_ffn scratch (the intermediate h)
+    layer_workspace: torch.Tensor  # moe_layer_decode scratch (decode path only)
 
     @classmethod
     def allocate(cls, shape, T: int, path: int, device="cuda", out_dtype=None):
@@ -42,6 +45,7 @@ class LayerBuffers:
         odt = out_dtype or ydt
         ws = max(B.moe_route_workspace_bytes(sh, T), 256)
         fws = max(B.moe_ffn_workspace_bytes(sh, T, path), 256)
+        lws = max(B.moe_layer_decode_workspace_bytes(sh, T), 256) if path == B.MOE_PATH_DECODE_F32 else 256
         return cls(
             shape=sh, T=T, path=path,
             topk_idx=torch.empty((T, k), **i32),
@@ -57,6 +61,7 @@ class LayerBuffers:
             out=torch.empty((T, d), dtype=odt, device=device),
             workspace=torch.empty((ws,), dtype=torch.uint8, device=device),
             ffn_workspace=torch.empty((fws,), dtype=torch.uint8, device=device),
+            layer_workspace=torch.empty((lws,), dtype=torch.uint8, device=device),
         )
 
 
@@ -69,4 +74,13 @@ def run_layer(x, w_router, bias, experts, shared, buf: LayerBuffers, stream=None
     B.moe_expert_ffn(sh, x, experts, shared, buf.offsets, buf.perm, buf.active, buf.n_active,
                      buf.path, buf.y, buf.y_shared, buf.ffn_workspace, stream)
     B.moe_combine(sh, buf.y, buf.y_shared, buf.inv_perm, buf.topk_w, buf.out, stream)
+    return buf.out
+
+
+def run_layer_decode(x, w_router, bias, experts, shared, buf: LayerBuffers, stream=None):
+    """The same layer for a decode batch of at most 8 tokens in one call
+    (moe_layer_decode): four launches, the same outputs as run_layer."""
+    B.moe_layer_decode(buf.shape, x, w_router, bias, experts, shared, buf.topk_idx, buf.topk_w,
+                       buf.counts, buf.offsets, buf.perm, buf.inv_perm, buf.active, buf.n_active,
+                       buf.y, buf.y_shared, buf.out, buf.layer_workspace, stream)
     return buf.out

@@ -89,6 +89,8 @@ def test_bad_shapes_are_rejected_by_every_call(lib, shape, status):
     assert lib.moe_combine(s, 4, P, None, 0, P, P, P, 0, None) == status
     assert lib.moe_route_union(s, 4, P, 0, P, None, P, P, P, P, P, P, P, P, P, 1 << 20,
                                None) == status
+    assert lib.moe_layer_decode(s, 4, P, 0, P, None, P, None, *([P] * 10), None, P, 0, P,
+                                1 << 30, None) == status
 
 
 def test_null_shape(lib):
@@ -132,6 +134,44 @@ def test_route_union_argument_checks(lib):
     assert call(counts=P + 2) == B.MOE_ERR_ALIGN
     assert call(nbytes=ws - 1) == B.MOE_ERR_WORKSPACE
     assert call(T=1 << 24) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_layer_decode_argument_checks(lib):
+    s = ctypes.byref(shp())
+    big = 1 << 30
+    ok = dict(T=4, x=P, xdt=0, w=P, bias=None, ex=P, sh=None, idx=P, tw=P, cnt=P, off=P, perm=P,
+              inv=P, act=P, na=P, y=P, ys=None, out=P, odt=0, ws=P, wsb=big)
+
+    def call(shape=s, **kw):
+        a = dict(ok, **kw)
+        return lib.moe_layer_decode(shape, a["T"], a["x"], a["xdt"], a["w"], a["bias"], a["ex"],
+                                    a["sh"], a["idx"], a["tw"], a["cnt"], a["off"], a["perm"],
+                                    a["inv"], a["act"], a["na"], a["y"], a["ys"], a["out"],
+                                    a["odt"], a["ws"], a["wsb"], None)
+
+    assert call(T=-1) == B.MOE_ERR_SHAPE
+    assert call(xdt=4) == B.MOE_ERR_DTYPE
+    assert call(odt=4) == B.MOE_ERR_DTYPE
+    # only small decode batches: at most 8 tokens, 64 slots and 256 experts
+    assert call(T=9) == B.MOE_ERR_UNSUPPORTED
+    assert call(shape=ctypes.byref(shp(E=64, k=16)), T=5) == B.MOE_ERR_UNSUPPORTED
+    assert call(shape=ctypes.byref(shp(E=512, k=8)), T=1) == B.MOE_ERR_UNSUPPORTED
+    for name in ("x", "w", "ex", "idx", "tw", "cnt", "off", "perm", "inv", "act", "na", "y",
+                 "out", "ws"):
+        assert call(**{name: None}) == B.MOE_ERR_NULL, name
+    assert call(sh=P) == B.MOE_ERR_NULL            # shared block given but no shared expert
+    s2 = ctypes.byref(shp(fs=256))
+    assert call(shape=s2, sh=P) == B.MOE_ERR_NULL  # y_shared missing
+    assert call(shape=s2, ys=P) == B.MOE_ERR_NULL  # shared block missing
+    assert call(x=MIS) == B.MOE_ERR_ALIGN
+    assert call(ex=MIS) == B.MOE_ERR_ALIGN
+    assert call(y=MIS) == B.MOE_ERR_ALIGN
+    assert call(out=MIS) == B.MOE_ERR_ALIGN
+    assert call(cnt=P + 2) == B.MOE_ERR_ALIGN
+    assert call(ws=P + 64) == B.MOE_ERR_ALIGN
+    need = moe.moe_layer_decode_workspace_bytes(shp(), 4)
+    assert need == moe.moe_route_workspace_bytes(shp(), 4) + moe.moe_ffn_workspace_bytes(shp(), 4, 0)
+    assert call(wsb=need - 1) == B.MOE_ERR_WORKSPACE
 
 
 def test_quantize_argument_checks(lib):

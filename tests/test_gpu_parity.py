@@ -15,7 +15,7 @@ import torch
 import oracle
 import synth
 import int4_routed_expert_logits_amd as moe
-from int4_routed_expert_logits_amd.layer import LayerBuffers, run_layer
+from int4_routed_expert_logits_amd.layer import LayerBuffers, run_layer, run_layer_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -335,13 +335,14 @@ def test_combine_parity(ybf16, obf16, shared):
 # whole layer, decode path
 # ----------------------------------------------------------------------------
 
-def gpu_layer(cfg, T, batch=0, path=DEC, experts_override=None):
+def gpu_layer(cfg, T, batch=0, path=DEC, experts_override=None, fused=False):
     L, dev = dev_layer(cfg)
     x, xf = tokens(cfg, T, batch)
     sh = moe.shape_of(L.shape)
     buf = LayerBuffers.allocate(sh, T, path)
     ex = dev["experts"] if experts_override is None else experts_override
-    run_layer(x, dev["w_router"], dev["bias"], ex, dev["shared"], buf)
+    run = run_layer_decode if fused else run_layer
+    run(x, dev["w_router"], dev["bias"], ex, dev["shared"], buf)
     torch.cuda.synchronize()
     return L, xf, buf
 
@@ -396,10 +397,12 @@ def check_routing_and_union(buf, ref_idx, ref_w, union):
 FULL_CASES = [(1, 4), (1, 3), (2, 1), (2, 16), (2, 5), (3, 64), (3, 13), (4, 1)]
 
 
-@pytest.mark.parametrize("cfg,T", FULL_CASES)
-def test_layer_decode_parity(cfg, T):
-    say(f"layer decode cfg={cfg} T={T}")
-    L, xf, buf = gpu_layer(cfg, T)
+# the separate calls, and (batches of at most 8 tokens) the one-call moe_layer_decode
+@pytest.mark.parametrize("cfg,T,fused", [(c, T, f) for c, T in FULL_CASES
+                                         for f in ((False, True) if T <= 8 else (False,))])
+def test_layer_decode_parity(cfg, T, fused):
+    say(f"layer decode cfg={cfg} T={T} fused={fused}")
+    L, xf, buf = gpu_layer(cfg, T, fused=fused)
     sh = L.shape
     ref = oracle.moe_layer(xf, L.w_router, L.bias, L.experts, L.shared, sh.d, sh.f,
                            sh.n_experts, sh.top_k)
@@ -427,6 +430,72 @@ def test_layer_decode_parity_19mb_layer_8_tokens_sampled():
     out = buf.out.cpu().numpy()
     ro = np.stack([ref["out"][t] for t in sorted(ref["out"])])
     assert rel_err(out[sorted(ref["out"])], ro) <= TOL_DECODE
+
+
+LAYER_OUTPUTS = ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm", "active",
+                 "n_active", "y", "y_shared", "out")
+
+
+@pytest.mark.parametrize("cfg,T,out_bf16", [(1, 4, False), (1, 3, True), (2, 1, False),
+                                            (2, 8, False), (2, 5, True), (3, 8, False),
+                                            (3, 1, False), (4, 1, False), (4, 8, True)])
+def test_layer_decode_call_equals_the_separate_calls(cfg, T, out_bf16):
+    """moe_layer_decode writes every output of route_union + expert_ffn +
+    combine, bit for bit (the same function computed with fewer launches)."""
+    say(f"moe_layer_decode vs separate calls cfg={cfg} T={T} out_bf16={out_bf16}")
+    L, dev = dev_layer(cfg)
+    x, _ = tokens(cfg, T)
+    sh = moe.shape_of(L.shape)
+    odt = torch.bfloat16 if out_bf16 else None
+    a = LayerBuffers.allocate(sh, T, DEC, out_dtype=odt)
+    b = LayerBuffers.allocate(sh, T, DEC, out_dtype=odt)
+    for t in (a.y, b.y):  # rows of unused positions are never written: same filler
+        t.fill_(0.0)
+    run_layer(x, dev["w_router"], dev["bias"], dev["experts"], dev["shared"], a)
+    run_layer_decode(x, dev["w_router"], dev["bias"], dev["experts"], dev["shared"], b)
+    torch.cuda.synchronize()
+    n = T * sh.top_k
+    for name in LAYER_OUTPUTS:
+        ta, tb = getattr(a, name), getattr(b, name)
+        if ta is None:
+            assert tb is None
+            continue
+        if name in ("perm", "inv_perm", "y"):
+            ta, tb = ta[:n], tb[:n]
+        assert torch.equal(ta.cpu(), tb.cpu()), name
+
+
+def test_layer_decode_call_reuses_its_workspace():
+    say("moe_layer_decode workspace reuse")
+    for cfg, T in ((4, 1), (2, 8)):
+        L, dev = dev_layer(cfg)
+        sh = moe.shape_of(L.shape)
+        buf = LayerBuffers.allocate(sh, T, DEC)
+        outs = []
+        for batch in (0, 1, 0, 1):
+            bits, _ = synth.make_tokens(cfg, T, batch=batch)
+            run_layer_decode(dev_x(bits), dev["w_router"], dev["bias"], dev["experts"],
+                             dev["shared"], buf)
+            torch.cuda.synchronize()
+            outs.append(buf.out.cpu().numpy().copy())
+        assert np.isfinite(outs[0]).all()
+        assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3])
+        assert not np.array_equal(outs[0], outs[1])
+
+
+def test_layer_decode_call_empty_batch():
+    say("moe_layer_decode T=0")
+    L, dev = dev_layer(2)
+    sh = moe.shape_of(L.shape)
+    buf = LayerBuffers.allocate(sh, 0, DEC)
+    buf.counts.fill_(7)
+    buf.n_active.fill_(7)
+    x = torch.empty((0, sh.d), dtype=torch.bfloat16, device="cuda")
+    run_layer_decode(x, dev["w_router"], dev["bias"], dev["experts"], dev["shared"], buf)
+    torch.cuda.synchronize()
+    assert int(buf.n_active.item()) == 0
+    assert int(buf.counts.sum().item()) == 0
+    assert int(buf.offsets[-1].item()) == 0
 
 
 def test_decode_is_deterministic_and_batch_invariant():
