@@ -1,7 +1,8 @@
 """Benchmark of the int4 routed-expert MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-graph]
-                    [--no-prefill] [--no-cpu-baseline]
+                    [--no-prefill] [--no-quantizer] [--no-cache] [--cache-slots S]
+                    [--no-cpu-baseline]
 
 A step is one pass of the whole layer -- route, batch-union, expert FFN,
 combine -- over one batch of synthetic tokens, with every input already
@@ -20,7 +21,9 @@ moe_combine: five launches) is timed too and reported beside it.
 The same run also reports the 2048-token prefill step of that layer (Zipf
 router bias, bf16 MFMA path) as tokens/s, the roofline of the dominant
 kernel (the expert FFN: HBM bytes for decode), timed with HIP events on the
-launch stream, and the CPU oracle timed on a bounded sample on the host cores.
+launch stream, the int4 quantiser, 1-token decode through a per-layer HBM
+expert cache whose misses stream from pinned host memory, and the CPU oracle
+timed on a bounded sample on the host cores.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -56,6 +59,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graphs")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-cache", action="store_true", help="skip the expert-cache leg")
+    ap.add_argument("--cache-slots", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--counters", action="store_true",
@@ -252,6 +257,11 @@ def main():
     if not args.no_quantizer:
         result["quantizer"] = bench_quantizer(torch, moe, dev)
 
+    # --------------------------------------------------------- expert cache
+    if not args.no_cache:
+        result["expert_cache"] = bench_cache(args, torch, moe, synth, sh, experts[0], shared[0],
+                                             w_router, dev)
+
     # ----------------------------------------------------------- CPU oracle
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(L, bb)
@@ -300,6 +310,81 @@ def bench_quantizer(torch, moe, dev, reps=20):
         "roofline": {"bound": "hbm", "kernel": "moe_quantize (gs64)", "achieved": round(gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": alg},
+    }
+
+
+PCIE_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def bench_cache(args, torch, moe, synth, sh, experts, shared, w_router, dev, warm=32, steps=64):
+    """1-token decode steps through a per-layer cache of --cache-slots
+    experts in HBM, the layer's 256 blocks in pinned host memory, Zipf(1.1)
+    router bias: tokens/s of the layer, hit rate, and the host -> HBM rate
+    of the misses against a plain pinned copy and the PCIe peak."""
+    from int4_routed_expert_logits_amd.layer import LayerBuffers
+    slots = args.cache_slots
+    bb = moe.moe_expert_bytes(sh.d, sh.f, 64)
+    host = torch.empty((experts.numel(),), dtype=torch.uint8, pin_memory=True)
+    host.copy_(experts.view(-1))
+    torch.cuda.synchronize()
+    # a plain pinned host -> HBM copy of 1 GiB: the practical link rate
+    blk = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    blk.copy_(host[: 1 << 30], non_blocking=True)
+    a.record()
+    for _ in range(3):
+        blk.copy_(host[: 1 << 30], non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    h2d = 3 * (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
+    del blk
+    dev_slots = torch.empty((slots * bb,), dtype=torch.uint8, device=dev)
+    bias = torch.from_numpy(synth.make_layer(5, experts=[]).bias).to(dev)
+    T = 1
+    buf = LayerBuffers.allocate(sh, T, moe.MOE_PATH_DECODE_F32)
+    ws = torch.empty((moe.moe_cache_workspace_bytes(sh, T, slots),), dtype=torch.uint8, device=dev)
+    xs = []
+    for i in range(warm + steps):
+        bits, _ = synth.make_tokens(4, T, batch=1000 + i)
+        xs.append(torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16))
+    copy_stream = torch.cuda.Stream()
+    cache = moe.moe_cache_create(sh, slots, dev_slots, host)
+    try:
+        def step(i):
+            moe.moe_cache_layer_decode(cache, xs[i], w_router, bias, shared, buf.topk_idx, buf.topk_w,
+                                       buf.y, buf.y_shared, buf.out, ws, copy_stream=copy_stream)
+        for i in range(warm):
+            step(i)
+        torch.cuda.synchronize()
+        h0, m0, b0 = moe.moe_cache_stats(cache)
+        t0 = time.perf_counter()
+        for i in range(warm, warm + steps):
+            step(i)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        h1, m1, b1 = moe.moe_cache_stats(cache)
+    finally:
+        torch.cuda.synchronize()
+        moe.moe_cache_destroy(cache)
+    hits, misses, nbytes = h1 - h0, m1 - m0, b1 - b0
+    fetch_gbps = nbytes / dt / 1e9
+    hit_rate = hits / max(1, hits + misses)
+    log(f"expert cache: {slots} slots, {steps / dt:.1f} tokens/s, hit rate {hit_rate:.3f}, "
+        f"{misses / steps:.2f} misses/token, host->HBM {fetch_gbps:.1f} GB/s "
+        f"(plain pinned copy {h2d:.1f} GB/s)")
+    return {
+        "value": round(steps / dt, 2),
+        "unit": "tokens/s (one layer)",
+        "workload": f"1-token decode steps of the d=6144 f=2048 layer through a {slots}-expert HBM "
+                    f"cache ({slots * bb / 1e9:.2f} GB), 256 blocks in pinned host memory, Zipf(1.1) "
+                    f"router bias, {warm} warm-up steps then {steps} timed",
+        "ms_per_step": round(dt * 1e3 / steps, 3),
+        "hit_rate": round(hit_rate, 4),
+        "misses_per_step": round(misses / steps, 3),
+        "roofline": {"bound": "pcie", "kernel": "host->HBM copies of missed experts",
+                     "achieved": round(fetch_gbps, 2), "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(fetch_gbps / PCIE_PEAK_GBPS, 4),
+                     "plain_pinned_copy_gbps": round(h2d, 2)},
     }
 
 

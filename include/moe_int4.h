@@ -20,6 +20,9 @@
  *                   for decode batches)
  *   moe_layer_decode the whole layer (route, union, expert FFN, combine) for
  *                   a decode batch of at most 8 tokens, in four launches
+ *   moe_cache_*     a per-layer cache of experts in HBM (LRU, pinned experts)
+ *                   whose misses stream from pinned host memory while the
+ *                   resident experts compute
  *   moe_quantize    float weights -> int4 codes + float16 scales (the
  *                   one-time conversion of a checkpoint)
  *   moe_pack_experts one-time byte permutation of the expert blocks into the
@@ -287,6 +290,82 @@ moe_status moe_layer_decode(const moe_shape* shape, int32_t T, const void* x, mo
                             int32_t* active, int32_t* n_active, void* y, void* y_shared,
                             void* out, moe_dtype out_dt, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/* ------------------------------------------------------------------------
+ * Per-layer expert cache (pages: zhichai.net, section on why mmap falls
+ * short -- every layer keeps an LRU cache of whole experts, and pinned hot
+ * experts take no part in eviction; yunpan.plus article, "capability 1" --
+ * per-layer LRU plus a pinned hot-store, and "capability 2" -- missing
+ * experts load asynchronously while the resident ones compute).
+ *
+ * A cache holds n_slots expert blocks in HBM for one layer whose E blocks
+ * live in pinned host memory.  Policy (host side, deterministic): a step's
+ * distinct experts that a slot holds are hits; the missing ones, in
+ * ascending id order, take the lowest empty slot, else the slot whose expert
+ * was used least recently (ties: the lower slot), never a pinned expert's
+ * slot or one used by the same step.  The cache object lives in host memory
+ * (allocated by moe_cache_create, freed by moe_cache_destroy); its first
+ * decode step also allocates a small pinned staging buffer and an event.
+ * Unlike the calls above, a cache keeps state: the calls on one cache must
+ * not overlap.
+ * ------------------------------------------------------------------------ */
+typedef struct moe_expert_cache moe_expert_cache;
+
+/* n_slots in [top_k, E].  device_slots: n_slots * moe_expert_bytes() bytes
+ * of device memory, 256-byte aligned; host_blocks: the layer's E packed
+ * blocks (moe_pack_experts layout) in pinned host memory (hipHostMalloc),
+ * 16-byte aligned.  Both stay owned by the caller and must outlive the
+ * cache.  Both NULL gives a planning-only cache (moe_cache_plan). */
+moe_status moe_cache_create(const moe_shape* shape, int32_t n_slots, uint8_t* device_slots,
+                            const uint8_t* host_blocks, moe_expert_cache** cache);
+void moe_cache_destroy(moe_expert_cache* cache);
+
+/* Pin (pinned != 0) or unpin an expert: a resident pinned expert is never
+ * evicted; pinning loads nothing by itself.  MOE_ERR_UNSUPPORTED if more
+ * than n_slots - top_k experts would be pinned. */
+moe_status moe_cache_pin(moe_expert_cache* cache, int32_t expert, int32_t pinned);
+
+/* One step of the policy on a planning-only cache, on the host (no GPU):
+ * experts [n] (host, ids in [0, E), repeats allowed) -> slot_of [n] (host
+ * out), and the experts the step fetches, in placement order: fetched [k']
+ * with evicted [k'] (the expert each displaced, -1 for an empty slot),
+ * k' = *n_fetched (arrays of n entries suffice).  MOE_ERR_UNSUPPORTED
+ * (state unchanged) if the pinned experts leave too few slots; on a cache
+ * with device slots MOE_ERR_UNSUPPORTED (the slots would no longer match
+ * what the device holds). */
+moe_status moe_cache_plan(moe_expert_cache* cache, int32_t n, const int32_t* experts,
+                          int32_t* slot_of, int32_t* fetched, int32_t* evicted,
+                          int32_t* n_fetched);
+
+/* Counters since creation: hits and misses (one per distinct expert of a
+ * step) and the bytes copied host -> HBM.  Any pointer may be NULL. */
+moe_status moe_cache_stats(const moe_expert_cache* cache, int64_t* hits, int64_t* misses,
+                           int64_t* bytes_fetched);
+
+/* Device scratch bytes of moe_cache_layer_decode (0 for an invalid shape). */
+size_t moe_cache_workspace_bytes(const moe_shape* shape, int32_t T, int32_t n_slots);
+
+/* One decode step of the layer through the cache: the router (as
+ * moe_route: topk_idx, topk_w), then -- after the one host wait of the
+ * call, for the routing -- the misses are copied from host_blocks into
+ * their slots on copy_stream while the FFN of the resident experts and the
+ * shared expert runs on `stream`; `stream` then waits for the copies, runs
+ * the FFN of the fetched experts and the combine.  out (out_dt) is, bit for
+ * bit, the layer output of the separate calls with every expert resident;
+ * y (float32 [T*k][d]) is in the cache's grouped order (by slot);
+ * y_shared (float32 [T][d]) as moe_expert_ffn writes it.
+ *  x: bf16 or f32 [T][d]; w_router, bias, shared: as for moe_route and
+ *  moe_expert_ffn.  workspace >= moe_cache_workspace_bytes(shape, T,
+ *  n_slots), 256-byte aligned.
+ * T * top_k <= 1024, and n_slots - (pinned experts) >= min(E, T * top_k)
+ * (else MOE_ERR_UNSUPPORTED, nothing enqueued).  MOE_ERR_NULL on a
+ * planning-only cache. */
+moe_status moe_cache_layer_decode(moe_expert_cache* cache, int32_t T, const void* x,
+                                  moe_dtype x_dt, const float* w_router, const float* bias,
+                                  const uint8_t* shared, int32_t* topk_idx, float* topk_w,
+                                  void* y, void* y_shared, void* out, moe_dtype out_dt,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  void* copy_stream);
 
 /* Static text for a status code. */
 const char* moe_status_str(moe_status status);

@@ -28,7 +28,9 @@ MOE_QUANT_GS64, MOE_QUANT_ROW = 0, 1
 EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_quantize", "moe_route_workspace_bytes",
            "moe_route", "moe_union", "moe_route_union", "moe_ffn_workspace_bytes",
            "moe_expert_ffn", "moe_combine", "moe_layer_decode_workspace_bytes",
-           "moe_layer_decode", "moe_status_str")
+           "moe_layer_decode", "moe_cache_create", "moe_cache_destroy", "moe_cache_pin",
+           "moe_cache_plan", "moe_cache_stats", "moe_cache_workspace_bytes",
+           "moe_cache_layer_decode", "moe_status_str")
 
 
 class Shape(ctypes.Structure):
@@ -88,6 +90,22 @@ def load():
                                       c_void_p] + [c_void_p] * 11 + [c_int32, c_void_p, c_size_t,
                                                                      c_void_p])
     lib.moe_layer_decode.restype = c_int32
+    vp = c_void_p
+    lib.moe_cache_create.argtypes = [sp, c_int32, vp, vp, POINTER(vp)]
+    lib.moe_cache_create.restype = c_int32
+    lib.moe_cache_destroy.argtypes = [vp]
+    lib.moe_cache_destroy.restype = None
+    lib.moe_cache_pin.argtypes = [vp, c_int32, c_int32]
+    lib.moe_cache_pin.restype = c_int32
+    lib.moe_cache_plan.argtypes = [vp, c_int32, vp, vp, vp, vp, vp]
+    lib.moe_cache_plan.restype = c_int32
+    lib.moe_cache_stats.argtypes = [vp, vp, vp, vp]
+    lib.moe_cache_stats.restype = c_int32
+    lib.moe_cache_workspace_bytes.argtypes = [sp, c_int32, c_int32]
+    lib.moe_cache_workspace_bytes.restype = c_size_t
+    lib.moe_cache_layer_decode.argtypes = [vp, c_int32, vp, c_int32, vp, vp, vp, vp, vp, vp, vp,
+                                           vp, c_int32, vp, c_size_t, vp, vp]
+    lib.moe_cache_layer_decode.restype = c_int32
     lib.moe_pack_experts.argtypes = [sp, ctypes.c_int64, c_void_p, c_void_p, c_void_p]
     lib.moe_pack_experts.restype = c_int32
     lib.moe_quantize.argtypes = [c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
@@ -241,3 +259,66 @@ def moe_layer_decode(shape, x, w_router, bias, experts, shared, topk_idx, topk_w
         _ptr(perm), _ptr(inv_perm), _ptr(active), _ptr(n_active), _ptr(y), _ptr(y_shared),
         _ptr(out), _dtype(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# per-layer expert cache
+# ----------------------------------------------------------------------------
+
+def moe_cache_create(shape, n_slots: int, device_slots=None, host_blocks=None) -> int:
+    """Handle of a new cache (device_slots / host_blocks: tensors or None
+    for a planning-only cache)."""
+    h = c_void_p()
+    _check("moe_cache_create", load().moe_cache_create(
+        ctypes.byref(_shape(shape)), n_slots, _ptr(device_slots), _ptr(host_blocks),
+        ctypes.byref(h)))
+    return h.value
+
+
+def moe_cache_destroy(cache: int):
+    load().moe_cache_destroy(cache)
+
+
+def moe_cache_pin(cache: int, expert: int, pinned: bool = True):
+    _check("moe_cache_pin", load().moe_cache_pin(cache, expert, 1 if pinned else 0))
+
+
+def moe_cache_plan(cache: int, experts):
+    """One policy step on a planning-only cache: experts (host ints) ->
+    (slot_of per entry, fetched experts in placement order, the expert each
+    displaced or -1)."""
+    import numpy as np
+    e = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+    n = e.size
+    slot_of = np.empty(max(n, 1), np.int32)
+    fetched = np.empty(max(n, 1), np.int32)
+    evicted = np.empty(max(n, 1), np.int32)
+    nf = c_int32(0)
+    _check("moe_cache_plan", load().moe_cache_plan(
+        cache, n, e.ctypes.data, slot_of.ctypes.data, fetched.ctypes.data, evicted.ctypes.data,
+        ctypes.addressof(nf)))
+    k = nf.value
+    return slot_of[:n].copy(), fetched[:k].copy(), evicted[:k].copy()
+
+
+def moe_cache_stats(cache: int):
+    """(hits, misses, bytes fetched) since creation."""
+    h, m, b = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check("moe_cache_stats", load().moe_cache_stats(cache, ctypes.addressof(h),
+                                                     ctypes.addressof(m), ctypes.addressof(b)))
+    return h.value, m.value, b.value
+
+
+def moe_cache_workspace_bytes(shape, T: int, n_slots: int) -> int:
+    return load().moe_cache_workspace_bytes(ctypes.byref(_shape(shape)), T, n_slots)
+
+
+def moe_cache_layer_decode(cache: int, x, w_router, bias, shared, topk_idx, topk_w, y, y_shared,
+                           out, workspace, stream=None, copy_stream=None):
+    """One decode step of the layer through the cache (copies of missing
+    experts on copy_stream, overlapped with the resident experts' FFN)."""
+    _check("moe_cache_layer_decode", load().moe_cache_layer_decode(
+        cache, x.shape[0], _ptr(x), _dtype(x), _ptr(w_router), _ptr(bias), _ptr(shared),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(y), _ptr(y_shared), _ptr(out), _dtype(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
+        _stream(copy_stream) if copy_stream is not None else _stream(stream)))
