@@ -26,6 +26,23 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// (v & mask) | bits in one VALU instruction (v_and_or_b32).  With both
+// constants known, the compiler emits an AND and an OR with a literal each (a
+// gfx9 VOP3 instruction reads at most one scalar or literal operand); an
+// empty asm statement hides the value of `bits` in a vector register, so the
+// and-or pattern is selected with the mask in a scalar register.  The asm
+// emits no instruction: every instruction here is the compiler's own, and so
+// is the hazard bookkeeping between it and the matrix instructions that
+// read its result.
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t c) {
+  asm("" : "+v"(c));
+  return c;
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bits_vgpr) {
+  return (v & mask) | bits_vgpr;
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64);
 // every lane of a group receives the group's sum.
 __device__ __forceinline__ float group_sum(float v, int width) {

@@ -28,10 +28,10 @@
 // staged once in LDS; the parts of a row are skewed by 16 bytes so that the
 // lanes of one LDS read hit different banks.
 //
-// Dequant: with the packed nibble order, ((w >> 4i) & 0x000F000F) ^ 0x43084308
-// is the bf16 pair (136 + q_a, 136 + q_b) of two neighbouring columns, exactly
-// (the XOR sets the exponent 2^7 and turns the two's-complement nibble q into
-// q + 8).  v_dot2_f32_bf16 multiplies it with the activation pair (products
+// Dequant: with the packed nibble order (offset-binary nibbles q + 8),
+// ((w >> 4i) & 0x000F000F) | 0x43004300 is the bf16 pair (136 + q_a, 136 + q_b)
+// of two neighbouring columns, exactly (the OR sets the exponent 2^7 above the
+// 7-bit mantissa q + 8): one shift and one and-or per pair.  v_dot2_f32_bf16 multiplies it with the activation pair (products
 // exact in fp32); the 136 offset is removed with the chunk's activation sum
 // and the fp16 group scale applied once per 32 codes.  float32 activations
 // and the float32 h fed to the down projection are carried as bf16 hi + lo
@@ -51,9 +51,9 @@ namespace moe {
 
 namespace {
 
-constexpr int kStep = 2;  // chunks per matrix per pipeline step
+constexpr int kStep = 2;  // chunks per matrix per pipeline step (3 and 4 measured slower)
 constexpr uint32_t kMask = 0x000F000Fu;
-constexpr uint32_t kMagicX = 0x43084308u;  // bf16 exponent 2^7 | nibble sign flip
+constexpr uint32_t kMagic = 0x43004300u;  // bf16 exponent 2^7 in both halves
 constexpr float kOffset = 136.0f;
 
 constexpr int kGuRows = 8;     // gate/up rows per wavefront
@@ -208,6 +208,7 @@ __device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int
     const int c = cl + i;
     if (c >= nl) break;
     float tc[NM][MT];
+    const uint32_t mg = opaque_vgpr(kMagic);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       // the activation pairs of this 8-column word, once for every matrix
@@ -223,10 +224,10 @@ __device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int
 #pragma unroll
       for (int mat = 0; mat < NM; ++mat) {
         const uint32_t u = w == 0 ? d.q[mat][i].x : w == 1 ? d.q[mat][i].y : w == 2 ? d.q[mat][i].z : d.q[mat][i].w;
-        const uint32_t b0 = (u & kMask) ^ kMagicX;
-        const uint32_t b1 = ((u >> 4) & kMask) ^ kMagicX;
-        const uint32_t b2 = ((u >> 8) & kMask) ^ kMagicX;
-        const uint32_t b3 = ((u >> 12) & kMask) ^ kMagicX;
+        const uint32_t b0 = and_or(u, kMask, mg);
+        const uint32_t b1 = and_or((u >> 4), kMask, mg);
+        const uint32_t b2 = and_or((u >> 8), kMask, mg);
+        const uint32_t b3 = and_or((u >> 12), kMask, mg);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m < nt) {

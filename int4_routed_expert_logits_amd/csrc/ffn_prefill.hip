@@ -25,9 +25,10 @@
 // them).
 //
 // Dequant into the MFMA: a 4-byte word of the packed codes holds 8
-// consecutive input columns, and ((w >> 4i) & 0x000F000F) ^ 0x43084308 is
-// the bf16 pair (136 + q) of columns 2i, 2i+1 -- exact -- so one word is one
-// 8-element B operand.  Per 64-column scale group g the MFMAs accumulate
+// consecutive input columns as offset-binary nibbles (q + 8), and
+// ((w >> 4i) & 0x000F000F) | 0x43004300 is the bf16 pair (136 + q) of columns
+// 2i, 2i+1 -- exact -- so one word is one 8-element B operand (seven VALU
+// instructions).  Per 64-column scale group g the MFMAs accumulate
 // P = sum_k x[m,k] (136 + q[k,n]) on top of a correction C = -136 S_g[m]
 // (S_g the row's activation sum over the group), and the group scale is
 // applied once: acc += s[n,g] * P.  C comes from the same MFMA with a B
@@ -54,7 +55,7 @@ constexpr int kBM = 32;        // rows per small M-tile
 constexpr int kBigM = 128;     // rows per big M-tile
 constexpr int kBigMinRows = 96;  // fewest rows a big tile is used for
 constexpr uint32_t kMask = 0x000F000Fu;
-constexpr uint32_t kMagicX = 0x43084308u;
+constexpr uint32_t kMagic = 0x43004300u;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kMaxLds = 160 * 1024;
 
@@ -189,8 +190,9 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 
 // The 8-element B operand of packed word w: bf16 pairs (136 + q).
 __device__ __forceinline__ bf16x8_t dequant_word(uint32_t w) {
-  const uint4 b = make_uint4((w & kMask) ^ kMagicX, ((w >> 4) & kMask) ^ kMagicX,
-                             ((w >> 8) & kMask) ^ kMagicX, ((w >> 12) & kMask) ^ kMagicX);
+  const uint32_t mg = opaque_vgpr(kMagic);
+  const uint4 b = make_uint4(and_or(w, kMask, mg), and_or(w >> 4, kMask, mg),
+                             and_or(w >> 8, kMask, mg), and_or(w >> 12, kMask, mg));
   return as_bf16x8(b);
 }
 
@@ -523,35 +525,54 @@ struct Big {
   static constexpr int kAWords = kBigM * kALd / 2;        // A buffer (32-bit words)
   static constexpr int kBWords = NM * kWgCols * 32 / 4;   // codes of one group
   static constexpr int kBufWords = kAWords + kBWords;
+  static constexpr int kPieces = NM * kTilesN / 2;        // 16-byte code pieces per thread
+  static_assert(kPieces >= 1 && NM * kTilesN % 2 == 0, "codes of a group: whole pieces per thread");
   static int lds_bytes(int groups) {
     return (2 * kBufWords + NM * kWgCols * groups / 2) * 4;
   }
 };
 
 // Global loads of group grp (clamped to the last group): this thread's 32 A
-// columns of its row and one 16-byte piece of the codes.  Every address is
-// valid -- rows past the slot read a row of the slot, tiles past the end of
-// the matrix read its last tile -- and big_store masks those, so the loads
+// columns of its row and kPieces 16-byte pieces of the codes.  Every address
+// is valid -- rows past the slot read a row of the slot, tiles past the end
+// of the matrix read its last tile -- and big_store masks those, so the loads
 // are unconditional and a wait for one group's loads leaves the next group's
 // in flight.
+//
+// Code piece p = t + 256 i of a group (i < kPieces) is row `row` (of 64) of
+// half h (32 columns) of packed tile tt of matrix mat, with
+// p = ((mat * kTilesN + tt) * 2 + h) * 64 + row.
+template <int NM, int NS>
+__device__ __forceinline__ void big_piece(int i, int& mat, int& tt, int& h, int& row) {
+  using C = Big<NM, NS>;
+  const int p = threadIdx.x + 256 * i;
+  mat = p / (C::kTilesN * 128);
+  const int r = p - mat * (C::kTilesN * 128);
+  tt = r / 128;
+  h = (r / 64) & 1;
+  row = r & 63;
+}
+
 template <int NM, int NS>
 __device__ __forceinline__ void big_load(const uint16_t* rowp, int ahalf, int grp, int groups,
                                          int K, int ntv, const uint8_t* const (&qbase)[NM],
-                                         uint4 (&ra)[4], uint4& rb) {
+                                         uint4 (&ra)[4], uint4 (&rb)[Big<NM, NS>::kPieces]) {
   grp = min(grp, groups - 1);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     ra[j] = *reinterpret_cast<const uint4*>(rowp + grp * 64 + ahalf * 32 + j * 8);
-  constexpr int kPer = 256 / NM;  // threads per matrix
-  const int t = threadIdx.x;
-  const int mat = t / kPer, r = t % kPer;
-  const int tt = min(r / 128, ntv - 1), h = (r / 64) & 1, row = r & 63;
-  const uint8_t* src = qbase[0];
 #pragma unroll
-  for (int mm = 1; mm < NM; ++mm)
-    if (mat == mm) src = qbase[mm];
-  rb = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(tt) * 32 * K +
-                                       static_cast<size_t>(2 * grp + h) * 1024 + row * 16);
+  for (int i = 0; i < Big<NM, NS>::kPieces; ++i) {
+    int mat, tt, h, row;
+    big_piece<NM, NS>(i, mat, tt, h, row);
+    tt = min(tt, ntv - 1);
+    const uint8_t* src = qbase[0];
+#pragma unroll
+    for (int mm = 1; mm < NM; ++mm)
+      if (mat == mm) src = qbase[mm];
+    rb[i] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(tt) * 32 * K +
+                                            static_cast<size_t>(2 * grp + h) * 1024 + row * 16);
+  }
 }
 
 __device__ __forceinline__ uint4 masked(const uint4& v, uint32_t keep) {
@@ -562,17 +583,19 @@ __device__ __forceinline__ uint4 masked(const uint4& v, uint32_t keep) {
 // the codes (zero past the matrix).
 template <int NM, int NS>
 __device__ __forceinline__ void big_store(uint32_t* buf, int arow, int ahalf, const uint4 (&ra)[4],
-                                          const uint4& rb, uint32_t akeep, uint32_t bkeep) {
+                                          const uint4 (&rb)[Big<NM, NS>::kPieces], uint32_t akeep,
+                                          int ntv) {
   using C = Big<NM, NS>;
   uint4* a = reinterpret_cast<uint4*>(buf + (arow * kALd + ahalf * 32) / 2);
 #pragma unroll
   for (int j = 0; j < 4; ++j) a[j] = masked(ra[j], akeep);
-  constexpr int kPer = 256 / NM;
-  const int t = threadIdx.x;
-  const int mat = t / kPer, r = t % kPer;
-  const int tt = r / 128, h = (r / 64) & 1, row = r & 63;
-  reinterpret_cast<uint4*>(buf + C::kAWords)[(mat * 2 + h) * C::kWgCols + tt * 64 + row] =
-      masked(rb, bkeep);
+#pragma unroll
+  for (int i = 0; i < C::kPieces; ++i) {
+    int mat, tt, h, row;
+    big_piece<NM, NS>(i, mat, tt, h, row);
+    reinterpret_cast<uint4*>(buf + C::kAWords)[(mat * 2 + h) * C::kWgCols + tt * 64 + row] =
+        masked(rb[i], tt < ntv ? 0xFFFFFFFFu : 0u);
+  }
 }
 
 template <int NM, int NS>
@@ -657,7 +680,6 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   const int t = threadIdx.x, arow = t >> 1, ahalf = t & 1;
   const int m = m0 + arow;
   const uint32_t akeep = m < sl.M ? 0xFFFFFFFFu : 0u;
-  const uint32_t bkeep = (t % (256 / NM)) / 128 < ntv ? 0xFFFFFFFFu : 0u;
   const uint16_t* rowp;
   {
     const int mr = m < sl.M ? m : m0;  // rows past the slot read the first row (masked)
@@ -673,10 +695,10 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
 
   // Two register sets: group g+1 is stored to LDS while g+2 is in flight,
   // so every group's loads have two groups of math to land.
-  uint4 ra[2][4], rb[2];
+  uint4 ra[2][4], rb[2][C::kPieces];
   big_load<NM, NS>(rowp, ahalf, 0, groups, K, ntv, qbase, ra[0], rb[0]);
   big_load<NM, NS>(rowp, ahalf, 1, groups, K, ntv, qbase, ra[1], rb[1]);
-  big_store<NM, NS>(buf0, arow, ahalf, ra[0], rb[0], akeep, bkeep);
+  big_store<NM, NS>(buf0, arow, ahalf, ra[0], rb[0], akeep, ntv);
   __syncthreads();
   f32x16_t acc[2][NM][NS];
 #pragma unroll
@@ -691,12 +713,12 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
     // group g0 is in buf0, group g0 + 1 in register set 1
     big_load<NM, NS>(rowp, ahalf, g0 + 2, groups, K, ntv, qbase, ra[0], rb[0]);
     big_math<NM, NS>(buf0, sc, groups, g0, wm, wn, col, half, acc);
-    big_store<NM, NS>(buf1, arow, ahalf, ra[1], rb[1], akeep, bkeep);
+    big_store<NM, NS>(buf1, arow, ahalf, ra[1], rb[1], akeep, ntv);
     __syncthreads();
     if (g0 + 1 < groups) {
       big_load<NM, NS>(rowp, ahalf, g0 + 3, groups, K, ntv, qbase, ra[1], rb[1]);
       big_math<NM, NS>(buf1, sc, groups, g0 + 1, wm, wn, col, half, acc);
-      big_store<NM, NS>(buf0, arow, ahalf, ra[0], rb[0], akeep, bkeep);
+      big_store<NM, NS>(buf0, arow, ahalf, ra[0], rb[0], akeep, ntv);
       __syncthreads();
     }
   }
@@ -715,9 +737,12 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
           if (n < N) out[n] = f32_to_bf16(acc[i][0][ns][e]);
         }
       } else {
-        const float hv = silu(acc[i][0][0][e]) * acc[i][1][0][e];
-        g.h[static_cast<size_t>(row_of(g, sl, mm)) * g.f + n0 + wn * C::kWaveCols + col] =
-            f32_to_bf16(hv);
+        uint16_t* hrow = g.h + static_cast<size_t>(row_of(g, sl, mm)) * g.f;
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          const int n = n0 + wn * C::kWaveCols + ns * 32 + col;
+          if (n < N) hrow[n] = f32_to_bf16(silu(acc[i][0][ns][e]) * acc[i][1][ns][e]);
+        }
       }
     }
   }
@@ -800,6 +825,8 @@ hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream) {
   g.y_shared = static_cast<uint16_t*>(p.y_shared);
   const int ms = max_small(p.T, p.k, g.slots, p.has_shared);
   const int mb = max_big(p.T, p.k, p.has_shared);
+  // gate/up: 64 columns of both matrices per workgroup (128 columns measured
+  // slower: the scales of the wider tile leave LDS for one workgroup per CU)
   using GU = Big<2, 1>;
   using DN = Big<1, 2>;
   const int lds_gu = GU::lds_bytes(p.d / 64), lds_dn = DN::lds_bytes(p.f / 64);

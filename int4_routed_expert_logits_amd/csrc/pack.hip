@@ -11,7 +11,10 @@
 // one contiguous kilobyte.  Inside each 4-byte word (8 columns 8w..8w+7) the
 // nibble of column 8w+j moves to bit 4*(j/2) + 16*(j%2), so that
 // (word >> 4i) & 0x000F000F holds columns (8w+2i, 8w+2i+1) in its two
-// 16-bit halves.  Scales follow the same 64-row tiles, group-major inside a
+// 16-bit halves, and each nibble is stored in offset binary (the
+// two's-complement code q with its top bit flipped, i.e. q + 8 in [0, 15]),
+// so that one OR with 0x43004300 turns such a pair into the exact bf16 pair
+// (136 + q_a, 136 + q_b).  Scales follow the same 64-row tiles, group-major inside a
 // tile: row t*64+l, group g goes to
 //     s_off + (t*(K/64)*64 + g*64 + l)*2
 // so the scales of one group for a whole tile are one 128-byte run (a
@@ -41,7 +44,7 @@ __device__ __forceinline__ uint32_t interleave_word(uint32_t w) {
   uint32_t out = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) out |= ((w >> (4 * j)) & 0xFu) << (4 * (j >> 1) + 16 * (j & 1));
-  return out;
+  return out ^ 0x88888888u;  // q -> q + 8 in every nibble
 }
 
 struct MatGeom {

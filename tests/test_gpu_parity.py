@@ -568,7 +568,9 @@ def test_empty_batch_is_a_no_op():
 def np_pack_block(blk, d, f):
     """The packed layout, restated with numpy reshapes: 64-row tiles, 32-column
     chunks of 16 bytes per row, nibble j of each 4-byte word moved to bit
-    4*(j//2) + 16*(j%2); scales in the same 64-row tiles, group-major."""
+    4*(j//2) + 16*(j%2) and stored as q + 8 (offset binary: the top bit of
+    each two's-complement nibble flipped); scales in the same 64-row tiles,
+    group-major."""
     blk = np.asarray(blk, dtype=np.uint8)
     out = np.empty_like(blk)
     s0 = 3 * d * f // 2
@@ -579,7 +581,9 @@ def np_pack_block(blk, d, f):
         words = blk[qo:qo + nq].view("<u4").reshape(N // 64, 64, K // 32, 4).astype(np.uint64)
         new = np.zeros_like(words)
         for j in range(8):
-            new |= ((words >> np.uint64(4 * j)) & np.uint64(0xF)) << np.uint64(4 * (j // 2) + 16 * (j % 2))
+            q = ((words >> np.uint64(4 * j)) & np.uint64(0xF)).astype(np.int64)
+            q = np.where(q >= 8, q - 16, q)                        # two's-complement code
+            new |= (q + 8).astype(np.uint64) << np.uint64(4 * (j // 2) + 16 * (j % 2))
         tiled = new.astype("<u4").transpose(0, 2, 1, 3)          # [tile][chunk][row][word]
         out[qo:qo + nq] = np.ascontiguousarray(tiled).view(np.uint8).reshape(-1)
         ns = N * (K // 64) * 2
