@@ -165,7 +165,7 @@ size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path)
     return round_up(moe::ffn_decode_workspace(T, shape->top_k, shape->n_experts, shape->d,
                                               shape->f, sh));
   if (path == MOE_PATH_PREFILL_BF16)
-    return round_up(moe::ffn_prefill_workspace(T, shape->top_k, shape->n_experts, shape->f, sh));
+    return round_up(moe::ffn_prefill_workspace(T, shape->top_k, shape->n_experts, shape->d, shape->f, sh));
   return 0;
 }
 

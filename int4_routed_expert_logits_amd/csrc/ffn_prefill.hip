@@ -31,9 +31,12 @@
 // instructions).  Per 64-column scale group g the MFMAs accumulate
 // P = sum_k x[m,k] (136 + q[k,n]) on top of a correction C = -136 S_g[m]
 // (S_g the row's activation sum over the group), and the group scale is
-// applied once: acc += s[n,g] * P.  C comes from the same MFMA with a B
-// operand that is -136 everywhere; it is the same for every column, so it is
-// formed once per row block and group and shared by every column tile.
+// applied once: acc += s[n,g] * P.  C is the same for every column, so it
+// is formed once per row block and group and shared by every column tile:
+// in the 32-row tiles by the same MFMA with a B operand that is -136
+// everywhere; in the 128-row tiles by one MFMA whose A operand holds the
+// row's group sum, precomputed per row and split into three bf16 parts
+// (prefill_rowsums), against -136 in the three matching B elements.
 // The weights enter the products exactly (so do x * 136); only the float32
 // accumulation and the bf16 rounding of H and Y round.  Activations are
 // bf16 (an f32 x is rejected by the C ABI).
@@ -80,6 +83,12 @@ struct PrefillArgs {
   int* n_tiles;
   int2* big_tiles;     // (slot, first row) of every 128-row M-tile
   int* n_big;
+  // Per row and 64-column group, the row's sum over the group split into
+  // three bf16 parts (hi | mid << 16, lo): of the x tokens [T][d/64] and of
+  // the h rows [T*k + T][f/64].  The 128-row tiles form the -136 * sum
+  // correction from them with one MFMA.
+  uint2* sum_x;
+  uint2* sum_h;
 };
 
 struct Slot {
@@ -180,6 +189,43 @@ __global__ __launch_bounds__(1024) void prefill_tiles(PrefillArgs g) {
     g.n_tiles[0] = base_s;
     g.n_big[0] = base_b;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Row sums per 64-column group: thread (row, group) adds the group's 64 bf16
+// values in float32 in a fixed order (eight runs of eight, then the runs in
+// order) and splits the sum s into bf16 parts hi + mid + lo (each the
+// nearest bf16 of what the parts before leave), which carry s to about 24
+// bits.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void prefill_rowsums(const uint16_t* src, int rows, int K,
+                                                       uint2* dst) {
+  const int groups = K / 64;
+  const long long i = blockIdx.x * 256ll + threadIdx.x;
+  if (i >= static_cast<long long>(rows) * groups) return;
+  const long long r = i / groups;
+  const int grp = static_cast<int>(i - r * groups);
+  const uint4* p = reinterpret_cast<const uint4*>(src + r * K + grp * 64);
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4 v = p[j];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float run = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      run += __uint_as_float(w[q] << 16);
+      run += __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+    sum += run;
+  }
+  const uint32_t hi = f32_to_bf16(sum);
+  const float r1 = sum - bf16_to_f32(static_cast<uint16_t>(hi));
+  const uint32_t mid = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(static_cast<uint16_t>(mid));
+  const uint32_t lo = f32_to_bf16(r2);
+  dst[i] = make_uint2(hi | (mid << 16), lo);
 }
 
 // ---------------------------------------------------------------------------
@@ -524,11 +570,12 @@ struct Big {
   static constexpr int kTilesN = kWgCols / 64;            // packed 64-row tiles per matrix
   static constexpr int kAWords = kBigM * kALd / 2;        // A buffer (32-bit words)
   static constexpr int kBWords = NM * kWgCols * 32 / 4;   // codes of one group
-  static constexpr int kBufWords = kAWords + kBWords;
+  static constexpr int kCWords = kBigM * 4;                // row sums: 16 bytes per row
+  static constexpr int kBufWords = kAWords + kBWords + kCWords;
   static constexpr int kPieces = NM * kTilesN / 2;        // 16-byte code pieces per thread
   static_assert(kPieces >= 1 && NM * kTilesN % 2 == 0, "codes of a group: whole pieces per thread");
   static int lds_bytes(int groups) {
-    return (2 * kBufWords + NM * kWgCols * groups / 2) * 4;
+    return (2 * kBufWords + NM * kWgCols * groups / 2 + 4) * 4;  // + 16 zero bytes
   }
 };
 
@@ -554,10 +601,12 @@ __device__ __forceinline__ void big_piece(int i, int& mat, int& tt, int& h, int&
 }
 
 template <int NM, int NS>
-__device__ __forceinline__ void big_load(const uint16_t* rowp, int ahalf, int grp, int groups,
-                                         int K, int ntv, const uint8_t* const (&qbase)[NM],
-                                         uint4 (&ra)[4], uint4 (&rb)[Big<NM, NS>::kPieces]) {
+__device__ __forceinline__ void big_load(const uint16_t* rowp, const uint2* sump, int ahalf,
+                                         int grp, int groups, int K, int ntv,
+                                         const uint8_t* const (&qbase)[NM], uint4 (&ra)[4],
+                                         uint2& rs, uint4 (&rb)[Big<NM, NS>::kPieces]) {
   grp = min(grp, groups - 1);
+  rs = sump[grp];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     ra[j] = *reinterpret_cast<const uint4*>(rowp + grp * 64 + ahalf * 32 + j * 8);
@@ -583,12 +632,16 @@ __device__ __forceinline__ uint4 masked(const uint4& v, uint32_t keep) {
 // the codes (zero past the matrix).
 template <int NM, int NS>
 __device__ __forceinline__ void big_store(uint32_t* buf, int arow, int ahalf, const uint4 (&ra)[4],
-                                          const uint4 (&rb)[Big<NM, NS>::kPieces], uint32_t akeep,
-                                          int ntv) {
+                                          const uint2& rs, const uint4 (&rb)[Big<NM, NS>::kPieces],
+                                          uint32_t akeep, int ntv) {
   using C = Big<NM, NS>;
   uint4* a = reinterpret_cast<uint4*>(buf + (arow * kALd + ahalf * 32) / 2);
 #pragma unroll
   for (int j = 0; j < 4; ++j) a[j] = masked(ra[j], akeep);
+  // the row's sum parts as the first three elements of an 8-element A operand
+  if (ahalf == 0)
+    reinterpret_cast<uint4*>(buf + C::kAWords + C::kBWords)[arow] =
+        make_uint4(rs.x & akeep, rs.y & akeep, 0u, 0u);
 #pragma unroll
   for (int i = 0; i < C::kPieces; ++i) {
     int mat, tt, h, row;
@@ -598,10 +651,16 @@ __device__ __forceinline__ void big_store(uint32_t* buf, int arow, int ahalf, co
   }
 }
 
+// B operand of the correction: -136 at k = 0, 1, 2 (the three sum parts),
+// zero elsewhere.
+__device__ __forceinline__ bf16x8_t minus136_x3() {
+  return as_bf16x8(make_uint4(0xC308C308u, 0x0000C308u, 0u, 0u));
+}
+
 template <int NM, int NS>
-__device__ __forceinline__ void big_math(const uint32_t* buf, const uint16_t* sc, int groups,
-                                         int grp, int wm, int wn, int col, int half,
-                                         f32x16_t (&acc)[2][NM][NS]) {
+__device__ __forceinline__ void big_math(const uint32_t* buf, const uint32_t* zero16,
+                                         const uint16_t* sc, int groups, int grp, int wm, int wn,
+                                         int col, int half, f32x16_t (&acc)[2][NM][NS]) {
   using C = Big<NM, NS>;
   uint4 a[2][4];
   f32x16_t corr[2];
@@ -611,13 +670,12 @@ __device__ __forceinline__ void big_math(const uint32_t* buf, const uint16_t* sc
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       a[i][j] = *reinterpret_cast<const uint4*>(buf + (r * kALd + half * 32 + j * 8) / 2);
-    // -136 * (row sums of the group), the same for every column: once per
-    // row block, shared by every matrix and column tile
-    corr[i] = f32x16_t{};
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][j]), minus136(), corr[i],
-                                                        0, 0, 0);
+    // -136 * (row sums of the group), the same for every column: one MFMA
+    // per row block from the staged sum parts (the lanes of the upper K half
+    // read zeros), shared by every matrix and column tile
+    const uint32_t* sp = half ? zero16 : buf + C::kAWords + C::kBWords + r * 4;
+    corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        as_bf16x8(*reinterpret_cast<const uint4*>(sp)), minus136_x3(), f32x16_t{}, 0, 0, 0);
   }
   const uint4* bq = reinterpret_cast<const uint4*>(buf + C::kAWords);
 #pragma unroll
@@ -681,24 +739,31 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   const int m = m0 + arow;
   const uint32_t akeep = m < sl.M ? 0xFFFFFFFFu : 0u;
   const uint16_t* rowp;
+  const uint2* sump;
   {
     const int mr = m < sl.M ? m : m0;  // rows past the slot read the first row (masked)
     if (DOWN) {
-      rowp = g.h + static_cast<size_t>(row_of(g, sl, mr)) * g.f;
+      const size_t hr = row_of(g, sl, mr);
+      rowp = g.h + hr * g.f;
+      sump = g.sum_h + hr * groups;
     } else {
       const int tok = sl.shared ? mr : g.perm[sl.p0 + mr] / g.top_k;
       rowp = g.x + static_cast<size_t>(tok) * g.d;
+      sump = g.sum_x + static_cast<size_t>(tok) * groups;
     }
   }
+  uint32_t* zero16 = lds + 2 * C::kBufWords + NM * C::kWgCols * groups / 2;
+  if (t < 4) zero16[t] = 0u;  // visible after the first barrier
   const int wv = t >> 6, lane = t & 63;
   const int wm = wv & 1, wn = wv >> 1, col = lane & 31, half = lane >> 5;
 
   // Two register sets: group g+1 is stored to LDS while g+2 is in flight,
   // so every group's loads have two groups of math to land.
   uint4 ra[2][4], rb[2][C::kPieces];
-  big_load<NM, NS>(rowp, ahalf, 0, groups, K, ntv, qbase, ra[0], rb[0]);
-  big_load<NM, NS>(rowp, ahalf, 1, groups, K, ntv, qbase, ra[1], rb[1]);
-  big_store<NM, NS>(buf0, arow, ahalf, ra[0], rb[0], akeep, ntv);
+  uint2 rs[2];
+  big_load<NM, NS>(rowp, sump, ahalf, 0, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
+  big_load<NM, NS>(rowp, sump, ahalf, 1, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
+  big_store<NM, NS>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
   __syncthreads();
   f32x16_t acc[2][NM][NS];
 #pragma unroll
@@ -711,14 +776,14 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
         for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = 0.0f;
   for (int g0 = 0; g0 < groups; g0 += 2) {
     // group g0 is in buf0, group g0 + 1 in register set 1
-    big_load<NM, NS>(rowp, ahalf, g0 + 2, groups, K, ntv, qbase, ra[0], rb[0]);
-    big_math<NM, NS>(buf0, sc, groups, g0, wm, wn, col, half, acc);
-    big_store<NM, NS>(buf1, arow, ahalf, ra[1], rb[1], akeep, ntv);
+    big_load<NM, NS>(rowp, sump, ahalf, g0 + 2, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
+    big_math<NM, NS>(buf0, zero16, sc, groups, g0, wm, wn, col, half, acc);
+    big_store<NM, NS>(buf1, arow, ahalf, ra[1], rs[1], rb[1], akeep, ntv);
     __syncthreads();
     if (g0 + 1 < groups) {
-      big_load<NM, NS>(rowp, ahalf, g0 + 3, groups, K, ntv, qbase, ra[1], rb[1]);
-      big_math<NM, NS>(buf1, sc, groups, g0 + 1, wm, wn, col, half, acc);
-      big_store<NM, NS>(buf0, arow, ahalf, ra[0], rb[0], akeep, ntv);
+      big_load<NM, NS>(rowp, sump, ahalf, g0 + 3, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
+      big_math<NM, NS>(buf1, zero16, sc, groups, g0 + 1, wm, wn, col, half, acc);
+      big_store<NM, NS>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
       __syncthreads();
     }
   }
@@ -758,12 +823,12 @@ int max_small(int T, int k, int slots, bool has_shared) {
 int max_big(int T, int k, bool has_shared) { return rows_of(T, k, has_shared) / kBigMinRows + 1; }
 
 struct PrefillLayout {
-  size_t h, tiles, big_tiles, counts, total;
+  size_t h, tiles, big_tiles, counts, sum_x, sum_h, total;
 };
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-PrefillLayout prefill_layout(int T, int k, int E, int f, bool has_shared) {
+PrefillLayout prefill_layout(int T, int k, int E, int d, int f, bool has_shared) {
   PrefillLayout l{};
   const int slots = (has_shared ? 1 : 0) + std::min(E, T * k);
   const size_t rows = rows_of(T, k, has_shared);
@@ -775,6 +840,10 @@ PrefillLayout prefill_layout(int T, int k, int E, int f, bool has_shared) {
   off += align256(static_cast<size_t>(max_big(T, k, has_shared)) * sizeof(int2));
   l.counts = off;
   off += 256;
+  l.sum_x = off;
+  off += align256(static_cast<size_t>(T) * (d / 64) * sizeof(uint2));
+  l.sum_h = off;
+  off += align256(rows * (f / 64) * sizeof(uint2));
   l.total = off;
   return l;
 }
@@ -788,13 +857,13 @@ hipError_t allow_lds(K kernel, int bytes) {
 
 }  // namespace
 
-size_t ffn_prefill_workspace(int T, int k, int E, int f, bool has_shared) {
-  return prefill_layout(T, k, E, f, has_shared).total;
+size_t ffn_prefill_workspace(int T, int k, int E, int d, int f, bool has_shared) {
+  return prefill_layout(T, k, E, d, f, has_shared).total;
 }
 
 hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream) {
   const size_t dd = p.d, ff = p.f;
-  const PrefillLayout l = prefill_layout(p.T, p.k, p.E, p.f, p.has_shared);
+  const PrefillLayout l = prefill_layout(p.T, p.k, p.E, p.d, p.f, p.has_shared);
   PrefillArgs g{};
   g.experts = p.experts;
   g.shared = p.shared;
@@ -821,6 +890,8 @@ hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream) {
   g.big_tiles = reinterpret_cast<int2*>(ws + l.big_tiles);
   g.n_tiles = reinterpret_cast<int*>(ws + l.counts);
   g.n_big = g.n_tiles + 1;
+  g.sum_x = reinterpret_cast<uint2*>(ws + l.sum_x);
+  g.sum_h = reinterpret_cast<uint2*>(ws + l.sum_h);
   g.y = static_cast<uint16_t*>(p.y);
   g.y_shared = static_cast<uint16_t*>(p.y_shared);
   const int ms = max_small(p.T, p.k, g.slots, p.has_shared);
@@ -843,10 +914,17 @@ hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream) {
   const int cgu = (p.f + GU::kWgCols - 1) / GU::kWgCols, cdn = (p.d + DN::kWgCols - 1) / DN::kWgCols;
   const int sgu = (p.f + 64 * kSmallNSubGU - 1) / (64 * kSmallNSubGU);
   const int sdn = (p.d + 64 * kSmallNSubDN - 1) / (64 * kSmallNSubDN);
+  auto rowsums = [&](const uint16_t* src, int rows, int K, uint2* dst) {
+    const long long n = static_cast<long long>(rows) * (K / 64);
+    return launch(prefill_rowsums, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                  stream, src, rows, K, dst);
+  };
+  if ((err = rowsums(g.x, p.T, p.d, g.sum_x)) != hipSuccess) return err;
   err = launch(prefill_big<2, 1, false>, grid(mb, cgu), dim3(256), lds_gu, stream, g);
   if (err != hipSuccess) return err;
   err = launch(prefill_small<2, kSmallNSubGU, false>, grid(ms, sgu), dim3(256), 0, stream, g);
   if (err != hipSuccess) return err;
+  if ((err = rowsums(g.h, rows_of(p.T, p.k, p.has_shared), p.f, g.sum_h)) != hipSuccess) return err;
   err = launch(prefill_big<1, 2, true>, grid(mb, cdn), dim3(256), lds_dn, stream, g);
   if (err != hipSuccess) return err;
   return launch(prefill_small<1, kSmallNSubDN, true>, grid(ms, sdn), dim3(256), 0, stream, g);

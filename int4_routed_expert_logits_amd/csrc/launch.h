@@ -103,7 +103,7 @@ hipError_t launch_ffn_decode_grouping(const FfnProblem& p, const RouteGroup& rg,
                                       hipStream_t stream);
 
 // ffn_prefill.hip: grouped GEMM on bf16 MFMA, bf16 intermediate and outputs.
-size_t ffn_prefill_workspace(int T, int k, int E, int f, bool has_shared);
+size_t ffn_prefill_workspace(int T, int k, int E, int d, int f, bool has_shared);
 hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream);
 
 // pack.hip: canonical -> packed expert blocks.
