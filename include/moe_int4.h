@@ -25,7 +25,7 @@
  *                   resident experts compute
  *   moe_quantize    float weights -> int4 codes + float16 scales (the
  *                   one-time conversion of a checkpoint)
- *   moe_pack_experts one-time byte permutation of the expert blocks into the
+ *   moe_pack_experts one-time byte bijection of the expert blocks into the
  *                   tiled layout the FFN kernels stream
  *
  * Conventions common to every call:
@@ -120,15 +120,17 @@ typedef struct {
 size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group);
 
 /* Convert expert blocks from the layout above to the packed layout that
- * moe_expert_ffn reads: a byte permutation of each block, same size, done
+ * moe_expert_ffn reads: a bijection of each block's bytes (a permutation of
+ * the nibbles and scales, and every code stored as q + 8), same size, done
  * once when the experts are loaded (as the pages' engine converts its
  * checkpoint once before serving: ssnai.com digest, first-command section).
  * For each matrix W [N][K] of the block (N, K multiples of 64) the codes are
  * regrouped into tiles of 64 rows: row t*64+l, columns 32c..32c+31 go to
  *     q_off + t*(64*K/2) + c*1024 + l*16
  * and inside each 4-byte word (columns 8w..8w+7) the nibble of column 8w+j
- * moves to bit 4*(j/2) + 16*(j%2), where q_off is the sub-array offset of
- * the canonical block.  Scales follow the same tiles, group-major inside a
+ * moves to bit 4*(j/2) + 16*(j%2), stored in offset binary (the
+ * two's-complement code q with its top bit flipped: q + 8 in [0, 15]), where
+ * q_off is the sub-array offset of the canonical block.  Scales follow the same tiles, group-major inside a
  * tile: the scale of row t*64+l, group g goes to
  *     s_off + (t*(K/64)*64 + g*64 + l)*2
  * where s_off is the scale sub-array offset of the canonical block.
