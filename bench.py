@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--cache-slots", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured HBM copy/read and bf16 GEMM rates")
     ap.add_argument("--counters", action="store_true",
                     help="only run what the HBM-traffic counter passes measure: a 1 GiB device "
                          "copy (calibration) and 20 decode expert-FFN launches")
@@ -249,9 +251,18 @@ def main():
         },
     }
 
+    # ------------------------------------------------------- measured peaks
+    if not args.no_peaks:
+        peaks = measured_peaks(torch, dev)
+        result["measured_peaks"] = peaks
+        result["roofline"]["frac_of_measured_copy"] = round(kern_gbps / peaks["torch_copy_gbps"], 4)
+
     # --------------------------------------------------------------- prefill
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts[0], shared[0], w_router, dev)
+        if "measured_peaks" in result and "roofline" in result["prefill"]:
+            pr = result["prefill"]["roofline"]
+            pr["frac_of_measured_gemm"] = round(pr["achieved"] / result["measured_peaks"]["torch_matmul_bf16_tflops"], 4)
 
     # ------------------------------------------------------------ quantiser
     if not args.no_quantizer:
@@ -268,6 +279,48 @@ def main():
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def measured_peaks(torch, dev, reps=10):
+    """What plain library work reaches on this GPU, beside the published
+    peaks: a 1 GiB device copy (read + write bytes counted), a float32 sum
+    over 1 GiB (read only), and an 8192^3 bf16 matrix product through
+    torch.matmul (the vendor BLAS)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    af = a.view(torch.float32)
+
+    def rate(fn, work):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return work / (e0.elapsed_time(e1) * 1e-3 / reps)
+
+    copy = rate(lambda: b.copy_(a), 2.0 * n) / 1e9
+    read = rate(lambda: af.sum(), float(n)) / 1e9
+    del a, b, af
+    m = 8192
+    x = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    w = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    gemm = rate(lambda: torch.matmul(x, w), 2.0 * m * m * m) / 1e12
+    del x, w
+    log(f"measured: device copy {copy:.0f} GB/s, 1 GiB read {read:.0f} GB/s, "
+        f"bf16 GEMM {gemm:.0f} TFLOP/s")
+    return {
+        "torch_copy_gbps": round(copy, 1),
+        "torch_sum_read_gbps": round(read, 1),
+        "torch_matmul_bf16_tflops": round(gemm, 1),
+        "how": "torch copy_ of 1 GiB (read + write bytes counted), torch sum over 1 GiB of "
+               "float32 (a library reduction, below what a plain streaming read reaches), "
+               "torch.matmul 8192x8192x8192 bf16 (vendor BLAS); 10 timed repetitions each",
+    }
 
 
 def bench_quantizer(torch, moe, dev, reps=20):
