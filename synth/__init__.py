@@ -63,7 +63,8 @@ class LayerShape:
 
 # The five workloads: tiny parity layer, small-expert decode layer,
 # many-small-experts layer with a shared expert and skewed routing, the
-# ~19 MB-expert layer for decode, and the same layer for 2048-token prefill.
+# ~19 MB-expert layer for decode, and the same layer for 2048-token prefill;
+# plus one more parity-test layer (6).
 WORKLOADS = {
     1: dict(shape=LayerShape(512, 256, 8, 2, 0, False, "f32"), tokens=(4,)),
     2: dict(shape=LayerShape(2048, 1024, 64, 8, 0, False, "bf16"), tokens=(1, 16)),
@@ -71,6 +72,12 @@ WORKLOADS = {
     4: dict(shape=LayerShape(6144, 2048, 256, 8, 2048, False, "bf16"), tokens=(1, 8)),
     5: dict(shape=LayerShape(6144, 2048, 256, 8, 2048, True, "bf16"), tokens=(2048,),
             layer_of=4),
+    # A parity-test layer (no workload of the pages): small enough for the
+    # float64 oracle at hundreds of tokens, with an odd number of 64-column
+    # groups along d (5) and along f (3), and, at 512 tokens with its Zipf
+    # bias, experts of well over 96 rows, so the 128-row prefill tiles are
+    # checked against the full oracle.
+    6: dict(shape=LayerShape(320, 192, 8, 2, 192, True, "bf16"), tokens=(512,)),
 }
 # Workload 5 runs on workload 4's layer (same router weights and expert
 # blocks); only its Zipf router bias and its token batches are its own.

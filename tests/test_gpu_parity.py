@@ -394,7 +394,7 @@ def check_routing_and_union(buf, ref_idx, ref_w, union):
     assert np.array_equal(buf.n_active.cpu().numpy(), n_active)
 
 
-FULL_CASES = [(1, 4), (1, 3), (2, 1), (2, 16), (2, 5), (3, 64), (3, 13), (4, 1)]
+FULL_CASES = [(1, 4), (1, 3), (2, 1), (2, 16), (2, 5), (3, 64), (3, 13), (4, 1), (6, 8), (6, 37)]
 
 
 # the separate calls, and (batches of at most 8 tokens) the one-call moe_layer_decode
@@ -621,7 +621,9 @@ def prefill_err(got, ref):
     got = np.asarray(got, dtype=np.float64)
     rms = float(np.sqrt(np.mean(ref ** 2)))
     return float(np.max(np.abs(got - ref) / (TOL_PREFILL * rms + 2.0 ** -8 * np.abs(ref))))
-PREFILL_FULL = [(2, 16), (2, 5), (3, 64), (3, 13)]
+# (6, 512) and (6, 97): 128-row tiles (full and partial), odd group counts
+# along d and f, partial column tiles, an unrouted expert
+PREFILL_FULL = [(2, 16), (2, 5), (3, 64), (3, 13), (6, 512), (6, 97)]
 
 
 @pytest.mark.parametrize("cfg,T", PREFILL_FULL)

@@ -392,7 +392,7 @@ def _torch_dense_masked(x, w_router, bias, blocks, shared, d, f, E, k, idx, wts)
     return out.numpy()
 
 
-@pytest.mark.parametrize("cfg,T", [(1, 4), (2, 1)])
+@pytest.mark.parametrize("cfg,T", [(1, 4), (2, 1), (6, 16)])
 def test_sparse_layer_equals_dense_masked_gates(cfg, T):
     layer = synth.make_layer(cfg)
     _, x = synth.make_tokens(cfg, T)
