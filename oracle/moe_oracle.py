@@ -285,11 +285,14 @@ def swiglu(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray) -> np.
 
 
 def expert_ffn(x, experts, shared, offsets, perm, active, n_active, top_k, d, f,
-               group: int = GROUP):
+               group: int = GROUP, weights=None):
     """O6-O7: for every expert with routed slots, gather its tokens
     (token of slot s = s // k) and run the SwiGLU expert on them; results go to
     ``y`` in grouped (permuted) order.  The shared expert runs on every token
-    in token order.  Returns (y [T*k, d], y_shared [T, d] or None), float64."""
+    in token order.  Returns (y [T*k, d], y_shared [T, d] or None), float64.
+    ``weights(block, d, f)`` decodes a block (default: the int4 gs64 block)."""
+    if weights is None:
+        weights = lambda blk, d_, f_: expert_weights(blk, d_, f_, group)  # noqa: E731
     x = np.asarray(x, dtype=np.float64)
     T = x.shape[0]
     y = np.zeros((T * top_k, d), dtype=np.float64)
@@ -297,11 +300,11 @@ def expert_ffn(x, experts, shared, offsets, perm, active, n_active, top_k, d, f,
         e = int(active[a])
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         tokens = np.asarray(perm[lo:hi], dtype=np.int64) // top_k
-        Wg, Wu, Wd = expert_weights(experts[e], d, f, group)
+        Wg, Wu, Wd = weights(experts[e], d, f)
         y[lo:hi] = swiglu(x[tokens], Wg, Wu, Wd)
     y_shared = None
     if shared is not None:
-        Wg, Wu, Wd = expert_weights(shared, d, f, group)
+        Wg, Wu, Wd = weights(shared, d, f)
         y_shared = swiglu(x, Wg, Wu, Wd)
     return y, y_shared
 
@@ -321,11 +324,15 @@ def combine(y, y_shared, inv_perm, topk_w, top_k):
     return out
 
 
-def moe_layer(x, w_router, bias, experts, shared, d, f, n_experts, top_k, group: int = GROUP):
-    """The whole layer, O1-O8.  Returns a dict of every intermediate."""
+def moe_layer(x, w_router, bias, experts, shared, d, f, n_experts, top_k, group: int = GROUP,
+              weights=None):
+    """The whole layer, O1-O8.  Returns a dict of every intermediate.
+    ``weights``: the block decoder (default int4 gs64; oracle.mxfp4's
+    expert_weights for MXFP4 blocks)."""
     idx, w, lg = route(x, w_router, bias, top_k)
     counts, offsets, perm, inv_perm, active, n_active = batch_union(idx, n_experts)
-    y, ys = expert_ffn(x, experts, shared, offsets, perm, active, n_active, top_k, d, f, group)
+    y, ys = expert_ffn(x, experts, shared, offsets, perm, active, n_active, top_k, d, f, group,
+                       weights)
     out = combine(y, ys, inv_perm, w, top_k)
     return dict(logits=lg, topk_idx=idx, topk_w=w, counts=counts, offsets=offsets, perm=perm,
                 inv_perm=inv_perm, active=active, n_active=n_active, y=y, y_shared=ys, out=out)
