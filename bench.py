@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--cache-slots", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--no-batch8", action="store_true",
+                    help="skip the 8-token decode leg (run with the 1-token headline)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured HBM copy/read and bf16 GEMM rates")
     ap.add_argument("--counters", action="store_true",
@@ -251,6 +253,12 @@ def main():
         },
     }
 
+    # ------------------------------------------ decode batch of 8 tokens (one call)
+    if T == 1 and not args.no_batch8:
+        result["decode_8_tokens"] = bench_decode_batch(args, torch, moe, synth, LayerBuffers,
+                                                       run_layer_decode, sh, experts, shared,
+                                                       w_router, bb, 8)
+
     # ------------------------------------------------------- measured peaks
     if not args.no_peaks:
         peaks = measured_peaks(torch, dev)
@@ -279,6 +287,64 @@ def main():
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_decode_batch(args, torch, moe, synth, LayerBuffers, run_layer_decode, sh, experts,
+                       shared, w_router, bb, T):
+    """Decode steps of T tokens (the 19 MB-expert layer's second decode batch
+    size) through moe_layer_decode, captured in a HIP graph over the rotating
+    layer copies; expert bytes = (distinct routed experts + shared) x block."""
+    dev = w_router.device
+    nb = len(experts)
+    xs, bufs = [], []
+    for b in range(nb):
+        bits, _ = synth.make_tokens(4, T, batch=100 + b)
+        xs.append(torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16))
+        bufs.append(LayerBuffers.allocate(sh, T, moe.MOE_PATH_DECODE_F32))
+
+    def step(i):
+        j = i % nb
+        run_layer_decode(xs[j], w_router, None, experts[j], shared[j], bufs[j])
+
+    for i in range(nb):
+        step(i)
+    torch.cuda.synchronize()
+    blocks = [int(b.n_active.item()) + 1 for b in bufs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(nb):
+            step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(nb):
+            step(i)
+    reps = max(1, args.steps // nb)
+    for _ in range(max(1, args.warmup // nb)):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / (reps * nb)
+    del graph
+    step_bytes = float(np.mean(blocks)) * bb
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    log(f"decode step, {T} tokens, moe_layer_decode: {ms * 1e3:.1f} us, {gbps:.0f} GB/s "
+        f"({np.mean(blocks):.1f} expert blocks per step), {T / (ms * 1e-3):.0f} tokens/s")
+    return {
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "us_per_step": round(ms * 1e3, 2),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "expert_blocks_per_step": round(float(np.mean(blocks)), 2),
+        "hbm_pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "workload": f"decode, {T} tokens per step, same layer, no router bias, hip graph over "
+                    f"{nb} layer copies",
+    }
 
 
 def measured_peaks(torch, dev, reps=10):
