@@ -21,12 +21,19 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t round_up(size_t n) { return (n + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign; }
 
-moe_status check_shape(const moe_shape* s) {
+// group 64: int4 codes with a float16 scale per 64 elements; group 32:
+// MXFP4 (E2M1 codes with an E8M0 scale per 32 elements), which only the
+// calls that pass mxfp4_ok take (the rest of the library is int4 only).
+constexpr int kGroupInt4 = 64;
+constexpr int kGroupMxfp4 = 32;
+
+moe_status check_shape(const moe_shape* s, bool mxfp4_ok = false) {
   if (!s) return MOE_ERR_NULL;
   if (s->d <= 0 || s->f <= 0 || s->n_experts <= 0 || s->top_k <= 0 || s->group <= 0 ||
       s->f_shared < 0)
     return MOE_ERR_SHAPE;
-  if (s->group != 64) return MOE_ERR_UNSUPPORTED;
+  if (s->group != kGroupInt4 && !(mxfp4_ok && s->group == kGroupMxfp4))
+    return MOE_ERR_UNSUPPORTED;
   if (s->d % 64 != 0 || s->f % 64 != 0) return MOE_ERR_SHAPE;
   if (s->d > kMaxDim || s->f > kMaxDim) return MOE_ERR_UNSUPPORTED;
   if (s->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
@@ -53,14 +60,17 @@ moe_status hip_status(hipError_t e) {
 extern "C" {
 
 size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group) {
-  if (group != 64 || d <= 0 || f <= 0 || d % 64 || f % 64) return 0;
+  if ((group != kGroupInt4 && group != kGroupMxfp4) || d <= 0 || f <= 0 || d % 64 || f % 64)
+    return 0;
   const size_t n = 3ull * static_cast<size_t>(d) * static_cast<size_t>(f);
-  return n / 2 + n / group * 2;
+  // int4: half a byte per code + a float16 per 64; MXFP4: half a byte per
+  // code + one byte per 32 (the same total)
+  return group == kGroupInt4 ? n / 2 + n / group * 2 : n / 2 + n / group;
 }
 
 moe_status moe_pack_experts(const moe_shape* shape, int64_t n_blocks, const uint8_t* src,
                             uint8_t* dst, void* stream) {
-  moe_status st = check_shape(shape);
+  moe_status st = check_shape(shape, true);
   if (st != MOE_OK) return st;
   if (n_blocks < 0) return MOE_ERR_SHAPE;
   if (n_blocks == 0) return MOE_OK;
@@ -70,8 +80,10 @@ moe_status moe_pack_experts(const moe_shape* shape, int64_t n_blocks, const uint
   const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
   const uintptr_t len = static_cast<uintptr_t>(bb) * static_cast<uintptr_t>(n_blocks);
   if (s0 < d0 + len && d0 < s0 + len) return MOE_ERR_SHAPE;  // overlapping buffers
-  return hip_status(moe::launch_pack(shape->d, shape->f, n_blocks, bb, src, dst,
-                                     static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(shape->group == kGroupMxfp4
+                        ? moe::launch_pack_mxfp4(shape->d, shape->f, n_blocks, bb, src, dst, s)
+                        : moe::launch_pack(shape->d, shape->f, n_blocks, bb, src, dst, s));
 }
 
 moe_status moe_quantize(int32_t N, int32_t K, const void* w, moe_dtype w_dt, moe_quant_mode mode,
@@ -88,14 +100,14 @@ moe_status moe_quantize(int32_t N, int32_t K, const void* w, moe_dtype w_dt, moe
 }
 
 size_t moe_route_workspace_bytes(const moe_shape* shape, int32_t T) {
-  if (check_shape(shape) != MOE_OK || T < 0) return 0;
+  if (check_shape(shape, true) != MOE_OK || T < 0) return 0;
   return round_up(moe::route_workspace(T, shape->d, shape->n_experts));
 }
 
 moe_status moe_route(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
                      const float* w_router, const float* bias, int32_t* topk_idx,
                      float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
-  moe_status st = check_shape(shape);
+  moe_status st = check_shape(shape, true);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(shape, T)) != MOE_OK) return st;
   if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
@@ -114,7 +126,7 @@ moe_status moe_route(const moe_shape* shape, int32_t T, const void* x, moe_dtype
 moe_status moe_union(const moe_shape* shape, int32_t T, const int32_t* topk_idx,
                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                      int32_t* active, int32_t* n_active, void* stream) {
-  moe_status st = check_shape(shape);
+  moe_status st = check_shape(shape, true);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(shape, T)) != MOE_OK) return st;
   if (!counts || !offsets || !active || !n_active) return MOE_ERR_NULL;
@@ -133,7 +145,7 @@ moe_status moe_route_union(const moe_shape* shape, int32_t T, const void* x, moe
                            float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv_perm, int32_t* active, int32_t* n_active,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  moe_status st = check_shape(shape);
+  moe_status st = check_shape(shape, true);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(shape, T)) != MOE_OK) return st;
   if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
@@ -159,8 +171,9 @@ moe_status moe_route_union(const moe_shape* shape, int32_t T, const void* x, moe
 }
 
 size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path) {
-  if (check_shape(shape) != MOE_OK || T < 0) return 0;
+  if (check_shape(shape, true) != MOE_OK || T < 0) return 0;
   const bool sh = shape->f_shared != 0;
+  if (shape->group == kGroupMxfp4 && path != MOE_PATH_DECODE_F32) return 0;
   if (path == MOE_PATH_DECODE_F32)
     return round_up(moe::ffn_decode_workspace(T, shape->top_k, shape->n_experts, shape->d,
                                               shape->f, sh));
@@ -174,10 +187,12 @@ moe_status moe_expert_ffn(const moe_shape* shape, int32_t T, const void* x, moe_
                           const int32_t* offsets, const int32_t* perm, const int32_t* active,
                           const int32_t* n_active, moe_path path, void* y, void* y_shared,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  moe_status st = check_shape(shape);
+  moe_status st = check_shape(shape, true);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(shape, T)) != MOE_OK) return st;
   if (path != MOE_PATH_DECODE_F32 && path != MOE_PATH_PREFILL_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool mxfp4 = shape->group == kGroupMxfp4;
+  if (mxfp4 && path != MOE_PATH_DECODE_F32) return MOE_ERR_UNSUPPORTED;  // no MXFP4 prefill
   if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
   if (path == MOE_PATH_PREFILL_BF16 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
   const bool has_shared = shape->f_shared != 0;
@@ -201,6 +216,7 @@ moe_status moe_expert_ffn(const moe_shape* shape, int32_t T, const void* x, moe_
   p.has_shared = has_shared;
   p.x_bf16 = x_dt == MOE_BF16;
   p.block_bytes = moe_expert_bytes(shape->d, shape->f, shape->group);
+  p.mxfp4 = mxfp4;
   p.x = x;
   p.experts = experts;
   p.shared = shared;
@@ -219,7 +235,7 @@ moe_status moe_expert_ffn(const moe_shape* shape, int32_t T, const void* x, moe_
 moe_status moe_combine(const moe_shape* shape, int32_t T, const void* y, const void* y_shared,
                        moe_dtype y_dt, const int32_t* inv_perm, const float* topk_w, void* out,
                        moe_dtype out_dt, void* stream) {
-  moe_status st = check_shape(shape);
+  moe_status st = check_shape(shape, true);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(shape, T)) != MOE_OK) return st;
   if ((y_dt != MOE_F32 && y_dt != MOE_BF16) || (out_dt != MOE_F32 && out_dt != MOE_BF16))

@@ -198,10 +198,25 @@ __device__ __forceinline__ void load_step(const TileRes<NM>& res, int c, int cb,
 // sc[mat]: the fp16 group scales of this lane's row, group j at
 // sc[mat][j * kSst] (the lane's range starts at chunk cb).  XW = 16 (bf16
 // pairs) or 32 (16 hi pairs, then 16 lo pairs).
-template <int NM, int MT, int XW, int kSst>
+// MXFP4 (MX): byte i of a code word is two E2M1 elements, columns 2i and
+// 2i + 1 of the word's eight; the hardware conversion gives them as a bf16
+// pair exactly.
+template <int I>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, I));
+}
+
+// E8M0 scale byte -> 2^(E - 127) as float32 (E = 0 is the subnormal 2^-127;
+// E = 255 is NaN, as the MX format defines it).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e == 0 ? __uint_as_float(0x00400000u)
+                : (e == 255 ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23));
+}
+
+template <int NM, int MT, int XW, int kSst, bool MX>
 __device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int cb, int nt,
                                           const uint32_t* xl, int tok_words, const float* xs,
-                                          int sum_words, const _Float16* const (&sc)[NM],
+                                          int sum_words, const void* const (&sc)[NM],
                                           float (&acc)[NM][MT]) {
 #pragma unroll
   for (int i = 0; i < kStep; ++i) {
@@ -224,10 +239,18 @@ __device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int
 #pragma unroll
       for (int mat = 0; mat < NM; ++mat) {
         const uint32_t u = w == 0 ? d.q[mat][i].x : w == 1 ? d.q[mat][i].y : w == 2 ? d.q[mat][i].z : d.q[mat][i].w;
-        const uint32_t b0 = and_or(u, kMask, mg);
-        const uint32_t b1 = and_or((u >> 4), kMask, mg);
-        const uint32_t b2 = and_or((u >> 8), kMask, mg);
-        const uint32_t b3 = and_or((u >> 12), kMask, mg);
+        uint32_t b0, b1, b2, b3;
+        if constexpr (MX) {
+          b0 = fp4_pair<0>(u);
+          b1 = fp4_pair<1>(u);
+          b2 = fp4_pair<2>(u);
+          b3 = fp4_pair<3>(u);
+        } else {
+          b0 = and_or(u, kMask, mg);
+          b1 = and_or((u >> 4), kMask, mg);
+          b2 = and_or((u >> 8), kMask, mg);
+          b3 = and_or((u >> 12), kMask, mg);
+        }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m < nt) {
@@ -249,11 +272,19 @@ __device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int
     }
 #pragma unroll
     for (int mat = 0; mat < NM; ++mat) {
-      const float sv = static_cast<float>(sc[mat][((cb + c) >> 1) * kSst]);
+      if constexpr (MX) {
+        // one E8M0 scale per 32-column chunk; the elements are exact, no offset
+        const float sv = e8m0_to_f32(static_cast<const uint8_t*>(sc[mat])[(cb + c) * kSst]);
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < nt)
-          acc[mat][m] = fmaf(sv, fmaf(-kOffset, xs[m * sum_words + c], tc[mat][m]), acc[mat][m]);
+        for (int m = 0; m < MT; ++m)
+          if (m < nt) acc[mat][m] = fmaf(sv, tc[mat][m], acc[mat][m]);
+      } else {
+        const float sv = static_cast<float>(static_cast<const _Float16*>(sc[mat])[((cb + c) >> 1) * kSst]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < nt)
+            acc[mat][m] = fmaf(sv, fmaf(-kOffset, xs[m * sum_words + c], tc[mat][m]), acc[mat][m]);
+      }
     }
   }
 }
@@ -265,10 +296,10 @@ __device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int
 //
 // `a` and `b` hold the first two steps' loads, issued by the caller before
 // it staged the activations, so their latency overlaps the staging.
-template <int NM, int MT, int XW, int kSst>
+template <int NM, int MT, int XW, int kSst, bool MX>
 __device__ __forceinline__ void sweep(const TileRes<NM>& res, int cb, int ce, int nmax, int rt,
                                       int nt, const uint32_t* xl, int tok_words, const float* xs,
-                                      int sum_words, const _Float16* const (&sc)[NM], Step<NM>& a,
+                                      int sum_words, const void* const (&sc)[NM], Step<NM>& a,
                                       Step<NM>& b, float (&acc)[NM][MT]) {
 #pragma unroll
   for (int mat = 0; mat < NM; ++mat)
@@ -276,9 +307,9 @@ __device__ __forceinline__ void sweep(const TileRes<NM>& res, int cb, int ce, in
     for (int m = 0; m < MT; ++m) acc[mat][m] = 0.0f;
   const int nl = ce - cb;
   for (int c0 = 0; c0 < nmax; c0 += 2 * kStep) {
-    math_step<NM, MT, XW, kSst>(a, c0, nl, cb, nt, xl, tok_words, xs, sum_words, sc, acc);
+    math_step<NM, MT, XW, kSst, MX>(a, c0, nl, cb, nt, xl, tok_words, xs, sum_words, sc, acc);
     load_step<NM>(res, cb + c0 + 2 * kStep, cb, ce, rt, a);
-    math_step<NM, MT, XW, kSst>(b, c0 + kStep, nl, cb, nt, xl, tok_words, xs, sum_words, sc, acc);
+    math_step<NM, MT, XW, kSst, MX>(b, c0 + kStep, nl, cb, nt, xl, tok_words, xs, sum_words, sc, acc);
     load_step<NM>(res, cb + c0 + 3 * kStep, cb, ce, rt, b);
   }
 }
@@ -321,6 +352,20 @@ __device__ __forceinline__ void stage_scales(const uint8_t* tile, int o, int row
     const int j = i / per, pc = i - j * per;
     const uint4 v = *reinterpret_cast<const uint4*>(tile + (j * 64 + o) * 2 + pc * 16);
     *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(dst) + (j * (rows + kScalePad) + pc * 8) * 2) = v;
+  }
+}
+
+// MXFP4: the E8M0 bytes of `rows` consecutive rows from row o of a packed
+// 64-row tile (block b of the tile's rows at tile + b * 64), into LDS as
+// [blocks][rows + kScalePadMx] bytes.
+constexpr int kScalePadMx = 16;
+__device__ __forceinline__ void stage_scales_mx(const uint8_t* tile, int o, int rows, int blocks,
+                                                uint32_t* dst) {
+  const int per = rows / 16;  // 16-byte pieces per block (rows is a multiple of 16)
+  for (int i = threadIdx.x; i < blocks * per; i += blockDim.x) {
+    const int b = i / per, pc = i - b * per;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + b * 64 + o + pc * 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(dst) + b * (rows + kScalePadMx) + pc * 16) = v;
   }
 }
 
@@ -410,8 +455,14 @@ __device__ void stage_h(const FfnArgs& g, const Slot& sl, int m0, int nt, const 
 
 // Words of a gate/up workgroup's LDS before the grouping prologue's region
 // (a multiple of 4, so the region is 16-byte aligned).
-__host__ __device__ constexpr int gu_words(int d, int mt, bool xf32) {
-  return ((kGuWaves * kGuRows + kScalePad) * (d / 64) +
+__host__ __device__ constexpr int gu_scale_words(int d, bool mx) {
+  // two matrices: fp16 per (row, 64 columns), or one E8M0 byte per (row, 32 columns)
+  return mx ? (kGuWaves * kGuRows + kScalePadMx) * (d / 32) / 2
+            : (kGuWaves * kGuRows + kScalePad) * (d / 64);
+}
+
+__host__ __device__ constexpr int gu_words(int d, int mt, bool xf32, bool mx = false) {
+  return (gu_scale_words(d, mx) +
           mt * (kGuParts * (((d / 32 + kGuParts - 1) / kGuParts) * (xf32 ? 32 : 16) + kSkewWords) +
                 kGuParts * ((d / 32 + kGuParts - 1) / kGuParts)) +
           3) / 4 * 4;
@@ -459,8 +510,9 @@ __device__ __forceinline__ void group_batch(const FfnArgs& g, const RouteArgs& r
   }
 }
 
-template <int MT, bool XF32, int RMP>
+template <int MT, bool XF32, int RMP, bool MX>
 __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g, RouteArgs rt_args) {
+  static_assert(!(MX && RMP > 0), "the grouping prologue runs with int4 blocks only");
   extern __shared__ __align__(16) uint32_t lds[];
   constexpr int XW = XF32 ? 32 : 16;
   const int32_t* perm = g.perm;
@@ -491,9 +543,11 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g, Rou
   const StageLayout L = stage_layout(g.d / 32, kGuParts, XW);
   constexpr int kRowsWg = kGuWaves * kGuRows;
   const int groups = g.d / 64;
-  constexpr int kSst = kRowsWg + kScalePad;
-  uint32_t* scl = lds;                                    // [2][groups][kSst] fp16
-  uint32_t* xl = lds + kSst * groups;                     // staged x
+  // scale strides: fp16 elements per group row, or bytes per MXFP4 block row
+  constexpr int kSst = MX ? kRowsWg + kScalePadMx : kRowsWg + kScalePad;
+  const int blocks = g.d / 32;
+  uint32_t* scl = lds;                                    // [2][groups][kSst] fp16 or [2][blocks][kSst] u8
+  uint32_t* xl = lds + gu_scale_words(g.d, MX);           // staged x
   float* xs = reinterpret_cast<float*>(xl + MT * L.tok_words);
   const int cb = L.cb(p), ce = L.cb(p + 1);
 
@@ -502,12 +556,20 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g, Rou
   res.q[0] = make_rsrc(sl.blk + g.q_gate + tq, 32u * g.d);
   res.q[1] = make_rsrc(sl.blk + g.q_up + tq, 32u * g.d);
   const int rl = wv * kGuRows + r;  // row inside the workgroup
-  const _Float16* const sc[2] = {
-      reinterpret_cast<const _Float16*>(scl) + rl,
-      reinterpret_cast<const _Float16*>(scl) + kSst * groups + rl};
-  const size_t ts = static_cast<size_t>(tile) * 64 * groups * 2;  // the tile's scales
-  stage_scales(sl.blk + g.s_gate + ts, row0 % 64, kRowsWg, groups, scl);
-  stage_scales(sl.blk + g.s_up + ts, row0 % 64, kRowsWg, groups, scl + kSst * groups / 2);
+  const void* sc[2];
+  if constexpr (MX) {
+    sc[0] = reinterpret_cast<const uint8_t*>(scl) + rl;
+    sc[1] = reinterpret_cast<const uint8_t*>(scl) + kSst * blocks + rl;
+    const size_t ts = static_cast<size_t>(tile) * 64 * blocks;  // the tile's scale bytes
+    stage_scales_mx(sl.blk + g.s_gate + ts, row0 % 64, kRowsWg, blocks, scl);
+    stage_scales_mx(sl.blk + g.s_up + ts, row0 % 64, kRowsWg, blocks, scl + kSst * blocks / 4);
+  } else {
+    sc[0] = reinterpret_cast<const _Float16*>(scl) + rl;
+    sc[1] = reinterpret_cast<const _Float16*>(scl) + kSst * groups + rl;
+    const size_t ts = static_cast<size_t>(tile) * 64 * groups * 2;  // the tile's scales
+    stage_scales(sl.blk + g.s_gate + ts, row0 % 64, kRowsWg, groups, scl);
+    stage_scales(sl.blk + g.s_up + ts, row0 % 64, kRowsWg, groups, scl + kSst * groups / 2);
+  }
   const int fchunks = g.f / 32;
   const int frow = row0 + wv * kGuRows + r;
 
@@ -520,7 +582,7 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g, Rou
     stage_x<XF32>(g, sl, perm, m0, nt, L, xl, xs);
     __syncthreads();
     float acc[2][MT];
-    sweep<2, MT, XW, kSst>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
+    sweep<2, MT, XW, kSst, MX>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
                      xs + p * L.cpp_max, L.sum_words, sc, first, second, acc);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -551,7 +613,7 @@ __global__ __launch_bounds__(kGuWaves * kWave) void decode_gateup(FfnArgs g, Rou
 // 16 rows; lane = 16 * part + row
 // ---------------------------------------------------------------------------
 
-template <int MT>
+template <int MT, bool MX>
 __global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
   extern __shared__ __align__(16) uint32_t lds[];
   const Slot sl = resolve_slot(g, blockIdx.y, g.active, g.offsets);
@@ -564,18 +626,26 @@ __global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
   const StageLayout L = stage_layout(g.f / 32, kDnParts, 32);
   constexpr int kRowsWg = kDnWaves * kDnRows;
   const int groups = g.f / 64;
-  constexpr int kSst = kRowsWg + kScalePad;
-  uint32_t* scl = lds;                                    // [groups][kSst] fp16
-  uint32_t* xl = lds + kSst * groups / 2;                 // staged h
+  constexpr int kSst = MX ? kRowsWg + kScalePadMx : kRowsWg + kScalePad;
+  const int blocks = g.f / 32;
+  uint32_t* scl = lds;                                    // [groups][kSst] fp16 or [blocks][kSst] u8
+  uint32_t* xl = lds + (MX ? kSst * blocks / 4 : kSst * groups / 2);  // staged h
   float* xs = reinterpret_cast<float*>(xl + MT * L.tok_words);
   const int cb = L.cb(p), ce = L.cb(p + 1);
 
   TileRes<1> res;
   res.q[0] = make_rsrc(sl.blk + g.q_down + static_cast<size_t>(tile) * 64 * (g.f / 2), 32u * g.f);
   const int rl = wv * kDnRows + r;
-  const _Float16* const sc[1] = {reinterpret_cast<const _Float16*>(scl) + rl};
-  stage_scales(sl.blk + g.s_down + static_cast<size_t>(tile) * 64 * groups * 2, row0 % 64,
-               kRowsWg, groups, scl);
+  const void* sc[1];
+  if constexpr (MX) {
+    sc[0] = reinterpret_cast<const uint8_t*>(scl) + rl;
+    stage_scales_mx(sl.blk + g.s_down + static_cast<size_t>(tile) * 64 * blocks, row0 % 64,
+                    kRowsWg, blocks, scl);
+  } else {
+    sc[0] = reinterpret_cast<const _Float16*>(scl) + rl;
+    stage_scales(sl.blk + g.s_down + static_cast<size_t>(tile) * 64 * groups * 2, row0 % 64,
+                 kRowsWg, groups, scl);
+  }
   const int drow = row0 + wv * kDnRows + r;
 
   for (int m0 = 0; m0 < sl.M; m0 += MT) {
@@ -587,7 +657,7 @@ __global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
     stage_h(g, sl, m0, nt, L, xl, xs);
     __syncthreads();
     float acc[1][MT];
-    sweep<1, MT, 32, kSst>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
+    sweep<1, MT, 32, kSst, MX>(res, cb, ce, L.cpp_max, rt, nt, xl + p * L.part_words, L.tok_words,
                      xs + p * L.cpp_max, L.sum_words, sc, first, second, acc);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -604,15 +674,16 @@ __global__ __launch_bounds__(kDnWaves * kWave) void decode_down(FfnArgs g) {
   }
 }
 
-int gu_lds_bytes(int d, int mt, bool xf32) {
+int gu_lds_bytes(int d, int mt, bool xf32, bool mx = false) {
   const int chunks = d / 32, cpp = (chunks + kGuParts - 1) / kGuParts, xw = xf32 ? 32 : 16;
-  const int scales = (kGuWaves * kGuRows + kScalePad) * (d / 64);  // words: two matrices of fp16
+  const int scales = gu_scale_words(d, mx);  // words: two matrices
   return (scales + mt * (kGuParts * (cpp * xw + kSkewWords) + kGuParts * cpp)) * 4;
 }
 
-int dn_lds_bytes(int f, int mt) {
+int dn_lds_bytes(int f, int mt, bool mx = false) {
   const int chunks = f / 32, cpp = (chunks + kDnParts - 1) / kDnParts;
-  const int scales = (kDnWaves * kDnRows + kScalePad) * (f / 64) / 2;
+  const int scales = mx ? (kDnWaves * kDnRows + kScalePadMx) * (f / 32) / 4
+                        : (kDnWaves * kDnRows + kScalePad) * (f / 64) / 2;
   return (scales + mt * (kDnParts * (cpp * 32 + kSkewWords) + kDnParts * cpp)) * 4;
 }
 
@@ -625,26 +696,26 @@ int gu_route_lds_bytes(int d, int mt, bool xf32) {
 // RMP = 0: the grouping comes from global memory; 8 or 16: the gate/up
 // kernel groups the batch (RouteArgs) and writes the grouping for the down
 // kernel.
-template <int MT, bool XF32, int RMP>
+template <int MT, bool XF32, int RMP, bool MX>
 hipError_t launch_mt(const FfnArgs& g, const RouteArgs& r, int slots, hipStream_t s) {
   const dim3 g1(g.f / (kGuWaves * kGuRows), slots), g2(g.d / (kDnWaves * kDnRows), slots);
-  const int gu_lds = RMP > 0 ? gu_route_lds_bytes(g.d, MT, XF32) : gu_lds_bytes(g.d, MT, XF32);
-  hipError_t err = launch(decode_gateup<MT, XF32, RMP>, g1, dim3(kGuWaves * kWave), gu_lds, s, g, r);
+  const int gu_lds = RMP > 0 ? gu_route_lds_bytes(g.d, MT, XF32) : gu_lds_bytes(g.d, MT, XF32, MX);
+  hipError_t err = launch(decode_gateup<MT, XF32, RMP, MX>, g1, dim3(kGuWaves * kWave), gu_lds, s, g, r);
   if (err != hipSuccess) return err;
-  return launch(decode_down<MT>, g2, dim3(kDnWaves * kWave), dn_lds_bytes(g.f, MT), s, g);
+  return launch(decode_down<MT, MX>, g2, dim3(kDnWaves * kWave), dn_lds_bytes(g.f, MT, MX), s, g);
 }
 
-template <int RMP>
+template <int RMP, bool MX = false>
 hipError_t launch_any_mt(const FfnArgs& g, const RouteArgs& r, int slots, int mt, bool xf32,
                          hipStream_t s) {
   if (xf32) {
-    if (mt == 4) return launch_mt<4, true, RMP>(g, r, slots, s);
-    if (mt == 2) return launch_mt<2, true, RMP>(g, r, slots, s);
-    return launch_mt<1, true, RMP>(g, r, slots, s);
+    if (mt == 4) return launch_mt<4, true, RMP, MX>(g, r, slots, s);
+    if (mt == 2) return launch_mt<2, true, RMP, MX>(g, r, slots, s);
+    return launch_mt<1, true, RMP, MX>(g, r, slots, s);
   }
-  if (mt == 4) return launch_mt<4, false, RMP>(g, r, slots, s);
-  if (mt == 2) return launch_mt<2, false, RMP>(g, r, slots, s);
-  return launch_mt<1, false, RMP>(g, r, slots, s);
+  if (mt == 4) return launch_mt<4, false, RMP, MX>(g, r, slots, s);
+  if (mt == 2) return launch_mt<2, false, RMP, MX>(g, r, slots, s);
+  return launch_mt<1, false, RMP, MX>(g, r, slots, s);
 }
 
 FfnArgs ffn_args(const FfnProblem& p) {
@@ -666,8 +737,13 @@ FfnArgs ffn_args(const FfnProblem& p) {
   g.q_up = ff * dd / 2;
   g.q_down = ff * dd;
   g.s_gate = 3 * dd * ff / 2;
-  g.s_up = g.s_gate + ff * (dd / 64) * 2;
-  g.s_down = g.s_up + ff * (dd / 64) * 2;
+  if (p.mxfp4) {  // one E8M0 byte per 32 elements
+    g.s_up = g.s_gate + ff * (dd / 32);
+    g.s_down = g.s_up + ff * (dd / 32);
+  } else {        // one float16 per 64 elements
+    g.s_up = g.s_gate + ff * (dd / 64) * 2;
+    g.s_down = g.s_up + ff * (dd / 64) * 2;
+  }
   g.x = p.x;
   g.hp = static_cast<uint32_t*>(p.workspace);
   g.y = static_cast<float*>(p.y);
@@ -682,7 +758,8 @@ int pick_mt(const FfnProblem& p, int gu_extra) {
   const bool xf32 = !p.x_bf16;
   int mt = p.T >= 4 ? 4 : (p.T >= 2 ? 2 : 1);
   auto fits = [&](int m) {
-    return gu_words(p.d, m, xf32) * 4 + gu_extra <= kMaxLds && dn_lds_bytes(p.f, m) <= kMaxLds;
+    return gu_words(p.d, m, xf32, p.mxfp4) * 4 + gu_extra <= kMaxLds &&
+           dn_lds_bytes(p.f, m, p.mxfp4) <= kMaxLds;
   };
   while (mt > 1 && !fits(mt)) mt /= 2;
   return fits(mt) ? mt : 0;
@@ -700,7 +777,8 @@ hipError_t launch_ffn_decode(const FfnProblem& p, hipStream_t stream) {
   const int slots = g.has_shared + std::min(p.E, p.T * p.k);
   const int mt = pick_mt(p, 0);
   if (mt == 0) return hipErrorNotSupported;
-  return launch_any_mt<0>(g, RouteArgs{}, slots, mt, !p.x_bf16, stream);
+  return p.mxfp4 ? launch_any_mt<0, true>(g, RouteArgs{}, slots, mt, !p.x_bf16, stream)
+                 : launch_any_mt<0, false>(g, RouteArgs{}, slots, mt, !p.x_bf16, stream);
 }
 
 bool ffn_decode_groups_batch(const FfnProblem& p, int P) {

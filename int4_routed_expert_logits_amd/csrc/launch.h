@@ -67,6 +67,7 @@ struct FfnProblem {
   int T, d, f, E, k;
   bool has_shared;
   bool x_bf16;
+  bool mxfp4 = false;  // MXFP4 blocks (decode path only) instead of int4 gs64
   size_t block_bytes;
   const void* x;
   const uint8_t* experts;
@@ -106,9 +107,11 @@ hipError_t launch_ffn_decode_grouping(const FfnProblem& p, const RouteGroup& rg,
 size_t ffn_prefill_workspace(int T, int k, int E, int d, int f, bool has_shared);
 hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream);
 
-// pack.hip: canonical -> packed expert blocks.
+// pack.hip: canonical -> packed expert blocks (int4 gs64, or MXFP4).
 hipError_t launch_pack(int d, int f, long long n_blocks, size_t block_bytes, const uint8_t* src,
                        uint8_t* dst, hipStream_t stream);
+hipError_t launch_pack_mxfp4(int d, int f, long long n_blocks, size_t block_bytes,
+                             const uint8_t* src, uint8_t* dst, hipStream_t stream);
 
 // combine.hip
 hipError_t launch_combine(int T, int d, int k, const void* y, const void* y_shared, bool y_bf16,

@@ -113,7 +113,86 @@ __global__ __launch_bounds__(256) void pack_scales(PackArgs a) {
   }
 }
 
+// MXFP4 blocks (E2M1 nibbles, one E8M0 byte per 32 elements): the codes move
+// to the same 64-row tiles but keep their nibble order and values (the
+// hardware's FP4 -> bf16 conversion takes a byte as two neighbouring
+// elements); the scale bytes follow the tiles block-major: row t*64+l, block
+// b at s_off + t*(K/32)*64 + b*64 + l.
+__device__ __forceinline__ void geom_mx(const PackArgs& a, int m, MatGeom& g) {
+  const size_t dd = a.d, ff = a.f;
+  const size_t s0 = 3 * dd * ff / 2;
+  if (m == 0) {
+    g.N = a.f; g.K = a.d; g.q_off = 0; g.s_off = s0;
+  } else if (m == 1) {
+    g.N = a.f; g.K = a.d; g.q_off = ff * dd / 2; g.s_off = s0 + ff * (dd / 32);
+  } else {
+    g.N = a.d; g.K = a.f; g.q_off = ff * dd; g.s_off = s0 + 2 * ff * (dd / 32);
+  }
+  g.units = static_cast<long long>(g.N) * (g.K / 32);
+  g.sunits = static_cast<long long>(g.N) * (g.K / 32);
+}
+
+__global__ __launch_bounds__(256) void pack_codes_mx(PackArgs a) {
+  const long long total = a.units_per_block * a.n_blocks;
+  for (long long i = blockIdx.x * 256ll + threadIdx.x; i < total; i += 256ll * gridDim.x) {
+    const long long b = i / a.units_per_block;
+    long long u = i - b * a.units_per_block;
+    MatGeom g;
+    int m = 0;
+    for (; m < 3; ++m) {
+      geom_mx(a, m, g);
+      if (u < g.units) break;
+      u -= g.units;
+    }
+    const int cpr = g.K / 32;
+    const int r = static_cast<int>(u / cpr), c = static_cast<int>(u % cpr);
+    const uint4 v = *reinterpret_cast<const uint4*>(a.src + b * a.block_bytes + g.q_off +
+                                                    static_cast<size_t>(r) * (g.K / 2) + c * 16);
+    const size_t dst_off = g.q_off + static_cast<size_t>(r / 64) * (64 * static_cast<size_t>(g.K) / 2) +
+                           static_cast<size_t>(c) * 1024 + static_cast<size_t>(r % 64) * 16;
+    *reinterpret_cast<uint4*>(a.dst + b * a.block_bytes + dst_off) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_scales_mx(PackArgs a) {
+  const long long total = a.sunits_per_block * a.n_blocks;
+  for (long long i = blockIdx.x * 256ll + threadIdx.x; i < total; i += 256ll * gridDim.x) {
+    const long long b = i / a.sunits_per_block;
+    long long u = i - b * a.sunits_per_block;
+    MatGeom g;
+    int m = 0;
+    for (; m < 3; ++m) {
+      geom_mx(a, m, g);
+      if (u < g.sunits) break;
+      u -= g.sunits;
+    }
+    const uint8_t* s = a.src + b * a.block_bytes + g.s_off;
+    uint8_t* d = a.dst + b * a.block_bytes + g.s_off;
+    const int G = g.K / 32;
+    const long long r = u / G, blk = u - r * G;
+    d[(r / 64) * G * 64 + blk * 64 + r % 64] = s[u];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pack_mxfp4(int d, int f, long long n_blocks, size_t block_bytes,
+                             const uint8_t* src, uint8_t* dst, hipStream_t stream) {
+  PackArgs a{};
+  a.src = src;
+  a.dst = dst;
+  a.block_bytes = block_bytes;
+  a.d = d;
+  a.f = f;
+  a.units_per_block = 3ll * d * f / 32;
+  a.sunits_per_block = 3ll * d * f / 32;
+  a.n_blocks = n_blocks;
+  const long long total = a.units_per_block * n_blocks;
+  const unsigned grid = static_cast<unsigned>(std::min<long long>((total + 255) / 256, 1 << 16));
+  hipError_t e = launch(pack_codes_mx, dim3(grid), dim3(256), 0, stream, a);
+  if (e != hipSuccess) return e;
+  return launch(pack_scales_mx, dim3(grid), dim3(256), 0, stream, a);
+}
 
 hipError_t launch_pack(int d, int f, long long n_blocks, size_t block_bytes, const uint8_t* src,
                        uint8_t* dst, hipStream_t stream) {

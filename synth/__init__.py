@@ -148,9 +148,20 @@ def _draw_block(ss: np.random.SeedSequence, d: int, f: int, group: int, out: np.
     out[nq:nq + 2 * ns] = rng.uniform(0.005, 0.02, ns).astype(np.float16).view(np.uint8)
 
 
-def make_layer(cfg: int, experts: Optional[Sequence[int]] = None) -> Layer:
+def _draw_block_mxfp4(ss: np.random.SeedSequence, d: int, f: int, out: np.ndarray) -> None:
+    """An MXFP4 expert block: uniform random nibbles (every E2M1 code equally
+    likely) and E8M0 scale bytes uniform on [118, 124] (2^-9 .. 2^-3)."""
+    rng = np.random.Generator(np.random.PCG64(ss))
+    nq = 3 * d * f // 2
+    out[:nq] = rng.integers(0, 256, size=nq, dtype=np.uint8)
+    out[nq:nq + 3 * d * f // 32] = rng.integers(118, 125, size=3 * d * f // 32, dtype=np.uint8)
+
+
+def make_layer(cfg: int, experts: Optional[Sequence[int]] = None, fmt: str = "int4") -> Layer:
     """Draw the layer of workload ``cfg``.  ``experts`` limits which routed
-    expert blocks are drawn (None: all); the others stay zero bytes."""
+    expert blocks are drawn (None: all); the others stay zero bytes.
+    ``fmt``: "int4" (gs64 codes + float16 scales) or "mxfp4" (E2M1 nibbles +
+    an E8M0 byte per 32 elements; same block size, same router and tokens)."""
     sh, kids, _ = _streams(cfg)
     E, d, f = sh.n_experts, sh.d, sh.f
     rng_w = np.random.Generator(np.random.PCG64(kids[0]))
@@ -167,14 +178,17 @@ def make_layer(cfg: int, experts: Optional[Sequence[int]] = None) -> Layer:
     drawn = np.zeros(E, dtype=bool)
     ids = range(E) if experts is None else sorted(set(int(e) for e in experts))
     ids = list(ids)
+    assert fmt in ("int4", "mxfp4"), fmt
+    draw = ((lambda ss, out: _draw_block(ss, d, f, sh.group, out)) if fmt == "int4"
+            else (lambda ss, out: _draw_block_mxfp4(ss, d, f, out)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, max(1, len(ids)))) as ex:
-        list(ex.map(lambda e: _draw_block(kids[3 + e], d, f, sh.group, blocks[e]), ids))
+        list(ex.map(lambda e: draw(kids[3 + e], blocks[e]), ids))
     drawn[ids] = True
     shared = None
     if sh.f_shared:
         assert sh.f_shared == f, "shared expert uses the routed expert's block shape"
         shared = np.zeros(bb, dtype=np.uint8)
-        _draw_block(kids[3 + E], d, f, sh.group, shared)
+        draw(kids[3 + E], shared)
     return Layer(cfg, sh, w_router, bias, blocks, shared, drawn)
 
 

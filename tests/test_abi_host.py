@@ -52,7 +52,9 @@ def test_expert_bytes(lib):
     assert lib.moe_expert_bytes(512, 256, 64) == 208_896
     assert lib.moe_expert_bytes(2048, 1024, 64) == 3_342_336
     assert lib.moe_expert_bytes(2048, 512, 64) == 1_671_168
-    assert lib.moe_expert_bytes(6144, 2048, 32) == 0
+    # group 32: MXFP4 blocks (one E8M0 byte per 32 codes), the same size
+    assert lib.moe_expert_bytes(6144, 2048, 32) == 20_054_016
+    assert lib.moe_expert_bytes(6144, 2048, 16) == 0
     assert lib.moe_expert_bytes(100, 2048, 64) == 0
 
 
@@ -65,7 +67,8 @@ def test_workspace_sizes(lib):
     assert moe.moe_ffn_workspace_bytes(s, 2048, moe.MOE_PATH_PREFILL_BF16) >= 2048 * 9 * 2048 * 2
     for v in (moe.moe_route_workspace_bytes(s, 3), moe.moe_ffn_workspace_bytes(s, 3, 0)):
         assert v % 256 == 0
-    assert moe.moe_route_workspace_bytes(shp(group=32), 4) == 0
+    assert moe.moe_route_workspace_bytes(shp(group=16), 4) == 0
+    assert moe.moe_route_workspace_bytes(shp(group=32), 4) == moe.moe_route_workspace_bytes(shp(), 4)
 
 
 def test_status_strings(lib):
@@ -76,7 +79,7 @@ def test_status_strings(lib):
 
 @pytest.mark.parametrize("shape,status", [
     (shp(d=0), B.MOE_ERR_SHAPE), (shp(d=96), B.MOE_ERR_SHAPE), (shp(f=-64), B.MOE_ERR_SHAPE),
-    (shp(group=32), B.MOE_ERR_UNSUPPORTED), (shp(d=16384), B.MOE_ERR_UNSUPPORTED),
+    (shp(group=16), B.MOE_ERR_UNSUPPORTED), (shp(d=16384), B.MOE_ERR_UNSUPPORTED),
     (shp(E=2048, k=8), B.MOE_ERR_UNSUPPORTED), (shp(E=4, k=5), B.MOE_ERR_SHAPE),
     (shp(E=64, k=33), B.MOE_ERR_UNSUPPORTED), (shp(fs=128), B.MOE_ERR_UNSUPPORTED),
     (shp(k=0), B.MOE_ERR_SHAPE),
@@ -91,6 +94,25 @@ def test_bad_shapes_are_rejected_by_every_call(lib, shape, status):
                                None) == status
     assert lib.moe_layer_decode(s, 4, P, 0, P, None, P, None, *([P] * 10), None, P, 0, P,
                                 1 << 30, None) == status
+
+
+def test_mxfp4_shapes_only_where_built(lib):
+    """group 32 (MXFP4 blocks) is taken by the calls that do not depend on the
+    block format and by the decode path of moe_expert_ffn; the prefill path,
+    the one-call layer and its workspace size refuse it."""
+    mx = shp(group=32)
+    s = ctypes.byref(mx)
+    dec, pre = B.MOE_PATH_DECODE_F32, B.MOE_PATH_PREFILL_BF16
+    assert moe.moe_ffn_workspace_bytes(mx, 4, dec) == moe.moe_ffn_workspace_bytes(shp(), 4, dec)
+    assert moe.moe_ffn_workspace_bytes(mx, 4, pre) == 0
+    assert moe.moe_layer_decode_workspace_bytes(mx, 4) == 0
+    assert lib.moe_expert_ffn(s, 4, P, 1, P, None, P, P, P, P, pre, P, None, P, 1 << 30,
+                              None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layer_decode(s, 4, P, 0, P, None, P, None, *([P] * 10), None, P, 0, P,
+                                1 << 30, None) == B.MOE_ERR_UNSUPPORTED
+    # the decode path takes it (here stopped by the NULL x, before any launch)
+    assert lib.moe_expert_ffn(s, 4, None, 1, P, None, P, P, P, P, dec, P, None, P, 1 << 30,
+                              None) == B.MOE_ERR_NULL
 
 
 def test_null_shape(lib):

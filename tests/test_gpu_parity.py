@@ -775,3 +775,103 @@ def test_quantize_full_expert_matrix_and_round_trip_through_the_ffn():
     torch.cuda.synchronize()
     ref = oracle.moe_layer(x, wr, None, ref_blocks, None, d, f, E, k)
     assert rel_err(buf.out.cpu().numpy(), ref["out"]) <= TOL_DECODE
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 experts (E2M1 codes, one E8M0 scale per 32 elements): shape group 32
+# ----------------------------------------------------------------------------
+
+from oracle import mxfp4 as oracle_mx  # noqa: E402
+
+
+def mx_shape(L):
+    s = L.shape
+    return moe.Shape(s.d, s.f, s.n_experts, s.top_k, 32, s.f_shared)
+
+
+def np_pack_block_mx(blk, d, f):
+    """The MXFP4 packed layout, restated with numpy reshapes: codes in 64-row
+    tiles of 32-column chunks (16 bytes per row, nibbles unchanged); scale
+    bytes in the same tiles, block-major."""
+    blk = np.asarray(blk, dtype=np.uint8)
+    out = np.empty_like(blk)
+    s0 = 3 * d * f // 2
+    mats = [(f, d, 0, s0), (f, d, f * d // 2, s0 + f * d // 32),
+            (d, f, f * d, s0 + 2 * f * d // 32)]
+    for N, K, qo, so in mats:
+        nq = N * K // 2
+        q = blk[qo:qo + nq].reshape(N // 64, 64, K // 32, 16).transpose(0, 2, 1, 3)
+        out[qo:qo + nq] = np.ascontiguousarray(q).reshape(-1)
+        ns = N * K // 32
+        sc = blk[so:so + ns].reshape(N // 64, 64, K // 32).transpose(0, 2, 1)
+        out[so:so + ns] = np.ascontiguousarray(sc).reshape(-1)
+    return out
+
+
+@pytest.mark.parametrize("d,f,n", [(128, 192, 3), (6144, 2048, 1)])
+def test_pack_mxfp4_matches_layout_definition(d, f, n):
+    say(f"pack mxfp4 d={d} f={f} n={n}")
+    rng = np.random.default_rng(d + f + 1)
+    bb = oracle_mx.block_bytes(d, f)
+    blocks = rng.integers(0, 256, size=(n, bb), dtype=np.uint8)
+    sh = moe.Shape(d, f, 8, 2, 32, 0)
+    assert moe.moe_expert_bytes(d, f, 32) == bb
+    got = packed(sh, blocks).cpu().numpy()
+    for b in range(n):
+        assert np.array_equal(got[b], np_pack_block_mx(blocks[b], d, f)), f"block {b}"
+
+
+_mx_layers = {}
+
+
+def mx_layer(cfg):
+    if cfg not in _mx_layers:
+        _mx_layers.clear()
+        torch.cuda.empty_cache()
+        L = synth.make_layer(cfg, fmt="mxfp4")
+        sh = mx_shape(L)
+        dev = dict(
+            w_router=torch.from_numpy(L.w_router).cuda(),
+            bias=None if L.bias is None else torch.from_numpy(L.bias).cuda(),
+            experts=packed(sh, L.experts),
+            shared=None if L.shared is None else packed(sh, L.shared[None])[0],
+        )
+        _mx_layers[cfg] = (L, sh, dev)
+    return _mx_layers[cfg]
+
+
+@pytest.mark.parametrize("cfg,T", [(6, 8), (6, 37), (2, 1), (2, 16), (4, 1)])
+def test_layer_decode_parity_mxfp4(cfg, T):
+    """MXFP4 experts through route, union, the decode FFN (shape group 32)
+    and combine, against the float64 oracle with MXFP4 block decoding."""
+    say(f"layer decode mxfp4 cfg={cfg} T={T}")
+    L, sh, dev = mx_layer(cfg)
+    x, xf = tokens(cfg, T, 0)
+    buf = LayerBuffers.allocate(sh, T, DEC)
+    run_layer(x, dev["w_router"], dev["bias"], dev["experts"], dev["shared"], buf)
+    torch.cuda.synchronize()
+    s = L.shape
+    ref = oracle.moe_layer(xf, L.w_router, L.bias, L.experts, L.shared, s.d, s.f, s.n_experts,
+                           s.top_k, weights=oracle_mx.expert_weights)
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"],
+                            (ref["counts"], ref["offsets"], ref["perm"], ref["inv_perm"],
+                             ref["active"], ref["n_active"]))
+    ey = rel_err(buf.y.cpu().numpy()[: T * s.top_k], ref["y"])
+    assert ey <= TOL_DECODE, f"y error {ey:.2e} rms"
+    if L.shared is not None:
+        es = rel_err(buf.y_shared.cpu().numpy()[:T], ref["y_shared"])
+        assert es <= TOL_DECODE, f"y_shared error {es:.2e} rms"
+    eo = rel_err(buf.out.cpu().numpy(), ref["out"])
+    assert eo <= TOL_DECODE, f"out error {eo:.2e} rms"
+
+
+def test_mxfp4_rejected_where_not_built():
+    """MXFP4 shapes (group 32) on the prefill path and in the one-call layer
+    are refused with MOE_ERR_UNSUPPORTED, not run as int4."""
+    L, sh, dev = mx_layer(6)
+    x, _ = tokens(6, 8, 0)
+    buf = LayerBuffers.allocate(sh, 8, DEC)
+    with pytest.raises(moe.MoeError):
+        moe.moe_expert_ffn(sh, x, dev["experts"], dev["shared"], buf.offsets, buf.perm,
+                           buf.active, buf.n_active, PRE, buf.y, buf.y_shared, buf.ffn_workspace)
+    assert moe.moe_layer_decode_workspace_bytes(sh, 8) == 0
