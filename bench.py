@@ -65,6 +65,7 @@ def parse():
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-batch8", action="store_true",
                     help="skip the 8-token decode leg (run with the 1-token headline)")
+    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 decode FFN leg")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured HBM copy/read and bf16 GEMM rates")
     ap.add_argument("--counters", action="store_true",
@@ -259,6 +260,11 @@ def main():
                                                        run_layer_decode, sh, experts, shared,
                                                        w_router, bb, 8)
 
+    # ----------------------------------------------------- MXFP4 decode FFN
+    if T == 1 and not args.no_mxfp4:
+        result["mxfp4_decode"] = bench_mxfp4_decode(args, torch, moe, synth, LayerBuffers,
+                                                    run_layer, w_router, xs, dev)
+
     # ------------------------------------------------------- measured peaks
     if not args.no_peaks:
         peaks = measured_peaks(torch, dev)
@@ -344,6 +350,64 @@ def bench_decode_batch(args, torch, moe, synth, LayerBuffers, run_layer_decode, 
         "hbm_pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "workload": f"decode, {T} tokens per step, same layer, no router bias, hip graph over "
                     f"{nb} layer copies",
+    }
+
+
+def bench_mxfp4_decode(args, torch, moe, synth, LayerBuffers, run_layer, w_router, xs, dev,
+                       copies=4):
+    """The decode expert FFN (moe_expert_ffn) on MXFP4 experts of the same
+    geometry (shape group 32: E2M1 codes, one E8M0 byte per 32; the same
+    20,054,016 bytes per expert), 1-token steps rotating over `copies` layer
+    copies, each launch event-timed like the int4 FFN."""
+    L = synth.make_layer(4, fmt="mxfp4")
+    s = L.shape
+    sh = moe.Shape(s.d, s.f, s.n_experts, s.top_k, 32, s.f_shared)
+    bb = L.expert_bytes
+    src = torch.from_numpy(L.experts).to(dev)
+    experts = [torch.empty_like(src)]
+    moe.moe_pack_experts(sh, s.n_experts, src, experts[0])
+    del src
+    src = torch.from_numpy(L.shared[None]).to(dev)
+    shared = [torch.empty_like(src)[0]]
+    moe.moe_pack_experts(sh, 1, src, shared[0])
+    del src, L
+    for _ in range(1, copies):
+        experts.append(experts[0].clone())
+        shared.append(shared[0].clone())
+    DEC = moe.MOE_PATH_DECODE_F32
+    nb = len(xs)
+    bufs = [LayerBuffers.allocate(sh, 1, DEC) for _ in range(nb)]
+    for j in range(nb):
+        run_layer(xs[j], w_router, None, experts[j % copies], shared[j % copies], bufs[j])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    n = max(args.steps, 2 * nb)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(args.warmup + n):
+        j = i % nb
+        b = bufs[j]
+        if i >= args.warmup:
+            ev[i - args.warmup][0].record(stream)
+        moe.moe_expert_ffn(sh, xs[j], experts[i % copies], shared[i % copies], b.offsets, b.perm,
+                           b.active, b.n_active, DEC, b.y, b.y_shared, b.ffn_workspace)
+        if i >= args.warmup:
+            ev[i - args.warmup][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(e) for a, e in ev])
+    blocks = [int(b.n_active.item()) + 1 for b in bufs]
+    step_bytes = float(np.mean(blocks)) * bb
+    gbps = step_bytes / (ms.mean() * 1e-3) / 1e9
+    log(f"MXFP4 expert FFN kernel: mean {ms.mean() * 1e3:.1f} us, {gbps:.0f} GB/s "
+        f"({np.mean(blocks):.1f} blocks of {bb} B)")
+    del experts, shared, bufs
+    torch.cuda.empty_cache()
+    return {
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "avg_launch_us": round(float(ms.mean()) * 1e3, 2),
+        "hbm_pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "workload": "moe_expert_ffn decode path, 1 token, MXFP4 experts of the d=6144 f=2048 "
+                    f"layer (E2M1 + E8M0 per 32, {bb} B per expert), {copies} layer copies rotated",
     }
 
 

@@ -64,7 +64,7 @@ typedef enum {
   MOE_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree        */
   MOE_ERR_DTYPE = 3,       /* dtype not allowed for this call or path         */
   MOE_ERR_ALIGN = 4,       /* a pointer is not aligned as documented          */
-  MOE_ERR_UNSUPPORTED = 5, /* well-formed but not provided (e.g. group != 64) */
+  MOE_ERR_UNSUPPORTED = 5, /* well-formed but not provided (e.g. group 16)    */
   MOE_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required      */
   MOE_ERR_HIP = 7          /* a HIP launch failed                             */
 } moe_status;
@@ -89,10 +89,23 @@ typedef enum { MOE_QUANT_GS64 = 0, MOE_QUANT_ROW = 1 } moe_quant_mode;
  *  f          routed-expert intermediate size; multiple of 64, 64..8192
  *  n_experts  routed experts E, 1..1024
  *  top_k      experts per token k, 1..min(E, 32)
- *  group      int4 quantisation group along the input dimension; must be 64
- *             (gs64, the grouping the pages recommend over per-row scales:
- *             yunpan.plus article, "capability 4"; ssnai.com digest,
- *             prerequisites)
+ *  group      the expert block format, named by its quantisation group along
+ *             the input dimension:
+ *               64  int4 codes with a float16 scale per 64 elements (gs64,
+ *                   the grouping the pages recommend over per-row scales:
+ *                   yunpan.plus article, "capability 4"; ssnai.com digest,
+ *                   prerequisites);
+ *               32  MXFP4 (OCP Microscaling v1.0): FP4 E2M1 codes with an
+ *                   E8M0 scale per 32 elements (the format the pages' Kimi K3
+ *                   engine streams its experts in: ssnai.com digest,
+ *                   prerequisites).  Taken by moe_expert_bytes,
+ *                   moe_pack_experts, moe_ffn_workspace_bytes and
+ *                   moe_expert_ffn on the DECODE path, and by the calls that
+ *                   do not read expert blocks (moe_route, moe_union,
+ *                   moe_route_union, moe_combine and the route workspace
+ *                   size); the PREFILL path, moe_layer_decode and the
+ *                   expert cache return MOE_ERR_UNSUPPORTED for it.
+ *             Anything else is MOE_ERR_UNSUPPORTED.
  *  f_shared   0 = no shared expert; otherwise the shared expert's
  *             intermediate size, which must equal f (same block layout) */
 typedef struct {
@@ -116,7 +129,13 @@ typedef struct {
  * s_*: IEEE float16 scales, one per 64 consecutive input elements of a row;
  * weight[r][c] = q[r][c] * s[r][c/64].
  * Gate and up are [f][d] (input d), down is [d][f] (input f).
- * Equals 3*d*f/2 + 3*d*f/group*2; 20,054,016 bytes at d=6144, f=2048. */
+ * Equals 3*d*f/2 + 3*d*f/group*2; 20,054,016 bytes at d=6144, f=2048.
+ *
+ * MXFP4 blocks (group 32) have the same size and order, with
+ *   s_gate[f][d/32] | s_up[f][d/32] | s_down[d][f/32]
+ * as E8M0 bytes E (scale 2^(E-127), E = 255 NaN), and each nibble an FP4
+ * E2M1 code (sign, two exponent bits with bias 1, one mantissa bit:
+ * +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}); weight[r][c] = e2m1(q[r][c]) * 2^(E[r][c/32]-127). */
 size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group);
 
 /* Convert expert blocks from the layout above to the packed layout that
@@ -134,6 +153,9 @@ size_t moe_expert_bytes(int32_t d, int32_t f, int32_t group);
  * tile: the scale of row t*64+l, group g goes to
  *     s_off + (t*(K/64)*64 + g*64 + l)*2
  * where s_off is the scale sub-array offset of the canonical block.
+ * MXFP4 blocks (group 32) go to the same 64-row tiles with their nibbles
+ * unchanged (no reordering, no offset), and their E8M0 bytes block-major
+ * inside a tile: row t*64+l, block b at s_off + t*(K/32)*64 + b*64 + l.
  *  n_blocks  number of consecutive blocks in src (0 is a no-op)
  *  src       canonical blocks, 16-byte aligned
  *  dst       packed blocks, 16-byte aligned, must not overlap src */
