@@ -65,7 +65,8 @@ def parse():
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-batch8", action="store_true",
                     help="skip the 8-token decode leg (run with the 1-token headline)")
-    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 decode FFN leg")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip the MXFP4 legs (decode FFN, and the prefill step unless --no-prefill)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured HBM copy/read and bf16 GEMM rates")
     ap.add_argument("--counters", action="store_true",
@@ -262,8 +263,10 @@ def main():
 
     # ----------------------------------------------------- MXFP4 decode FFN
     if T == 1 and not args.no_mxfp4:
-        result["mxfp4_decode"] = bench_mxfp4_decode(args, torch, moe, synth, LayerBuffers,
-                                                    run_layer, w_router, xs, dev)
+        result["mxfp4_decode"], mx_pre = bench_mxfp4(args, torch, moe, synth, LayerBuffers,
+                                                     run_layer, w_router, xs, dev)
+        if mx_pre is not None:
+            result["mxfp4_prefill"] = mx_pre
 
     # ------------------------------------------------------- measured peaks
     if not args.no_peaks:
@@ -353,12 +356,13 @@ def bench_decode_batch(args, torch, moe, synth, LayerBuffers, run_layer_decode, 
     }
 
 
-def bench_mxfp4_decode(args, torch, moe, synth, LayerBuffers, run_layer, w_router, xs, dev,
-                       copies=4):
-    """The decode expert FFN (moe_expert_ffn) on MXFP4 experts of the same
-    geometry (shape group 32: E2M1 codes, one E8M0 byte per 32; the same
-    20,054,016 bytes per expert), 1-token steps rotating over `copies` layer
-    copies, each launch event-timed like the int4 FFN."""
+def bench_mxfp4(args, torch, moe, synth, LayerBuffers, run_layer, w_router, xs, dev, copies=4):
+    """The expert FFN (moe_expert_ffn) on MXFP4 experts of the same geometry
+    (shape group 32: E2M1 codes, one E8M0 byte per 32; the same 20,054,016
+    bytes per expert): the decode path in 1-token steps rotating over
+    `copies` layer copies, each launch event-timed like the int4 FFN, then
+    (unless --no-prefill) the 2048-token prefill step as for int4 experts.
+    Returns (decode result, prefill result or None)."""
     L = synth.make_layer(4, fmt="mxfp4")
     s = L.shape
     sh = moe.Shape(s.d, s.f, s.n_experts, s.top_k, 32, s.f_shared)
@@ -399,7 +403,12 @@ def bench_mxfp4_decode(args, torch, moe, synth, LayerBuffers, run_layer, w_route
     gbps = step_bytes / (ms.mean() * 1e-3) / 1e9
     log(f"MXFP4 expert FFN kernel: mean {ms.mean() * 1e3:.1f} us, {gbps:.0f} GB/s "
         f"({np.mean(blocks):.1f} blocks of {bb} B)")
-    del experts, shared, bufs
+    del bufs
+    pre = None
+    if not args.no_prefill:
+        pre = bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts[0],
+                            shared[0], w_router, dev, fmt="mxfp4")
+    del experts, shared
     torch.cuda.empty_cache()
     return {
         "value": round(gbps, 1),
@@ -408,7 +417,7 @@ def bench_mxfp4_decode(args, torch, moe, synth, LayerBuffers, run_layer, w_route
         "hbm_pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "workload": "moe_expert_ffn decode path, 1 token, MXFP4 experts of the d=6144 f=2048 "
                     f"layer (E2M1 + E8M0 per 32, {bb} B per expert), {copies} layer copies rotated",
-    }
+    }, pre
 
 
 def measured_peaks(torch, dev, reps=10):
@@ -571,8 +580,10 @@ def bench_cache(args, torch, moe, synth, sh, experts, shared, w_router, dev, war
     }
 
 
-def bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts, shared, w_router, dev):
-    """2048-token prefill step of the same layer (Zipf router bias)."""
+def bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts, shared, w_router, dev,
+                  fmt="int4"):
+    """2048-token prefill step of the same layer (Zipf router bias); fmt names
+    the expert block format of `experts` (int4 gs64 or MXFP4)."""
     L5 = synth.make_layer(5, experts=[])
     bias = torch.from_numpy(L5.bias).to(dev)
     T = 2048
@@ -608,7 +619,7 @@ def bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts,
     flops = 6.0 * sh.d * sh.f * (T * sh.top_k + T)
     tflops = flops / (ffn_ms.mean() * 1e-3) / 1e12
     n_active = int(buf.n_active.item())
-    log(f"prefill step: {ms:.3f} ms ({T / ms * 1e3:.0f} tokens/s); expert FFN {ffn_ms.mean():.3f} ms "
+    log(f"{fmt} prefill step: {ms:.3f} ms ({T / ms * 1e3:.0f} tokens/s); expert FFN {ffn_ms.mean():.3f} ms "
         f"= {tflops:.0f} TFLOP/s ({n_active} active experts)")
     return {
         "value": round(T / (ms * 1e-3), 1),
@@ -616,7 +627,8 @@ def bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts,
         "ms_per_step": round(ms, 4),
         "steps": n,
         "dtype": "bf16",
-        "workload": "prefill, 2048 tokens, same layer, Zipf(1.1) router bias",
+        "workload": "prefill, 2048 tokens, same layer, Zipf(1.1) router bias"
+                    + ("" if fmt == "int4" else ", MXFP4 experts (E2M1 + E8M0 per 32)"),
         "active_experts": n_active,
         "roofline": {
             "bound": "mfma",
@@ -625,7 +637,7 @@ def bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts,
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-            "traffic": load_traffic("prefill"),
+            "traffic": load_traffic("prefill") if fmt == "int4" else None,
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": round(float(ffn_ms.mean()) * 1e3, 1),
         },

@@ -100,11 +100,11 @@ typedef enum { MOE_QUANT_GS64 = 0, MOE_QUANT_ROW = 1 } moe_quant_mode;
  *                   engine streams its experts in: ssnai.com digest,
  *                   prerequisites).  Taken by moe_expert_bytes,
  *                   moe_pack_experts, moe_ffn_workspace_bytes and
- *                   moe_expert_ffn on the DECODE path, and by the calls that
+ *                   moe_expert_ffn on both paths, and by the calls that
  *                   do not read expert blocks (moe_route, moe_union,
  *                   moe_route_union, moe_combine and the route workspace
- *                   size); the PREFILL path, moe_layer_decode and the
- *                   expert cache return MOE_ERR_UNSUPPORTED for it.
+ *                   size); moe_layer_decode and the expert cache return
+ *                   MOE_ERR_UNSUPPORTED for it.
  *             Anything else is MOE_ERR_UNSUPPORTED.
  *  f_shared   0 = no shared expert; otherwise the shared expert's
  *             intermediate size, which must equal f (same block layout) */
@@ -248,7 +248,9 @@ size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path)
  * t = perm[p] / top_k,
  *   y[p] = W_down_e ( silu(W_gate_e x[t]) * (W_up_e x[t]) ),  silu(z) = z/(1+e^-z)
  * with every weight dequantised from int4 as q * s (group 64 along the input
- * dimension); and for the shared expert (if shape->f_shared) and every token,
+ * dimension; MXFP4 blocks: E2M1 value times 2^(E - 127) per 32 elements,
+ * which PREFILL rounds to bf16 exactly for E in 2 .. 252); and for the
+ * shared expert (if shape->f_shared) and every token,
  *   y_shared[t] = the same SwiGLU with the shared block
  * (pages: zhichai.net, MoE sparsity and three-tier sections -- 8 routed + 1
  * shared expert active per layer, int4 experts; the SwiGLU form is not on

@@ -173,7 +173,6 @@ moe_status moe_route_union(const moe_shape* shape, int32_t T, const void* x, moe
 size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path) {
   if (check_shape(shape, true) != MOE_OK || T < 0) return 0;
   const bool sh = shape->f_shared != 0;
-  if (shape->group == kGroupMxfp4 && path != MOE_PATH_DECODE_F32) return 0;
   if (path == MOE_PATH_DECODE_F32)
     return round_up(moe::ffn_decode_workspace(T, shape->top_k, shape->n_experts, shape->d,
                                               shape->f, sh));
@@ -192,7 +191,6 @@ moe_status moe_expert_ffn(const moe_shape* shape, int32_t T, const void* x, moe_
   if ((st = check_tokens(shape, T)) != MOE_OK) return st;
   if (path != MOE_PATH_DECODE_F32 && path != MOE_PATH_PREFILL_BF16) return MOE_ERR_UNSUPPORTED;
   const bool mxfp4 = shape->group == kGroupMxfp4;
-  if (mxfp4 && path != MOE_PATH_DECODE_F32) return MOE_ERR_UNSUPPORTED;  // no MXFP4 prefill
   if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
   if (path == MOE_PATH_PREFILL_BF16 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
   const bool has_shared = shape->f_shared != 0;

@@ -87,6 +87,13 @@ __device__ __forceinline__ double wave_sum_f64_tree(double v) {
   return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
+// E8M0 scale byte (MX formats) -> 2^(E - 127) as float32: E = 0 is the
+// subnormal 2^-127, E = 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e == 0 ? __uint_as_float(0x00400000u)
+                : (e == 255 ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 }  // namespace moe

@@ -206,13 +206,6 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, I));
 }
 
-// E8M0 scale byte -> 2^(E - 127) as float32 (E = 0 is the subnormal 2^-127;
-// E = 255 is NaN, as the MX format defines it).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  return e == 0 ? __uint_as_float(0x00400000u)
-                : (e == 255 ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23));
-}
-
 template <int NM, int MT, int XW, int kSst, bool MX>
 __device__ __forceinline__ void math_step(const Step<NM>& d, int cl, int nl, int cb, int nt,
                                           const uint32_t* xl, int tok_words, const float* xs,

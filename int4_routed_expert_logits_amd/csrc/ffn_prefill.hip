@@ -242,6 +242,19 @@ __device__ __forceinline__ bf16x8_t dequant_word(uint32_t w) {
   return as_bf16x8(b);
 }
 
+// MXFP4: the 8-element B operand of code word w (byte i holds elements 2i and
+// 2i + 1, low nibble first), each E2M1 value times the block scale sv as bf16,
+// one hardware conversion per pair.  Exact while every product is a normal
+// bf16, i.e. for E8M0 exponents 2 .. 252.
+__device__ __forceinline__ bf16x8_t dequant_word_mx(uint32_t w, float sv) {
+  const uint4 b = make_uint4(
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sv, 0)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sv, 1)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sv, 2)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sv, 3)));
+  return as_bf16x8(b);
+}
+
 __device__ __forceinline__ uint32_t word_of(const uint4& q, int j) {
   return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
 }
@@ -352,12 +365,15 @@ __device__ __forceinline__ void small_scale_store(uint16_t* sbuf, const uint4& v
 }
 
 // abuf: [32 rows][kALdS] bf16.
-template <int NM, int NSUB>
 // sc: this lane's scale of subtile 0 of matrix 0 for this group in the LDS
-// scale buffer; subtile sb of matrix mat sits (mat * 64 * NSUB + sb * 16)
-// rows further.
+// scale buffer (bytes).  int4: fp16 scales, one per row: subtile sb of matrix
+// mat sits (mat * 64 * NSUB + sb * 16) rows further.  MX: per 64-row tile
+// the E8M0 bytes of the group's first block of 32 (rows 0..63), then of its
+// second, and the lane's pointer already selects the block of its 16 columns
+// of K.
+template <int NM, int NSUB, bool MX>
 __device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCodes<NM, NSUB>& st,
-                                           const uint16_t* sc, int col, int kq,
+                                           const uint8_t* sc, int col, int kq,
                                            f32x4_t (&acc)[kSmallRB][NM][NSUB]) {
   uint4 a[kSmallRB][2];
   f32x4_t corr[kSmallRB];
@@ -367,19 +383,41 @@ __device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCode
     const uint4* ap = reinterpret_cast<const uint4*>(abuf + (r * kALdS + kq * 16) / 2);
     a[rb][0] = ap[0];
     a[rb][1] = ap[1];
+    if constexpr (MX) continue;
     // -136 * (row sums of the group), the same for every column
     corr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][0]), minus136(),
                                                        f32x4_t{}, 0, 0, 0);
     corr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][1]), minus136(), corr[rb],
                                                        0, 0, 0);
   }
+  if constexpr (MX) {
+    // power-of-two scales folded into the conversion: the products
+    // accumulate straight into acc
+#pragma unroll
+    for (int mat = 0; mat < NM; ++mat) {
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) {
+        const float sv = e8m0_to_f32(sc[2 * mat * 64 * NSUB + (sb >> 2) * 128 + (sb & 3) * 16]);
+        const bf16x8_t b0 = dequant_word_mx(st.q[mat][sb].x, sv);
+        const bf16x8_t b1 = dequant_word_mx(st.q[mat][sb].y, sv);
+#pragma unroll
+        for (int rb = 0; rb < kSmallRB; ++rb) {
+          acc[rb][mat][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][0]), b0,
+                                                                     acc[rb][mat][sb], 0, 0, 0);
+          acc[rb][mat][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][1]), b1,
+                                                                     acc[rb][mat][sb], 0, 0, 0);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mat = 0; mat < NM; ++mat) {
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
       const bf16x8_t b0 = dequant_word(st.q[mat][sb].x), b1 = dequant_word(st.q[mat][sb].y);
-      const float sv = static_cast<float>(
-          __builtin_bit_cast(_Float16, sc[mat * 64 * NSUB + sb * 16]));
+      const float sv = static_cast<float>(__builtin_bit_cast(
+          _Float16, reinterpret_cast<const uint16_t*>(sc)[mat * 64 * NSUB + sb * 16]));
 #pragma unroll
       for (int rb = 0; rb < kSmallRB; ++rb) {
         f32x4_t p = corr[rb];
@@ -410,7 +448,7 @@ __device__ __forceinline__ void small_a_store(uint32_t* abuf, const uint4& raw, 
 
 constexpr int kSmallBufWords = 32 * kALdS / 2;
 
-template <int NM, int NSUB, bool DOWN>
+template <int NM, int NSUB, bool DOWN, bool MX>
 __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
   constexpr int kWaveN = 16 * NSUB;
   __shared__ __align__(16) uint32_t abufs[2][kSmallBufWords];
@@ -467,8 +505,12 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
     ssrc = sl.blk + (mat == 0 ? soff[0] : soff[NM - 1]) +
            (static_cast<size_t>(pt) * groups * 64 + (threadIdx.x & 7) * 8) * 2;
   }
-  // this lane's scale (subtile 0 of matrix 0, first group of a pass) in scale buffer 0
-  const uint16_t* scl = reinterpret_cast<const uint16_t*>(sbufs) + wv * kWaveN + col;
+  // this lane's scale (subtile 0 of matrix 0, first group of a pass) in scale
+  // buffer 0; a group's slot is 2 * kScaleRows bytes.  MX: the 64-row tiles of
+  // the slot are 128 bytes each, the block of K columns kq * 16.. is
+  // kq / 2 of the group's two.
+  const uint8_t* scl = reinterpret_cast<const uint8_t*>(sbufs) +
+                       (MX ? 2 * wv * kWaveN + col + (kq >> 1) * 64 : 2 * (wv * kWaveN + col));
 
   f32x4_t acc[kSmallRB][NM][NSUB];
 #pragma unroll
@@ -505,8 +547,8 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
     for (int i = 0; i < kRing; ++i) {
       const int grp = g0 + i;
       if (active)
-        small_math<NM, NSUB>(abufs[i & 1], ring[i], scl + (pb * kRing + i) * kScaleRows, col,
-                             kq, acc);
+        small_math<NM, NSUB, MX>(abufs[i & 1], ring[i], scl + (pb * kRing + i) * 2 * kScaleRows,
+                                 col, kq, acc);
       small_a_store(abufs[(i + 1) & 1], areg[(i + 1) & 1], akeep);
       if (i == kRing - 1) small_scale_store(sbufs[pb ^ 1], snext);
       __syncthreads();
@@ -523,8 +565,8 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
       const int grp = full + i;
       if (grp < groups) {
         if (active)
-          small_math<NM, NSUB>(abufs[i & 1], ring[i], scl + (pb * kRing + i) * kScaleRows, col,
-                               kq, acc);
+          small_math<NM, NSUB, MX>(abufs[i & 1], ring[i],
+                                   scl + (pb * kRing + i) * 2 * kScaleRows, col, kq, acc);
         small_a_store(abufs[(i + 1) & 1], areg[(i + 1) & 1], akeep);
         __syncthreads();
         areg[(i + 1) & 1] = small_a_load(srcrow, min(grp + 3, groups - 1));
@@ -600,13 +642,16 @@ __device__ __forceinline__ void big_piece(int i, int& mat, int& tt, int& h, int&
   row = r & 63;
 }
 
-template <int NM, int NS>
+template <int NM, int NS, bool MX>
 __device__ __forceinline__ void big_load(const uint16_t* rowp, const uint2* sump, int ahalf,
                                          int grp, int groups, int K, int ntv,
                                          const uint8_t* const (&qbase)[NM], uint4 (&ra)[4],
                                          uint2& rs, uint4 (&rb)[Big<NM, NS>::kPieces]) {
   grp = min(grp, groups - 1);
-  rs = sump[grp];
+  if constexpr (MX)
+    rs = make_uint2(0u, 0u);  // (no offset to correct)
+  else
+    rs = sump[grp];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     ra[j] = *reinterpret_cast<const uint4*>(rowp + grp * 64 + ahalf * 32 + j * 8);
@@ -630,7 +675,7 @@ __device__ __forceinline__ uint4 masked(const uint4& v, uint32_t keep) {
 
 // The loaded group into LDS buffer `buf`: A rows (zero past the slot), then
 // the codes (zero past the matrix).
-template <int NM, int NS>
+template <int NM, int NS, bool MX>
 __device__ __forceinline__ void big_store(uint32_t* buf, int arow, int ahalf, const uint4 (&ra)[4],
                                           const uint2& rs, const uint4 (&rb)[Big<NM, NS>::kPieces],
                                           uint32_t akeep, int ntv) {
@@ -639,7 +684,7 @@ __device__ __forceinline__ void big_store(uint32_t* buf, int arow, int ahalf, co
 #pragma unroll
   for (int j = 0; j < 4; ++j) a[j] = masked(ra[j], akeep);
   // the row's sum parts as the first three elements of an 8-element A operand
-  if (ahalf == 0)
+  if (!MX && ahalf == 0)
     reinterpret_cast<uint4*>(buf + C::kAWords + C::kBWords)[arow] =
         make_uint4(rs.x & akeep, rs.y & akeep, 0u, 0u);
 #pragma unroll
@@ -657,7 +702,10 @@ __device__ __forceinline__ bf16x8_t minus136_x3() {
   return as_bf16x8(make_uint4(0xC308C308u, 0x0000C308u, 0u, 0u));
 }
 
-template <int NM, int NS>
+// sc: the staged scales.  int4: fp16 [NM][64-row tile][groups][64 rows].
+// MX: E8M0 bytes [NM][64-row tile][2 * groups blocks][64 rows], the same
+// size.
+template <int NM, int NS, bool MX>
 __device__ __forceinline__ void big_math(const uint32_t* buf, const uint32_t* zero16,
                                          const uint16_t* sc, int groups, int grp, int wm, int wn,
                                          int col, int half, f32x16_t (&acc)[2][NM][NS]) {
@@ -670,6 +718,7 @@ __device__ __forceinline__ void big_math(const uint32_t* buf, const uint32_t* ze
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       a[i][j] = *reinterpret_cast<const uint4*>(buf + (r * kALd + half * 32 + j * 8) / 2);
+    if constexpr (MX) continue;
     // -136 * (row sums of the group), the same for every column: one MFMA
     // per row block from the staged sum parts (the lanes of the upper K half
     // read zeros), shared by every matrix and column tile
@@ -678,6 +727,31 @@ __device__ __forceinline__ void big_math(const uint32_t* buf, const uint32_t* ze
         as_bf16x8(*reinterpret_cast<const uint4*>(sp)), minus136_x3(), f32x16_t{}, 0, 0, 0);
   }
   const uint4* bq = reinterpret_cast<const uint4*>(buf + C::kAWords);
+  if constexpr (MX) {
+    // the lane's block of 32 is K half `half` of the group; power-of-two
+    // scales folded into the conversion, products straight into acc
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(sc);
+#pragma unroll
+    for (int mat = 0; mat < NM; ++mat) {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const int n = wn * C::kWaveCols + ns * 32 + col;
+        const uint4 q = bq[(mat * 2 + half) * C::kWgCols + n];
+        const float sv = e8m0_to_f32(sb[2 * mat * C::kWgCols * groups + (n >> 6) * 128 * groups +
+                                        grp * 128 + half * 64 + (n & 63)]);
+        bf16x8_t bw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bw[j] = dequant_word_mx(word_of(q, j), sv);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][mat][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][j]), bw[j],
+                                                                      acc[i][mat][ns], 0, 0, 0);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mat = 0; mat < NM; ++mat) {
 #pragma unroll
@@ -703,7 +777,7 @@ __device__ __forceinline__ void big_math(const uint32_t* buf, const uint32_t* ze
   }
 }
 
-template <int NM, int NS, bool DOWN>
+template <int NM, int NS, bool DOWN, bool MX>
 __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   using C = Big<NM, NS>;
   extern __shared__ __align__(16) uint32_t lds[];
@@ -721,7 +795,8 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   const int ntv = min(C::kTilesN, (N - n0) / 64);  // packed tiles inside the matrix
   uint32_t* buf0 = lds;
   uint32_t* buf1 = lds + C::kBufWords;
-  // scales as packed: [NM][64-row tile][groups][64] fp16
+  // scales as packed: [NM][64-row tile][groups][64] fp16 (MX: the E8M0 bytes
+  // [NM][64-row tile][2 * groups][64], byte for byte the same size)
   uint16_t* sc = reinterpret_cast<uint16_t*>(lds + 2 * C::kBufWords);
 
   const size_t soff[2] = {DOWN ? g.s_down : g.s_gate, g.s_up};
@@ -761,9 +836,9 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   // so every group's loads have two groups of math to land.
   uint4 ra[2][4], rb[2][C::kPieces];
   uint2 rs[2];
-  big_load<NM, NS>(rowp, sump, ahalf, 0, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
-  big_load<NM, NS>(rowp, sump, ahalf, 1, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
-  big_store<NM, NS>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
+  big_load<NM, NS, MX>(rowp, sump, ahalf, 0, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
+  big_load<NM, NS, MX>(rowp, sump, ahalf, 1, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
+  big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
   __syncthreads();
   f32x16_t acc[2][NM][NS];
 #pragma unroll
@@ -776,14 +851,14 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
         for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = 0.0f;
   for (int g0 = 0; g0 < groups; g0 += 2) {
     // group g0 is in buf0, group g0 + 1 in register set 1
-    big_load<NM, NS>(rowp, sump, ahalf, g0 + 2, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
-    big_math<NM, NS>(buf0, zero16, sc, groups, g0, wm, wn, col, half, acc);
-    big_store<NM, NS>(buf1, arow, ahalf, ra[1], rs[1], rb[1], akeep, ntv);
+    big_load<NM, NS, MX>(rowp, sump, ahalf, g0 + 2, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
+    big_math<NM, NS, MX>(buf0, zero16, sc, groups, g0, wm, wn, col, half, acc);
+    big_store<NM, NS, MX>(buf1, arow, ahalf, ra[1], rs[1], rb[1], akeep, ntv);
     __syncthreads();
     if (g0 + 1 < groups) {
-      big_load<NM, NS>(rowp, sump, ahalf, g0 + 3, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
-      big_math<NM, NS>(buf1, zero16, sc, groups, g0 + 1, wm, wn, col, half, acc);
-      big_store<NM, NS>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
+      big_load<NM, NS, MX>(rowp, sump, ahalf, g0 + 3, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
+      big_math<NM, NS, MX>(buf1, zero16, sc, groups, g0 + 1, wm, wn, col, half, acc);
+      big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
       __syncthreads();
     }
   }
@@ -857,6 +932,52 @@ hipError_t allow_lds(K kernel, int bytes) {
 
 }  // namespace
 
+namespace {
+
+// The launches of one prefill FFN.  int4 blocks: the row-sum pass over x
+// before gate/up and over h before down (the offset correction); MXFP4 blocks
+// have no offset and skip both.
+template <bool MX>
+hipError_t prefill_kernels(const FfnProblem& p, const PrefillArgs& g, hipStream_t stream) {
+  const int ms = max_small(p.T, p.k, g.slots, p.has_shared);
+  const int mb = max_big(p.T, p.k, p.has_shared);
+  // gate/up: 64 columns of both matrices per workgroup (128 columns measured
+  // slower: the scales of the wider tile leave LDS for one workgroup per CU)
+  using GU = Big<2, 1>;
+  using DN = Big<1, 2>;
+  const int lds_gu = GU::lds_bytes(p.d / 64), lds_dn = DN::lds_bytes(p.f / 64);
+  if (lds_gu > kMaxLds || lds_dn > kMaxLds) return hipErrorNotSupported;
+  hipError_t err;
+  if ((err = allow_lds(prefill_big<2, 1, false, MX>, lds_gu)) != hipSuccess) return err;
+  if ((err = allow_lds(prefill_big<1, 2, true, MX>, lds_dn)) != hipSuccess) return err;
+  if ((err = launch(prefill_tiles, dim3(1), dim3(1024), 0, stream, g)) != hipSuccess) return err;
+  // 1-D grids: enough workgroups for the largest possible tile lists, in
+  // whole rounds of the XCDs
+  auto grid = [](int tiles, int cols) {
+    return dim3((static_cast<unsigned>(tiles) * cols + kXcds - 1) / kXcds * kXcds);
+  };
+  const int cgu = (p.f + GU::kWgCols - 1) / GU::kWgCols, cdn = (p.d + DN::kWgCols - 1) / DN::kWgCols;
+  const int sgu = (p.f + 64 * kSmallNSubGU - 1) / (64 * kSmallNSubGU);
+  const int sdn = (p.d + 64 * kSmallNSubDN - 1) / (64 * kSmallNSubDN);
+  auto rowsums = [&](const uint16_t* src, int rows, int K, uint2* dst) {
+    const long long n = static_cast<long long>(rows) * (K / 64);
+    return launch(prefill_rowsums, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                  stream, src, rows, K, dst);
+  };
+  if (!MX && (err = rowsums(g.x, p.T, p.d, g.sum_x)) != hipSuccess) return err;
+  err = launch(prefill_big<2, 1, false, MX>, grid(mb, cgu), dim3(256), lds_gu, stream, g);
+  if (err != hipSuccess) return err;
+  err = launch(prefill_small<2, kSmallNSubGU, false, MX>, grid(ms, sgu), dim3(256), 0, stream, g);
+  if (err != hipSuccess) return err;
+  if (!MX && (err = rowsums(g.h, rows_of(p.T, p.k, p.has_shared), p.f, g.sum_h)) != hipSuccess)
+    return err;
+  err = launch(prefill_big<1, 2, true, MX>, grid(mb, cdn), dim3(256), lds_dn, stream, g);
+  if (err != hipSuccess) return err;
+  return launch(prefill_small<1, kSmallNSubDN, true, MX>, grid(ms, sdn), dim3(256), 0, stream, g);
+}
+
+}  // namespace
+
 size_t ffn_prefill_workspace(int T, int k, int E, int d, int f, bool has_shared) {
   return prefill_layout(T, k, E, d, f, has_shared).total;
 }
@@ -881,7 +1002,7 @@ hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream) {
   g.q_up = ff * dd / 2;
   g.q_down = ff * dd;
   g.s_gate = 3 * dd * ff / 2;
-  g.s_up = g.s_gate + ff * (dd / 64) * 2;
+  g.s_up = g.s_gate + ff * (dd / 64) * 2;  // (MXFP4: ff * (dd / 32) bytes, the same)
   g.s_down = g.s_up + ff * (dd / 64) * 2;
   g.x = static_cast<const uint16_t*>(p.x);
   char* ws = static_cast<char*>(p.workspace);
@@ -894,40 +1015,7 @@ hipError_t launch_ffn_prefill(const FfnProblem& p, hipStream_t stream) {
   g.sum_h = reinterpret_cast<uint2*>(ws + l.sum_h);
   g.y = static_cast<uint16_t*>(p.y);
   g.y_shared = static_cast<uint16_t*>(p.y_shared);
-  const int ms = max_small(p.T, p.k, g.slots, p.has_shared);
-  const int mb = max_big(p.T, p.k, p.has_shared);
-  // gate/up: 64 columns of both matrices per workgroup (128 columns measured
-  // slower: the scales of the wider tile leave LDS for one workgroup per CU)
-  using GU = Big<2, 1>;
-  using DN = Big<1, 2>;
-  const int lds_gu = GU::lds_bytes(p.d / 64), lds_dn = DN::lds_bytes(p.f / 64);
-  if (lds_gu > kMaxLds || lds_dn > kMaxLds) return hipErrorNotSupported;
-  hipError_t err;
-  if ((err = allow_lds(prefill_big<2, 1, false>, lds_gu)) != hipSuccess) return err;
-  if ((err = allow_lds(prefill_big<1, 2, true>, lds_dn)) != hipSuccess) return err;
-  if ((err = launch(prefill_tiles, dim3(1), dim3(1024), 0, stream, g)) != hipSuccess) return err;
-  // 1-D grids: enough workgroups for the largest possible tile lists, in
-  // whole rounds of the XCDs
-  auto grid = [](int tiles, int cols) {
-    return dim3((static_cast<unsigned>(tiles) * cols + kXcds - 1) / kXcds * kXcds);
-  };
-  const int cgu = (p.f + GU::kWgCols - 1) / GU::kWgCols, cdn = (p.d + DN::kWgCols - 1) / DN::kWgCols;
-  const int sgu = (p.f + 64 * kSmallNSubGU - 1) / (64 * kSmallNSubGU);
-  const int sdn = (p.d + 64 * kSmallNSubDN - 1) / (64 * kSmallNSubDN);
-  auto rowsums = [&](const uint16_t* src, int rows, int K, uint2* dst) {
-    const long long n = static_cast<long long>(rows) * (K / 64);
-    return launch(prefill_rowsums, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                  stream, src, rows, K, dst);
-  };
-  if ((err = rowsums(g.x, p.T, p.d, g.sum_x)) != hipSuccess) return err;
-  err = launch(prefill_big<2, 1, false>, grid(mb, cgu), dim3(256), lds_gu, stream, g);
-  if (err != hipSuccess) return err;
-  err = launch(prefill_small<2, kSmallNSubGU, false>, grid(ms, sgu), dim3(256), 0, stream, g);
-  if (err != hipSuccess) return err;
-  if ((err = rowsums(g.h, rows_of(p.T, p.k, p.has_shared), p.f, g.sum_h)) != hipSuccess) return err;
-  err = launch(prefill_big<1, 2, true>, grid(mb, cdn), dim3(256), lds_dn, stream, g);
-  if (err != hipSuccess) return err;
-  return launch(prefill_small<1, kSmallNSubDN, true>, grid(ms, sdn), dim3(256), 0, stream, g);
+  return p.mxfp4 ? prefill_kernels<true>(p, g, stream) : prefill_kernels<false>(p, g, stream);
 }
 
 }  // namespace moe

@@ -98,21 +98,21 @@ def test_bad_shapes_are_rejected_by_every_call(lib, shape, status):
 
 def test_mxfp4_shapes_only_where_built(lib):
     """group 32 (MXFP4 blocks) is taken by the calls that do not depend on the
-    block format and by the decode path of moe_expert_ffn; the prefill path,
-    the one-call layer and its workspace size refuse it."""
+    block format and by both paths of moe_expert_ffn, with the int4 workspace
+    sizes; the one-call layer and its workspace size refuse it."""
     mx = shp(group=32)
     s = ctypes.byref(mx)
     dec, pre = B.MOE_PATH_DECODE_F32, B.MOE_PATH_PREFILL_BF16
     assert moe.moe_ffn_workspace_bytes(mx, 4, dec) == moe.moe_ffn_workspace_bytes(shp(), 4, dec)
-    assert moe.moe_ffn_workspace_bytes(mx, 4, pre) == 0
+    assert moe.moe_ffn_workspace_bytes(mx, 4, pre) == moe.moe_ffn_workspace_bytes(shp(), 4, pre)
+    assert moe.moe_ffn_workspace_bytes(mx, 4, pre) > 0
     assert moe.moe_layer_decode_workspace_bytes(mx, 4) == 0
-    assert lib.moe_expert_ffn(s, 4, P, 1, P, None, P, P, P, P, pre, P, None, P, 1 << 30,
-                              None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_layer_decode(s, 4, P, 0, P, None, P, None, *([P] * 10), None, P, 0, P,
                                 1 << 30, None) == B.MOE_ERR_UNSUPPORTED
-    # the decode path takes it (here stopped by the NULL x, before any launch)
-    assert lib.moe_expert_ffn(s, 4, None, 1, P, None, P, P, P, P, dec, P, None, P, 1 << 30,
-                              None) == B.MOE_ERR_NULL
+    # both paths take it (here stopped by the NULL x, before any launch)
+    for path in (dec, pre):
+        assert lib.moe_expert_ffn(s, 4, None, 1, P, None, P, P, P, P, path, P, None, P, 1 << 30,
+                                  None) == B.MOE_ERR_NULL
 
 
 def test_null_shape(lib):

@@ -347,9 +347,11 @@ def gpu_layer(cfg, T, batch=0, path=DEC, experts_override=None, fused=False):
     return L, xf, buf
 
 
-def oracle_sampled(L, xf, sample_tokens):
+def oracle_sampled(L, xf, sample_tokens, weights=None):
     """Oracle routing and grouping for the whole batch, expert outputs and
-    layer outputs only for the sampled tokens (one expert at a time)."""
+    layer outputs only for the sampled tokens (one expert at a time).
+    weights: the oracle's block decoder (default int4 gs64)."""
+    weights = oracle.expert_weights if weights is None else weights
     sh = L.shape
     idx, w, lg = oracle.route(xf, L.w_router, L.bias, sh.top_k)
     union = oracle.batch_union(idx, sh.n_experts)
@@ -364,7 +366,7 @@ def oracle_sampled(L, xf, sample_tokens):
     rows = {}
     for e, toks in need.items():
         blk = L.shared if e == "shared" else L.experts[e]
-        wts = oracle.expert_weights(blk, sh.d, sh.f)
+        wts = weights(blk, sh.d, sh.f)
         res = oracle.swiglu(np.asarray(xf[toks], dtype=np.float64), *wts)
         for t, r in zip(toks, res):
             rows[(e, t)] = r
@@ -865,13 +867,66 @@ def test_layer_decode_parity_mxfp4(cfg, T):
     assert eo <= TOL_DECODE, f"out error {eo:.2e} rms"
 
 
+# (6, 512) and (6, 97): 128-row tiles full and partial, odd group counts,
+# partial column tiles; (3, 64): 256 experts with the shared expert
+@pytest.mark.parametrize("cfg,T", [(6, 512), (6, 97), (2, 16), (3, 64)])
+def test_layer_prefill_parity_mxfp4(cfg, T):
+    """bf16 x through route, union, the MFMA FFN over MXFP4 blocks (the E8M0
+    scale folded into the E2M1 -> bf16 conversion) and a bf16 combine,
+    against the float64 oracle with MXFP4 block decoding, at the 2e-2 * rms
+    bound of the bf16 path."""
+    say(f"layer prefill mxfp4 cfg={cfg} T={T}")
+    L, sh, dev = mx_layer(cfg)
+    x, xf = tokens(cfg, T, 0)
+    buf = LayerBuffers.allocate(sh, T, PRE)
+    run_layer(x, dev["w_router"], dev["bias"], dev["experts"], dev["shared"], buf)
+    torch.cuda.synchronize()
+    s = L.shape
+    ref = oracle.moe_layer(xf, L.w_router, L.bias, L.experts, L.shared, s.d, s.f, s.n_experts,
+                           s.top_k, weights=oracle_mx.expert_weights)
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"],
+                            (ref["counts"], ref["offsets"], ref["perm"], ref["inv_perm"],
+                             ref["active"], ref["n_active"]))
+    ey = prefill_err(buf.y.float().cpu().numpy()[: T * s.top_k], ref["y"])
+    assert ey <= 1.0, f"y error {ey:.2f} x bound"
+    if L.shared is not None:
+        es = prefill_err(buf.y_shared.float().cpu().numpy()[:T], ref["y_shared"])
+        assert es <= 1.0, f"y_shared error {es:.2f} x bound"
+    eo = prefill_err(buf.out.float().cpu().numpy(), ref["out"])
+    assert eo <= 1.0, f"out error {eo:.2f} x bound"
+
+
+def test_layer_prefill_parity_mxfp4_2048_sampled():
+    """The 2048-token Zipf-routed batch over the d=6144, f=2048 layer with
+    MXFP4 blocks: every expert output of three sampled tokens and their layer
+    outputs against the oracle."""
+    sample = [0, 1000, 2047]
+    say(f"layer prefill mxfp4 cfg=5 T=2048 (sampled {sample})")
+    L, sh, dev = mx_layer(5)
+    x, xf = tokens(5, 2048, 0)
+    buf = LayerBuffers.allocate(sh, 2048, PRE)
+    run_layer(x, dev["w_router"], dev["bias"], dev["experts"], dev["shared"], buf)
+    torch.cuda.synchronize()
+    ref = oracle_sampled(L, xf, sample, weights=oracle_mx.expert_weights)
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"], ref["union"])
+    y = buf.y.float().cpu().numpy()
+    got = np.stack([y[p] for p in ref["y"]])
+    assert prefill_err(got, np.stack(list(ref["y"].values()))) <= 1.0
+    ysh = buf.y_shared.float().cpu().numpy()
+    assert prefill_err(ysh[sample], np.stack([ref["y_shared"][t] for t in sample])) <= 1.0
+    out = buf.out.float().cpu().numpy()
+    assert prefill_err(out[sample], np.stack([ref["out"][t] for t in sample])) <= 1.0
+
+
 def test_mxfp4_rejected_where_not_built():
-    """MXFP4 shapes (group 32) on the prefill path and in the one-call layer
-    are refused with MOE_ERR_UNSUPPORTED, not run as int4."""
+    """The one-call layer refuses MXFP4 shapes (group 32) with
+    MOE_ERR_UNSUPPORTED rather than running them as int4."""
     L, sh, dev = mx_layer(6)
-    x, _ = tokens(6, 8, 0)
-    buf = LayerBuffers.allocate(sh, 8, DEC)
-    with pytest.raises(moe.MoeError):
-        moe.moe_expert_ffn(sh, x, dev["experts"], dev["shared"], buf.offsets, buf.perm,
-                           buf.active, buf.n_active, PRE, buf.y, buf.y_shared, buf.ffn_workspace)
     assert moe.moe_layer_decode_workspace_bytes(sh, 8) == 0
+    x, _ = tokens(6, 8, 0)
+    buf = LayerBuffers.allocate(moe.shape_of(L.shape), 8, DEC)  # int4 sizes
+    with pytest.raises(moe.MoeError):
+        moe.moe_layer_decode(sh, x, dev["w_router"], dev["bias"], dev["experts"], dev["shared"],
+                             buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.perm,
+                             buf.inv_perm, buf.active, buf.n_active, buf.y, buf.y_shared, buf.out,
+                             buf.layer_workspace)
