@@ -67,7 +67,7 @@ struct FfnProblem {
   int T, d, f, E, k;
   bool has_shared;
   bool x_bf16;
-  bool mxfp4 = false;  // MXFP4 blocks (decode path only) instead of int4 gs64
+  bool mxfp4 = false;  // MXFP4 blocks instead of int4 gs64
   size_t block_bytes;
   const void* x;
   const uint8_t* experts;
