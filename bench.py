@@ -260,6 +260,10 @@ def main():
         result["decode_8_tokens"] = bench_decode_batch(args, torch, moe, synth, LayerBuffers,
                                                        run_layer_decode, sh, experts, shared,
                                                        w_router, bb, 8)
+        # a multi-token-prediction verify batch (the pages: 2.2-2.8 tokens per forward)
+        result["decode_3_tokens_mtp_verify"] = bench_decode_batch(
+            args, torch, moe, synth, LayerBuffers, run_layer_decode, sh, experts, shared,
+            w_router, bb, 3)
 
     # ----------------------------------------------------- MXFP4 decode FFN
     if T == 1 and not args.no_mxfp4:
@@ -300,8 +304,9 @@ def main():
 
 def bench_decode_batch(args, torch, moe, synth, LayerBuffers, run_layer_decode, sh, experts,
                        shared, w_router, bb, T):
-    """Decode steps of T tokens (the 19 MB-expert layer's second decode batch
-    size) through moe_layer_decode, captured in a HIP graph over the rotating
+    """Decode steps of T tokens (8: the 19 MB-expert layer's second decode
+    batch size; 3: a multi-token-prediction verify batch) through
+    moe_layer_decode, captured in a HIP graph over the rotating
     layer copies; expert bytes = (distinct routed experts + shared) x block."""
     dev = w_router.device
     nb = len(experts)

@@ -440,7 +440,8 @@ LAYER_OUTPUTS = ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm", 
 
 @pytest.mark.parametrize("cfg,T,out_bf16", [(1, 4, False), (1, 3, True), (2, 1, False),
                                             (2, 8, False), (2, 5, True), (3, 8, False),
-                                            (3, 1, False), (4, 1, False), (4, 8, True)])
+                                            (3, 1, False), (4, 1, False), (4, 2, False),
+                                            (4, 3, True), (4, 4, False), (4, 8, True)])
 def test_layer_decode_call_equals_the_separate_calls(cfg, T, out_bf16):
     """moe_layer_decode writes every output of route_union + expert_ffn +
     combine, bit for bit (the same function computed with fewer launches)."""
@@ -465,6 +466,21 @@ def test_layer_decode_call_equals_the_separate_calls(cfg, T, out_bf16):
         if name in ("perm", "inv_perm", "y"):
             ta, tb = ta[:n], tb[:n]
         assert torch.equal(ta.cpu(), tb.cpu()), name
+
+
+def test_layer_decode_mtp_verify_batch_sampled():
+    """A multi-token-prediction verify batch (3 tokens: the pages' 2.2-2.8
+    tokens per forward) of the 19 MB-expert layer through moe_layer_decode:
+    routing and grouping exact, every expert output and layer output of all
+    three tokens against the oracle."""
+    say("moe_layer_decode MTP verify batch cfg=4 T=3")
+    L, xf, buf = gpu_layer(4, 3, fused=True)
+    ref = oracle_sampled(L, xf, [0, 1, 2])
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"], ref["union"])
+    y = buf.y.cpu().numpy()
+    got = np.stack([y[p] for p in ref["y"]])
+    assert rel_err(got, np.stack(list(ref["y"].values()))) <= TOL_DECODE
+    assert rel_err(buf.out.cpu().numpy(), np.stack([ref["out"][t] for t in range(3)])) <= TOL_DECODE
 
 
 def test_layer_decode_call_reuses_its_workspace():
