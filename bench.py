@@ -281,9 +281,12 @@ def main():
     # --------------------------------------------------------------- prefill
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts[0], shared[0], w_router, dev)
-        if "measured_peaks" in result and "roofline" in result["prefill"]:
-            pr = result["prefill"]["roofline"]
-            pr["frac_of_measured_gemm"] = round(pr["achieved"] / result["measured_peaks"]["torch_matmul_bf16_tflops"], 4)
+    if "measured_peaks" in result:
+        for leg in ("prefill", "mxfp4_prefill"):
+            if "roofline" in result.get(leg, {}):
+                pr = result[leg]["roofline"]
+                pr["frac_of_measured_gemm"] = round(
+                    pr["achieved"] / result["measured_peaks"]["torch_matmul_bf16_tflops"], 4)
 
     # ------------------------------------------------------------ quantiser
     if not args.no_quantizer:
