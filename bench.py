@@ -423,6 +423,11 @@ def bench_mxfp4(args, torch, moe, synth, LayerBuffers, run_layer, w_router, xs, 
         "unit": "GB/s",
         "avg_launch_us": round(float(ms.mean()) * 1e3, 2),
         "hbm_pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn (decode, MXFP4)",
+                     "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic("decode", "mxfp4"),
+                     "algorithmic_bytes_per_launch": step_bytes},
         "workload": "moe_expert_ffn decode path, 1 token, MXFP4 experts of the d=6144 f=2048 "
                     f"layer (E2M1 + E8M0 per 32, {bb} B per expert), {copies} layer copies rotated",
     }, pre
@@ -645,7 +650,7 @@ def bench_prefill(args, torch, moe, synth, LayerBuffers, run_layer, sh, experts,
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-            "traffic": load_traffic("prefill") if fmt == "int4" else None,
+            "traffic": load_traffic("prefill", fmt),
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": round(float(ffn_ms.mean()) * 1e3, 1),
         },
@@ -657,7 +662,9 @@ def counter_workload(args, torch, moe, synth, LayerBuffers, run_layer, dev):
     1 GiB device-to-device copy, three times (reads and writes exactly 2^30
     bytes each: the calibration of the counters), then 20 one-token decode
     expert-FFN launches on rotating layer copies, as in the timed run, then
-    three 2048-token prefill expert-FFN launches (Zipf-biased routing)."""
+    three 2048-token prefill expert-FFN launches (Zipf-biased routing); then
+    the same decode and prefill launches over MXFP4 experts of the same
+    geometry."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
@@ -694,7 +701,6 @@ def counter_workload(args, torch, moe, synth, LayerBuffers, run_layer, dev):
                            b.active, b.n_active, DEC, b.y, b.y_shared, b.ffn_workspace)
     torch.cuda.synchronize()
     active = [int(b.n_active.item()) + 1 for b in bufs]
-    del bufs
     L5 = synth.make_layer(5, experts=[])
     bits, _ = synth.make_tokens(5, 2048)
     x5 = torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
@@ -705,17 +711,44 @@ def counter_workload(args, torch, moe, synth, LayerBuffers, run_layer, dev):
         moe.moe_expert_ffn(sh, x5, experts[0], shared[0], pb.offsets, pb.perm, pb.active,
                            pb.n_active, PRE, pb.y, pb.y_shared, pb.ffn_workspace)
     torch.cuda.synchronize()
+    del experts, shared
+    # the same launches over MXFP4 blocks (same router, so the same grouping)
+    Lm = synth.make_layer(4, fmt="mxfp4")
+    shm = moe.Shape(sh.d, sh.f, sh.n_experts, sh.top_k, 32, sh.f_shared)
+    src = torch.from_numpy(Lm.experts).to(dev)
+    mx = [torch.empty_like(src)]
+    moe.moe_pack_experts(shm, Lm.shape.n_experts, src, mx[0])
+    del src
+    src = torch.from_numpy(Lm.shared[None]).to(dev)
+    mxs = [torch.empty_like(src)[0]]
+    moe.moe_pack_experts(shm, 1, src, mxs[0])
+    del src, Lm
+    for _ in range(3):
+        mx.append(mx[0].clone())
+        mxs.append(mxs[0].clone())
+    torch.cuda.synchronize()
+    for i in range(20):
+        b = bufs[i % 4]
+        moe.moe_expert_ffn(shm, xs[i % 4], mx[i % 4], mxs[i % 4], b.offsets, b.perm, b.active,
+                           b.n_active, DEC, b.y, b.y_shared, b.ffn_workspace)
+    for _ in range(3):
+        moe.moe_expert_ffn(shm, x5, mx[0], mxs[0], pb.offsets, pb.perm, pb.active, pb.n_active,
+                           PRE, pb.y, pb.y_shared, pb.ffn_workspace)
+    torch.cuda.synchronize()
     log(f"counter workload done: copy 3 x {n} B; 20 decode FFN launches of {active} expert blocks; "
-        f"3 prefill FFN launches ({int(pb.n_active.item())} active experts)")
+        f"3 prefill FFN launches ({int(pb.n_active.item())} active experts); the same over "
+        f"MXFP4 blocks")
     return 0
 
 
-def load_traffic(which="decode"):
-    """HBM bytes per expert-FFN launch (decode or prefill) from the committed
-    counter summary, or None when that path's kernel source has changed since
-    the counters were taken (its SHA-256 is recorded with them)."""
+def load_traffic(which="decode", fmt="int4"):
+    """HBM bytes per expert-FFN launch (decode or prefill; int4 or MXFP4
+    blocks) from the committed counter summary, or None when that path's
+    kernel source has changed since the counters were taken (its SHA-256 is
+    recorded with them)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{which}_ffn_traffic.json")
+    suffix = "" if fmt == "int4" else "_" + fmt
+    path = os.path.join(ROOT, "profiles", f"{which}_ffn_traffic{suffix}.json")
     src = os.path.join(ROOT, "int4_routed_expert_logits_amd", "csrc", f"ffn_{which}.hip")
     try:
         with open(path) as fh:
