@@ -934,6 +934,47 @@ def test_layer_prefill_parity_mxfp4_2048_sampled():
     assert prefill_err(out[sample], np.stack([ref["out"][t] for t in sample])) <= 1.0
 
 
+@pytest.mark.parametrize("fmt,path,T", [("int4", "prefill", 300), ("mxfp4", "prefill", 300),
+                                         ("int4", "decode", 8), ("mxfp4", "decode", 8)])
+def test_layer_all_tokens_to_the_same_experts(fmt, path, T):
+    """Degenerate routing: a router bias of +1000 on experts 0 and 1 sends
+    every token to the same two experts (each holds all T rows: full and
+    partial 128-row tiles plus 32-row tiles on the prefill path), every other
+    expert is unrouted; layer against the oracle."""
+    say(f"layer all tokens to experts 0,1 fmt={fmt} path={path} T={T}")
+    if fmt == "int4":
+        L, dev = dev_layer(6)
+        sh = moe.shape_of(L.shape)
+        weights = None
+    else:
+        L, sh, dev = mx_layer(6)
+        weights = oracle_mx.expert_weights
+    s = L.shape
+    bias = np.zeros(s.n_experts, dtype=np.float32)
+    bias[: s.top_k] = 1000.0
+    x, xf = tokens(6, T, 3)
+    P = PRE if path == "prefill" else DEC
+    buf = LayerBuffers.allocate(sh, T, P)
+    run_layer(x, dev["w_router"], torch.from_numpy(bias).cuda(), dev["experts"], dev["shared"],
+              buf)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(xf, L.w_router, bias, L.experts, L.shared, s.d, s.f, s.n_experts,
+                           s.top_k, **({} if weights is None else {"weights": weights}))
+    assert set(np.unique(ref["topk_idx"])) == set(range(s.top_k))
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"],
+                            (ref["counts"], ref["offsets"], ref["perm"], ref["inv_perm"],
+                             ref["active"], ref["n_active"]))
+    n = T * s.top_k
+    if P == PRE:
+        assert prefill_err(buf.y.float().cpu().numpy()[:n], ref["y"]) <= 1.0
+        assert prefill_err(buf.y_shared.float().cpu().numpy()[:T], ref["y_shared"]) <= 1.0
+        assert prefill_err(buf.out.float().cpu().numpy(), ref["out"]) <= 1.0
+    else:
+        assert rel_err(buf.y.cpu().numpy()[:n], ref["y"]) <= TOL_DECODE
+        assert rel_err(buf.y_shared.cpu().numpy()[:T], ref["y_shared"]) <= TOL_DECODE
+        assert rel_err(buf.out.cpu().numpy(), ref["out"]) <= TOL_DECODE
+
+
 def test_mxfp4_rejected_where_not_built():
     """The one-call layer refuses MXFP4 shapes (group 32) with
     MOE_ERR_UNSUPPORTED rather than running them as int4."""
