@@ -257,7 +257,8 @@ __global__ __launch_bounds__(64 * kFusedMaxT) void topk_union(
 
 // Parts of d per logit, the same rule for every batch in a size class: the
 // split kernel spreads the router matrix over E*P wavefronts; the matrix-core
-// kernel cuts d into parts of at least 384 columns.  The top-k kernel holds
+// kernel cuts d into parts of at least 768 columns (384 measured slower for
+// the 2048-token batch: twice the float64 partial sums to write and re-read).  The top-k kernel holds
 // up to 16 parts for E <= 256, 8 for E <= 512, 4 beyond.
 int route_parts(int T, int d, int E) {
   const int cap = E <= 256 ? 16 : (E <= 512 ? 8 : 4);
@@ -267,7 +268,7 @@ int route_parts(int T, int d, int E) {
     const int by_len = d / 256;
     if (P > by_len) P = by_len;
   } else {
-    P = d / 384;
+    P = d / 768;
   }
   return P < 1 ? 1 : (P > cap ? cap : P);
 }

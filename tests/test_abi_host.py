@@ -60,8 +60,8 @@ def test_expert_bytes(lib):
 
 def test_workspace_sizes(lib):
     s = shp(6144, 2048, 256, 8, 64, 2048)
-    # float64 partial sums: 16 parts of d per logit for a 2048-token batch, 8 at T = 1
-    assert moe.moe_route_workspace_bytes(s, 2048) == 2048 * 256 * 16 * 8
+    # float64 partial sums: 8 parts of d per logit for a 2048-token batch, 8 at T = 1
+    assert moe.moe_route_workspace_bytes(s, 2048) == 2048 * 256 * 8 * 8
     assert moe.moe_route_workspace_bytes(s, 1) == 256 * 8 * 8
     assert moe.moe_ffn_workspace_bytes(s, 1, moe.MOE_PATH_DECODE_F32) >= (8 + 1) * 2048 * 4
     assert moe.moe_ffn_workspace_bytes(s, 2048, moe.MOE_PATH_PREFILL_BF16) >= 2048 * 9 * 2048 * 2

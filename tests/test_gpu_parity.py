@@ -127,7 +127,7 @@ def route_parts(T, d, E):
     if T <= 32:
         P = min(2048 // E, d // 256)
     else:
-        P = d // 384
+        P = d // 768
     return max(1, min(P, cap))
 
 
