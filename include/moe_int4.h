@@ -248,8 +248,12 @@ size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path)
  * t = perm[p] / top_k,
  *   y[p] = W_down_e ( silu(W_gate_e x[t]) * (W_up_e x[t]) ),  silu(z) = z/(1+e^-z)
  * with every weight dequantised from int4 as q * s (group 64 along the input
- * dimension; MXFP4 blocks: E2M1 value times 2^(E - 127) per 32 elements,
- * which PREFILL rounds to bf16 exactly for E in 2 .. 252); and for the
+ * dimension; MXFP4 blocks: E2M1 value times 2^(E - 127) per 32 elements, for
+ * every E8M0 byte: products of activations and E2M1 values are exact, and
+ * each block's scale multiplies its partial sum in float32 -- or, on
+ * PREFILL for tiles whose scale bytes all lie in 2 .. 252, is folded exactly
+ * into the bf16 weight operand; E = 255 makes the block's weights NaN); and
+ * for the
  * shared expert (if shape->f_shared) and every token,
  *   y_shared[t] = the same SwiGLU with the shared block
  * (pages: zhichai.net, MoE sparsity and three-tier sections -- 8 routed + 1
@@ -368,6 +372,15 @@ moe_status moe_cache_plan(moe_expert_cache* cache, int32_t n, const int32_t* exp
 moe_status moe_cache_stats(const moe_expert_cache* cache, int64_t* hits, int64_t* misses,
                            int64_t* bytes_fetched);
 
+/* The experts the latest step of this cache (moe_cache_layer_decode or
+ * moe_cache_plan) fetched, in placement order: fetched [k'] with evicted [k']
+ * (the expert each displaced, -1 for an empty slot), k' = *n_fetched.  A
+ * step whose copies could not all be queued records nothing (its slots are
+ * left empty).  capacity: entries the two host arrays hold (n_experts always
+ * suffices); MOE_ERR_SHAPE if fewer than k'. */
+moe_status moe_cache_last_fetch(const moe_expert_cache* cache, int32_t capacity, int32_t* fetched,
+                                int32_t* evicted, int32_t* n_fetched);
+
 /* Device scratch bytes of moe_cache_layer_decode (0 for an invalid shape). */
 size_t moe_cache_workspace_bytes(const moe_shape* shape, int32_t T, int32_t n_slots);
 
@@ -385,7 +398,9 @@ size_t moe_cache_workspace_bytes(const moe_shape* shape, int32_t T, int32_t n_sl
  *  n_slots), 256-byte aligned.
  * T * top_k <= 1024, and n_slots - (pinned experts) >= min(E, T * top_k)
  * (else MOE_ERR_UNSUPPORTED, nothing enqueued).  MOE_ERR_NULL on a
- * planning-only cache. */
+ * planning-only cache.  If a host -> slot copy cannot be queued, the call
+ * returns MOE_ERR_HIP with the step's fetched experts unmapped (their slots
+ * empty), so no later step reads a partly written slot as a hit. */
 moe_status moe_cache_layer_decode(moe_expert_cache* cache, int32_t T, const void* x,
                                   moe_dtype x_dt, const float* w_router, const float* bias,
                                   const uint8_t* shared, int32_t* topk_idx, float* topk_w,

@@ -29,7 +29,7 @@ EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_quantize", "moe_route_wo
            "moe_route", "moe_union", "moe_route_union", "moe_ffn_workspace_bytes",
            "moe_expert_ffn", "moe_combine", "moe_layer_decode_workspace_bytes",
            "moe_layer_decode", "moe_cache_create", "moe_cache_destroy", "moe_cache_pin",
-           "moe_cache_plan", "moe_cache_stats", "moe_cache_workspace_bytes",
+           "moe_cache_plan", "moe_cache_stats", "moe_cache_last_fetch", "moe_cache_workspace_bytes",
            "moe_cache_layer_decode", "moe_status_str")
 
 
@@ -101,6 +101,8 @@ def load():
     lib.moe_cache_plan.restype = c_int32
     lib.moe_cache_stats.argtypes = [vp, vp, vp, vp]
     lib.moe_cache_stats.restype = c_int32
+    lib.moe_cache_last_fetch.argtypes = [vp, c_int32, vp, vp, vp]
+    lib.moe_cache_last_fetch.restype = c_int32
     lib.moe_cache_workspace_bytes.argtypes = [sp, c_int32, c_int32]
     lib.moe_cache_workspace_bytes.restype = c_size_t
     lib.moe_cache_layer_decode.argtypes = [vp, c_int32, vp, c_int32, vp, vp, vp, vp, vp, vp, vp,
@@ -307,6 +309,17 @@ def moe_cache_stats(cache: int):
     _check("moe_cache_stats", load().moe_cache_stats(cache, ctypes.addressof(h),
                                                      ctypes.addressof(m), ctypes.addressof(b)))
     return h.value, m.value, b.value
+
+
+def moe_cache_last_fetch(cache: int, capacity: int):
+    """The latest step's fetched experts in placement order and the expert
+    each displaced (-1 for an empty slot): (fetched, evicted) lists."""
+    f = (ctypes.c_int32 * max(capacity, 1))()
+    e = (ctypes.c_int32 * max(capacity, 1))()
+    n = ctypes.c_int32()
+    _check("moe_cache_last_fetch", load().moe_cache_last_fetch(
+        cache, capacity, ctypes.addressof(f), ctypes.addressof(e), ctypes.addressof(n)))
+    return list(f[:n.value]), list(e[:n.value])
 
 
 def moe_cache_workspace_bytes(shape, T: int, n_slots: int) -> int:

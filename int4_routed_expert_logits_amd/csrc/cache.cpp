@@ -47,6 +47,9 @@ struct moe_expert_cache {
   // per-step host scratch
   std::vector<uint8_t> mark;
   std::vector<int32_t> distinct;
+  // the latest step's fetched experts in placement order and the expert each
+  // displaced (-1: an empty slot)
+  std::vector<int32_t> last_fetched, last_evicted;
   // pinned staging and the copy event, created on the first decode step
   int32_t* stage = nullptr;
   size_t stage_ints = 0;
@@ -97,6 +100,8 @@ bool plan_step(moe_expert_cache* c, int n, const int32_t* experts, int32_t* slot
   }
   if (misses > free_slots) return false;
   const int64_t now = ++c->step;
+  c->last_fetched.clear();
+  c->last_evicted.clear();
   for (int e : c->distinct) {
     const int s = c->expert_slot[e];
     if (s >= 0) {
@@ -126,11 +131,28 @@ bool plan_step(moe_expert_cache* c, int n, const int32_t* experts, int32_t* slot
     if (fetched) fetched[nf] = e;
     if (fetched_slot) fetched_slot[nf] = victim;
     if (evicted) evicted[nf] = old;
+    c->last_fetched.push_back(e);
+    c->last_evicted.push_back(old);
     ++nf;
   }
   for (int i = 0; i < n; ++i) slot_of[i] = c->expert_slot[experts[i]];
   *n_fetched = nf;
   return true;
+}
+
+// Undo the placement of a step's fetched experts after their copies could not
+// all be queued: their slots become empty (whatever part of a block reached
+// a slot is never read as a hit), and the latest-step record is cleared.
+// The experts they displaced were already unmapped by the plan.
+void unplace_fetched(moe_expert_cache* c, const int32_t* fetched, const int32_t* fetched_slot,
+                     int nf) {
+  for (int i = 0; i < nf; ++i) {
+    c->slot_expert[fetched_slot[i]] = -1;
+    c->slot_used[fetched_slot[i]] = 0;
+    c->expert_slot[fetched[i]] = -1;
+  }
+  c->last_fetched.clear();
+  c->last_evicted.clear();
 }
 
 // Device workspace of a cached decode step, in order: router partial sums,
@@ -204,6 +226,8 @@ moe_status moe_cache_create(const moe_shape* shape, int32_t n_slots, uint8_t* de
   c->pinned.assign(shape->n_experts, 0);
   c->mark.assign(shape->n_experts, 0);
   c->distinct.reserve(shape->n_experts);
+  c->last_fetched.reserve(shape->n_experts);
+  c->last_evicted.reserve(shape->n_experts);
   *cache = c;
   return MOE_OK;
 }
@@ -248,6 +272,20 @@ moe_status moe_cache_stats(const moe_expert_cache* cache, int64_t* hits, int64_t
   if (hits) *hits = cache->hits;
   if (misses) *misses = cache->misses;
   if (bytes_fetched) *bytes_fetched = cache->bytes_fetched;
+  return MOE_OK;
+}
+
+moe_status moe_cache_last_fetch(const moe_expert_cache* cache, int32_t capacity, int32_t* fetched,
+                                int32_t* evicted, int32_t* n_fetched) {
+  if (!cache || !n_fetched) return MOE_ERR_NULL;
+  const int nf = static_cast<int>(cache->last_fetched.size());
+  if (capacity < nf) return MOE_ERR_SHAPE;
+  if (nf > 0 && (!fetched || !evicted)) return MOE_ERR_NULL;
+  for (int i = 0; i < nf; ++i) {
+    fetched[i] = cache->last_fetched[i];
+    evicted[i] = cache->last_evicted[i];
+  }
+  *n_fetched = nf;
   return MOE_OK;
 }
 
@@ -321,9 +359,15 @@ moe_status moe_cache_layer_decode(moe_expert_cache* cache, int32_t T, const void
     err = hipMemcpyAsync(cache->dev_slots + static_cast<size_t>(fslot[i]) * cache->block_bytes,
                          cache->host_blocks + static_cast<size_t>(fetched[i]) * cache->block_bytes,
                          cache->block_bytes, hipMemcpyHostToDevice, cs);
-    cache->bytes_fetched += static_cast<int64_t>(cache->block_bytes);
+    if (err == hipSuccess) cache->bytes_fetched += static_cast<int64_t>(cache->block_bytes);
   }
   if (err == hipSuccess && nf > 0) err = hipEventRecord(cache->fetched_ev, cs);
+  if (err != hipSuccess) {
+    // a slot whose copy was not queued (or not fenced by the event) must not
+    // be taken for its expert later
+    unplace_fetched(cache, fetched.data(), fslot.data(), nf);
+    return MOE_ERR_HIP;
+  }
   // list A: the slots of this step's hits, list B: the fetched slots (both
   // ascending, -1 padded)
   int32_t* la = h_up + n;

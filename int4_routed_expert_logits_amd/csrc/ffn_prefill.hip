@@ -41,6 +41,7 @@
 // accumulation and the bf16 rounding of H and Y round.  Activations are
 // bf16 (an f32 x is rejected by the C ABI).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -61,6 +62,19 @@ constexpr uint32_t kMask = 0x000F000Fu;
 constexpr uint32_t kMagic = 0x43004300u;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kMaxLds = 160 * 1024;
+// E8M0 exponents for which every E2M1 value times 2^(E - 127) is a normal
+// bf16 (0.5 * 2^-125 .. 6 * 2^125), so the scale can be folded into the
+// element conversion exactly; groups with other exponents take the
+// unfolded form.
+constexpr uint32_t kMxFoldLo = 2, kMxFoldHi = 252;
+
+// True if any of the four E8M0 bytes of v lies outside kMxFoldLo .. kMxFoldHi.
+__device__ __forceinline__ bool mx_wide(uint32_t v) {
+  bool w = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w |= ((v >> (8 * i)) & 0xFFu) - kMxFoldLo > kMxFoldHi - kMxFoldLo;
+  return w;
+}
 
 struct PrefillArgs {
   const uint8_t* experts;
@@ -245,7 +259,8 @@ __device__ __forceinline__ bf16x8_t dequant_word(uint32_t w) {
 // MXFP4: the 8-element B operand of code word w (byte i holds elements 2i and
 // 2i + 1, low nibble first), each E2M1 value times the block scale sv as bf16,
 // one hardware conversion per pair.  Exact while every product is a normal
-// bf16, i.e. for E8M0 exponents 2 .. 252.
+// bf16, i.e. for E8M0 exponents 2 .. 252 (callers pass sv = 1 and scale the
+// products in float32 for groups with other exponents).
 __device__ __forceinline__ bf16x8_t dequant_word_mx(uint32_t w, float sv) {
   const uint4 b = make_uint4(
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sv, 0)),
@@ -391,21 +406,38 @@ __device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCode
                                                        0, 0, 0);
   }
   if constexpr (MX) {
-    // power-of-two scales folded into the conversion: the products
-    // accumulate straight into acc
+    // E8M0 byte of this lane's column in subtile sb of matrix mat, block b
+    // of the group (`sc` points at the lane's own block; blocks are 64 bytes
+    // apart)
+    const int own = kq >> 1;
+    auto ebyte = [&](int mat, int sb, int b) -> uint32_t {
+      return sc[2 * mat * 64 * NSUB + (sb >> 2) * 128 + (sb & 3) * 16 + (b - own) * 64];
+    };
+    // These tiles are bound by the weight stream, so the scale is not folded
+    // into the conversion: the elements convert unscaled (exact), each block
+    // of 32 gets its own MFMA chain (lanes of the other block pass zero
+    // codes), and the block's scale 2^(E - 127) multiplies the chain's sum in
+    // float32 -- exact for every E8M0 byte, as on the decode path.  Output
+    // lane (col, kq) holds column col: it applies that column's scale of
+    // each block.
 #pragma unroll
     for (int mat = 0; mat < NM; ++mat) {
 #pragma unroll
       for (int sb = 0; sb < NSUB; ++sb) {
-        const float sv = e8m0_to_f32(sc[2 * mat * 64 * NSUB + (sb >> 2) * 128 + (sb & 3) * 16]);
-        const bf16x8_t b0 = dequant_word_mx(st.q[mat][sb].x, sv);
-        const bf16x8_t b1 = dequant_word_mx(st.q[mat][sb].y, sv);
 #pragma unroll
-        for (int rb = 0; rb < kSmallRB; ++rb) {
-          acc[rb][mat][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][0]), b0,
-                                                                     acc[rb][mat][sb], 0, 0, 0);
-          acc[rb][mat][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][1]), b1,
-                                                                     acc[rb][mat][sb], 0, 0, 0);
+        for (int b = 0; b < 2; ++b) {
+          const float sv = e8m0_to_f32(ebyte(mat, sb, b));
+          const bf16x8_t b0 = dequant_word_mx(own == b ? st.q[mat][sb].x : 0u, 1.0f);
+          const bf16x8_t b1 = dequant_word_mx(own == b ? st.q[mat][sb].y : 0u, 1.0f);
+#pragma unroll
+          for (int rb = 0; rb < kSmallRB; ++rb) {
+            f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][0]), b0,
+                                                                f32x4_t{}, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][1]), b1, p, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rb][mat][sb][e] = fmaf(sv, p[e], acc[rb][mat][sb][e]);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one block's chains at a time
         }
       }
     }
@@ -705,7 +737,7 @@ __device__ __forceinline__ bf16x8_t minus136_x3() {
 // sc: the staged scales.  int4: fp16 [NM][64-row tile][groups][64 rows].
 // MX: E8M0 bytes [NM][64-row tile][2 * groups blocks][64 rows], the same
 // size.
-template <int NM, int NS, bool MX>
+template <int NM, int NS, bool MX, bool WIDE = false>
 __device__ __forceinline__ void big_math(const uint32_t* buf, const uint32_t* zero16,
                                          const uint16_t* sc, int groups, int grp, int wm, int wn,
                                          int col, int half, f32x16_t (&acc)[2][NM][NS]) {
@@ -728,26 +760,64 @@ __device__ __forceinline__ void big_math(const uint32_t* buf, const uint32_t* ze
   }
   const uint4* bq = reinterpret_cast<const uint4*>(buf + C::kAWords);
   if constexpr (MX) {
-    // the lane's block of 32 is K half `half` of the group; power-of-two
-    // scales folded into the conversion, products straight into acc
+    // the lane's block of 32 is K half `half` of the group; E8M0 byte of
+    // column n, block b of this group:
     const uint8_t* sb = reinterpret_cast<const uint8_t*>(sc);
+    auto ebyte = [&](int mat, int n, int b) -> uint32_t {
+      return sb[2 * mat * C::kWgCols * groups + (n >> 6) * 128 * groups + grp * 128 + b * 64 +
+                (n & 63)];
+    };
+    if constexpr (!WIDE) {
+      // power-of-two scales folded into the conversion, products straight
+      // into acc
+#pragma unroll
+      for (int mat = 0; mat < NM; ++mat) {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          const int n = wn * C::kWaveCols + ns * 32 + col;
+          const uint4 q = bq[(mat * 2 + half) * C::kWgCols + n];
+          const float sv = e8m0_to_f32(ebyte(mat, n, half));
+          bf16x8_t bw[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bw[j] = dequant_word_mx(word_of(q, j), sv);
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][mat][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  as_bf16x8(a[i][j]), bw[j], acc[i][mat][ns], 0, 0, 0);
+        }
+      }
+      return;
+    }
+    // The tile has a scale outside 2 .. 252 (a product E2M1 * 2^(E-127) that
+    // is not a normal bf16, or E = 255): the elements convert unscaled
+    // (exact), each block of 32 gets its own MFMA chain -- the lanes of the
+    // other K half pass zero codes -- and its scale multiplies the chain's
+    // sum in float32, as on the decode path.  Output lane (col, half) holds
+    // column col, so it applies that column's scale of each block.
 #pragma unroll
     for (int mat = 0; mat < NM; ++mat) {
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         const int n = wn * C::kWaveCols + ns * 32 + col;
         const uint4 q = bq[(mat * 2 + half) * C::kWgCols + n];
-        const float sv = e8m0_to_f32(sb[2 * mat * C::kWgCols * groups + (n >> 6) * 128 * groups +
-                                        grp * 128 + half * 64 + (n & 63)]);
-        bf16x8_t bw[4];
+#pragma unroll 1
+        for (int b = 0; b < 2; ++b) {  // (a loop: one block's operands live at a time)
+          const float sv = e8m0_to_f32(ebyte(mat, n, b));
+          bf16x8_t bw[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bw[j] = dequant_word_mx(word_of(q, j), sv);
+          for (int j = 0; j < 4; ++j) bw[j] = dequant_word_mx(half == b ? word_of(q, j) : 0u, 1.0f);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < 2; ++i) {
+            f32x16_t p = f32x16_t{};
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][mat][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][j]), bw[j],
-                                                                      acc[i][mat][ns], 0, 0, 0);
+            for (int j = 0; j < 4; ++j)
+              p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][j]), bw[j], p, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = fmaf(sv, p[e], acc[i][mat][ns][e]);
+          }
+        }
       }
     }
     return;
@@ -802,13 +872,18 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   const size_t soff[2] = {DOWN ? g.s_down : g.s_gate, g.s_up};
   const size_t qoff[2] = {DOWN ? g.q_down : g.q_gate, g.q_up};
   const uint8_t* qbase[NM];
+  bool wide = false;  // MX: a staged scale byte outside 2 .. 252
 #pragma unroll
   for (int mat = 0; mat < NM; ++mat) {
     qbase[mat] = sl.blk + qoff[mat] + static_cast<size_t>(n0 / 64) * 32 * K;
     const uint4* src = reinterpret_cast<const uint4*>(sl.blk + soff[mat] +
                                                       static_cast<size_t>(n0) * groups * 2);
     uint4* dst = reinterpret_cast<uint4*>(sc + mat * C::kWgCols * groups);
-    for (int i = threadIdx.x; i < ntv * 64 * groups / 8; i += 256) dst[i] = src[i];
+    for (int i = threadIdx.x; i < ntv * 64 * groups / 8; i += 256) {
+      const uint4 v = src[i];
+      dst[i] = v;
+      if constexpr (MX) wide |= mx_wide(v.x) | mx_wide(v.y) | mx_wide(v.z) | mx_wide(v.w);
+    }
   }
   const int t = threadIdx.x, arow = t >> 1, ahalf = t & 1;
   const int m = m0 + arow;
@@ -832,35 +907,49 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   const int wv = t >> 6, lane = t & 63;
   const int wm = wv & 1, wn = wv >> 1, col = lane & 31, half = lane >> 5;
 
-  // Two register sets: group g+1 is stored to LDS while g+2 is in flight,
-  // so every group's loads have two groups of math to land.
-  uint4 ra[2][4], rb[2][C::kPieces];
-  uint2 rs[2];
-  big_load<NM, NS, MX>(rowp, sump, ahalf, 0, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
-  big_load<NM, NS, MX>(rowp, sump, ahalf, 1, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
-  big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
-  __syncthreads();
   f32x16_t acc[2][NM][NS];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int mat = 0; mat < NM; ++mat)
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = 0.0f;
-  for (int g0 = 0; g0 < groups; g0 += 2) {
-    // group g0 is in buf0, group g0 + 1 in register set 1
-    big_load<NM, NS, MX>(rowp, sump, ahalf, g0 + 2, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
-    big_math<NM, NS, MX>(buf0, zero16, sc, groups, g0, wm, wn, col, half, acc);
-    big_store<NM, NS, MX>(buf1, arow, ahalf, ra[1], rs[1], rb[1], akeep, ntv);
+  // The main loop, with the scales folded into the element conversion or
+  // (MX tiles with a scale byte outside 2 .. 252) applied per block in
+  // float32.  The choice is per workgroup and uniform.
+  auto main_loop = [&](auto wide_tag) {
+    constexpr bool W = decltype(wide_tag)::value;
+    // Two register sets: group g+1 is stored to LDS while g+2 is in flight,
+    // so every group's loads have two groups of math to land.
+    uint4 ra[2][4], rb[2][C::kPieces];
+    uint2 rs[2];
+    big_load<NM, NS, MX>(rowp, sump, ahalf, 0, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
+    big_load<NM, NS, MX>(rowp, sump, ahalf, 1, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
+    big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
     __syncthreads();
-    if (g0 + 1 < groups) {
-      big_load<NM, NS, MX>(rowp, sump, ahalf, g0 + 3, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
-      big_math<NM, NS, MX>(buf1, zero16, sc, groups, g0 + 1, wm, wn, col, half, acc);
-      big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int mat = 0; mat < NM; ++mat)
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = 0.0f;
+    for (int g0 = 0; g0 < groups; g0 += 2) {
+      // group g0 is in buf0, group g0 + 1 in register set 1
+      big_load<NM, NS, MX>(rowp, sump, ahalf, g0 + 2, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
+      big_math<NM, NS, MX, W>(buf0, zero16, sc, groups, g0, wm, wn, col, half, acc);
+      big_store<NM, NS, MX>(buf1, arow, ahalf, ra[1], rs[1], rb[1], akeep, ntv);
       __syncthreads();
+      if (g0 + 1 < groups) {
+        big_load<NM, NS, MX>(rowp, sump, ahalf, g0 + 3, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
+        big_math<NM, NS, MX, W>(buf1, zero16, sc, groups, g0 + 1, wm, wn, col, half, acc);
+        big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
+        __syncthreads();
+      }
     }
+  };
+  if constexpr (MX) {
+    if (__syncthreads_or(wide))
+      main_loop(std::true_type{});
+    else
+      main_loop(std::false_type{});
+  } else {
+    main_loop(std::false_type{});
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {

@@ -55,6 +55,8 @@ def test_policy_matches_the_reference_model(E, k, slots, T, pins, seed):
             assert slot_of.tolist() == [placed[int(e)] for e in ids]
             assert fetched.tolist() == rf
             assert evicted.tolist() == [-1 if rev[e] is None else rev[e] for e in rf]
+            # the latest-step record the GPU tests read after a decode step
+            assert moe.moe_cache_last_fetch(h, E) == (fetched.tolist(), evicted.tolist())
         hits, misses, nbytes = moe.moe_cache_stats(h)
         assert (hits, misses, nbytes) == (ref.hits, ref.misses, 0)
     finally:
@@ -73,6 +75,12 @@ def test_a_step_that_cannot_fit_leaves_the_state_unchanged():
         assert ei.value.status == B.MOE_ERR_UNSUPPORTED
         slot_of, fetched, _ = moe.moe_cache_plan(h, [2, 3])
         assert fetched.size == 0  # 2 and 3 still resident
+        assert moe.moe_cache_last_fetch(h, 16) == ([], [])
+        moe.moe_cache_plan(h, [0, 9])
+        assert moe.moe_cache_last_fetch(h, 16) == ([9], [2])  # 2 and 3 tie; lower slot
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_cache_last_fetch(h, 0)  # one entry does not fit in none
+        assert ei.value.status == B.MOE_ERR_SHAPE
     finally:
         moe.moe_cache_destroy(h)
 

@@ -16,6 +16,7 @@ import oracle
 import synth
 import int4_routed_expert_logits_amd as moe
 from int4_routed_expert_logits_amd.layer import LayerBuffers, run_layer, run_layer_decode
+from oracle_rows import oracle_sampled, expert_rows, prefill_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -347,42 +348,6 @@ def gpu_layer(cfg, T, batch=0, path=DEC, experts_override=None, fused=False):
     return L, xf, buf
 
 
-def oracle_sampled(L, xf, sample_tokens, weights=None):
-    """Oracle routing and grouping for the whole batch, expert outputs and
-    layer outputs only for the sampled tokens (one expert at a time).
-    weights: the oracle's block decoder (default int4 gs64)."""
-    weights = oracle.expert_weights if weights is None else weights
-    sh = L.shape
-    idx, w, lg = oracle.route(xf, L.w_router, L.bias, sh.top_k)
-    union = oracle.batch_union(idx, sh.n_experts)
-    inv = union[3]
-    # expert -> sampled tokens that use it; one expert's weights in memory at a time
-    need = {}
-    for t in sample_tokens:
-        for j in range(sh.top_k):
-            need.setdefault(int(idx[t, j]), []).append(t)
-        if L.shared is not None:
-            need.setdefault("shared", []).append(t)
-    rows = {}
-    for e, toks in need.items():
-        blk = L.shared if e == "shared" else L.experts[e]
-        wts = weights(blk, sh.d, sh.f)
-        res = oracle.swiglu(np.asarray(xf[toks], dtype=np.float64), *wts)
-        for t, r in zip(toks, res):
-            rows[(e, t)] = r
-        del wts
-    y, ysh, out = {}, {}, {}
-    for t in sample_tokens:
-        acc = np.zeros(sh.d)
-        for j in range(sh.top_k):
-            p = int(inv[t * sh.top_k + j])
-            y[p] = rows[(int(idx[t, j]), t)]
-            acc += float(w[t, j]) * y[p]
-        ysh[t] = rows[("shared", t)] if L.shared is not None else np.zeros(sh.d)
-        out[t] = acc + ysh[t]
-    return dict(topk_idx=idx, topk_w=w, union=union, y=y, y_shared=ysh, out=out, logits=lg)
-
-
 def check_routing_and_union(buf, ref_idx, ref_w, union):
     counts, offsets, perm, inv, active, n_active = union
     assert np.array_equal(buf.topk_idx.cpu().numpy(), ref_idx)
@@ -630,15 +595,29 @@ PRE = moe.MOE_PATH_PREFILL_BF16
 TOL_PREFILL = 2e-2
 
 
-def prefill_err(got, ref):
-    """Largest error of a bf16 prefill output in units of the stated bound:
-    2e-2 * rms(ref) for the arithmetic, plus the output's own round-to-
-    nearest bf16 rounding of up to 2^-8 * |ref| (outputs here reach ~6.5
-    rms, where that rounding alone is ~2.5e-2 rms).  <= 1 passes."""
+# An ideal kernel that keeps h and y in bf16 (the prefill path's storage
+# format) already reaches 1.6-2.5e-2 * rms at the worst element of these
+# layers (float64 simulation), so the strict ratio is printed and held to a
+# sanity cap, and the pass/fail bound is element-wise.
+STRICT_CAP = 3e-2
+
+
+def prefill_err(got, ref, name="", check=True):
+    """Largest error of a bf16 prefill output in units of the bound actually
+    checked, element by element: 2e-2 * rms(ref) for the arithmetic plus
+    half an ulp of the bf16 result at |ref| (at most 2^-8 * |ref|: outputs
+    here reach ~6.5 rms, where that rounding alone is ~2.5e-2 rms); <= 1
+    passes.  Also prints the strict max|err| / rms(ref) and, with check,
+    asserts it stays under STRICT_CAP."""
     ref = np.asarray(ref, dtype=np.float64)
     got = np.asarray(got, dtype=np.float64)
     rms = float(np.sqrt(np.mean(ref ** 2)))
-    return float(np.max(np.abs(got - ref) / (TOL_PREFILL * rms + 2.0 ** -8 * np.abs(ref))))
+    strict = float(np.max(np.abs(got - ref))) / rms
+    bound = float(np.max(np.abs(got - ref) / (TOL_PREFILL * rms + 2.0 ** -8 * np.abs(ref))))
+    say(f"  {name}: strict max|err|/rms = {strict:.4f}, element-wise bound ratio = {bound:.3f}")
+    if check:
+        assert strict <= STRICT_CAP, f"{name}: strict error {strict:.4f} * rms"
+    return bound
 # (6, 512) and (6, 97): 128-row tiles (full and partial), odd group counts
 # along d and f, partial column tiles, an unrouted expert
 PREFILL_FULL = [(2, 16), (2, 5), (3, 64), (3, 13), (6, 512), (6, 97)]
@@ -656,13 +635,20 @@ def test_layer_prefill_parity(cfg, T):
     check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"],
                             (ref["counts"], ref["offsets"], ref["perm"], ref["inv_perm"],
                              ref["active"], ref["n_active"]))
-    ey = prefill_err(buf.y.float().cpu().numpy()[: T * sh.top_k], ref["y"])
+    ey = prefill_err(buf.y.float().cpu().numpy()[: T * sh.top_k], ref["y"], "y")
     assert ey <= 1.0, f"y error {ey:.2f} x bound"
     if L.shared is not None:
-        es = prefill_err(buf.y_shared.float().cpu().numpy()[:T], ref["y_shared"])
+        es = prefill_err(buf.y_shared.float().cpu().numpy()[:T], ref["y_shared"], "y_shared")
         assert es <= 1.0, f"y_shared error {es:.2f} x bound"
-    eo = prefill_err(buf.out.float().cpu().numpy(), ref["out"])
+    eo = prefill_err(buf.out.float().cpu().numpy(), ref["out"], "out (bf16)")
     assert eo <= 1.0, f"out error {eo:.2f} x bound"
+    # the same y combined into a float32 out: only y's bf16 storage and the
+    # arithmetic remain
+    out32 = torch.empty((T, sh.d), dtype=torch.float32, device="cuda")
+    moe.moe_combine(moe.shape_of(sh), buf.y, buf.y_shared, buf.inv_perm, buf.topk_w, out32)
+    torch.cuda.synchronize()
+    e32 = prefill_err(out32.cpu().numpy(), ref["out"], "out (f32 combine)")
+    assert e32 <= 1.0, f"out (f32) error {e32:.2f} x bound"
 
 
 @pytest.mark.parametrize("cfg,T,sample", [(4, 40, [0, 17, 39]), (5, 2048, [0, 1000, 2047])])
@@ -677,11 +663,52 @@ def test_layer_prefill_parity_19mb_layer_sampled(cfg, T, sample):
     check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"], ref["union"])
     y = buf.y.float().cpu().numpy()
     got = np.stack([y[p] for p in ref["y"]])
-    assert prefill_err(got, np.stack(list(ref["y"].values()))) <= 1.0
+    assert prefill_err(got, np.stack(list(ref["y"].values())), "y") <= 1.0
     ysh = buf.y_shared.float().cpu().numpy()
-    assert prefill_err(ysh[sample], np.stack([ref["y_shared"][t] for t in sample])) <= 1.0
+    assert prefill_err(ysh[sample], np.stack([ref["y_shared"][t] for t in sample]),
+                       "y_shared") <= 1.0
     out = buf.out.float().cpu().numpy()
-    assert prefill_err(out[sample], np.stack([ref["out"][t] for t in sample])) <= 1.0
+    assert prefill_err(out[sample], np.stack([ref["out"][t] for t in sample]), "out") <= 1.0
+
+
+@pytest.mark.timeout(900)
+def test_layer_prefill_parity_2048_every_tile():
+    """The 2048-token Zipf-routed batch of the ~19 MB-expert layer at full
+    size: the first and the last row of every 128-row and every 32-row M-tile
+    of every expert (and of the shared expert's tiles), plus every row of the
+    heaviest expert and of the one-row experts, against the oracle."""
+    say("layer prefill cfg=5 T=2048, every tile's first and last row")
+    L, xf, buf = gpu_layer(5, 2048, path=PRE)
+    sh = L.shape
+    idx, w, _ = oracle.route(xf, L.w_router, L.bias, sh.top_k)
+    union = oracle.batch_union(idx, sh.n_experts)
+    counts, offsets, perm, inv, active, n_active = union
+    check_routing_and_union(buf, idx, w, union)
+    requests, positions = {}, []
+    heavy = int(np.argmax(counts))
+    n_tiles = 0
+    for a in range(int(n_active[0])):
+        e = int(active[a])
+        lo, M = int(offsets[e]), int(counts[e])
+        tiles = prefill_tiles(M)
+        n_tiles += len(tiles)
+        rows = sorted({r for t in tiles for r in t}) if e != heavy and M > 1 else range(M)
+        for r in rows:
+            p = lo + r
+            positions.append((e, p, int(perm[p]) // sh.top_k))
+            requests.setdefault(e, []).append(int(perm[p]) // sh.top_k)
+    shared_rows = sorted({r for t in prefill_tiles(2048) for r in t})
+    requests["shared"] = shared_rows
+    say(f"  {n_tiles} routed M-tiles over {int(n_active[0])} experts, {len(positions)} rows; "
+        f"heaviest expert {heavy} with {int(counts[heavy])} rows")
+    rows = expert_rows(L, xf, requests)
+    y = buf.y.float().cpu().numpy()
+    got = np.stack([y[p] for _, p, _ in positions])
+    ref = np.stack([rows[(e, t)] for e, _, t in positions])
+    assert prefill_err(got, ref, "y (tile rows)") <= 1.0
+    ysh = buf.y_shared.float().cpu().numpy()
+    assert prefill_err(ysh[shared_rows], np.stack([rows[("shared", t)] for t in shared_rows]),
+                       "y_shared (tile rows)") <= 1.0
 
 
 def test_prefill_empty_batch():
@@ -903,12 +930,12 @@ def test_layer_prefill_parity_mxfp4(cfg, T):
     check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"],
                             (ref["counts"], ref["offsets"], ref["perm"], ref["inv_perm"],
                              ref["active"], ref["n_active"]))
-    ey = prefill_err(buf.y.float().cpu().numpy()[: T * s.top_k], ref["y"])
+    ey = prefill_err(buf.y.float().cpu().numpy()[: T * s.top_k], ref["y"], "y")
     assert ey <= 1.0, f"y error {ey:.2f} x bound"
     if L.shared is not None:
-        es = prefill_err(buf.y_shared.float().cpu().numpy()[:T], ref["y_shared"])
+        es = prefill_err(buf.y_shared.float().cpu().numpy()[:T], ref["y_shared"], "y_shared")
         assert es <= 1.0, f"y_shared error {es:.2f} x bound"
-    eo = prefill_err(buf.out.float().cpu().numpy(), ref["out"])
+    eo = prefill_err(buf.out.float().cpu().numpy(), ref["out"], "out (bf16)")
     assert eo <= 1.0, f"out error {eo:.2f} x bound"
 
 
@@ -927,11 +954,86 @@ def test_layer_prefill_parity_mxfp4_2048_sampled():
     check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"], ref["union"])
     y = buf.y.float().cpu().numpy()
     got = np.stack([y[p] for p in ref["y"]])
-    assert prefill_err(got, np.stack(list(ref["y"].values()))) <= 1.0
+    assert prefill_err(got, np.stack(list(ref["y"].values())), "y") <= 1.0
     ysh = buf.y_shared.float().cpu().numpy()
-    assert prefill_err(ysh[sample], np.stack([ref["y_shared"][t] for t in sample])) <= 1.0
+    assert prefill_err(ysh[sample], np.stack([ref["y_shared"][t] for t in sample]),
+                       "y_shared") <= 1.0
     out = buf.out.float().cpu().numpy()
-    assert prefill_err(out[sample], np.stack([ref["out"][t] for t in sample])) <= 1.0
+    assert prefill_err(out[sample], np.stack([ref["out"][t] for t in sample]), "out") <= 1.0
+
+
+# MXFP4 scale bytes at and beyond the range where E2M1 * 2^(E - 127) is a
+# normal bf16 (2 .. 252), and the NaN byte.
+MX_EDGE_E = [0, 1, 2, 126, 252, 253, 254, 255]
+
+
+def mx_edge_layer(E):
+    """Layer 6 with MXFP4 blocks whose gate and up scale bytes are all E (every
+    routed expert and the shared one), and bf16 tokens scaled by a power of two
+    that keeps each product E2M1 * 2^(E - 127) * x, and the sums of 32 of
+    them, inside the float32 range: x * 2^117 for E <= 2, x * 2^-118 for
+    E >= 252 (every |x| first raised to at least 2^-8, so the scaled tokens
+    stay normal bf16 numbers).  The down blocks keep their drawn scales."""
+    L = synth.make_layer(6, fmt="mxfp4")
+    s = L.shape
+    n_gu = 2 * s.f * s.d // 32  # gate and up scale bytes, right after the codes
+    q_end = 3 * s.d * s.f // 2
+    L.experts[:, q_end:q_end + n_gu] = E
+    L.shared[q_end:q_end + n_gu] = E
+    k = 117 if E <= 2 else (-118 if 252 <= E <= 254 else 0)
+    return L, k
+
+
+def mx_edge_tokens(T, k):
+    bits, xf = synth.make_tokens(6, T, 5)
+    xf = np.sign(xf) * np.maximum(np.abs(xf), 2.0 ** -8)  # exact in bf16
+    xf = (xf * 2.0 ** k).astype(np.float32)  # a power of two: exact
+    bits = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(synth.bf16_to_f32(bits), xf)
+    return bits, xf
+
+
+@pytest.mark.parametrize("path,T", [("decode", 37), ("prefill", 300)])
+@pytest.mark.parametrize("E", MX_EDGE_E)
+def test_mxfp4_every_scale_byte(E, path, T):
+    """MXFP4 blocks are decoded exactly for every E8M0 byte, on both paths:
+    the edge exponents 0, 1, 2, 252, 253, 254 (whose weights are bf16
+    subnormals or overflow bf16 when folded into the element conversion) and
+    E = 255, which makes every weight of the block NaN, as in the oracle.
+    The prefill batch has 128-row and 32-row tiles and the shared expert."""
+    say(f"mxfp4 scale byte E={E} path={path} T={T}")
+    L, k = mx_edge_layer(E)
+    sh = mx_shape(L)
+    s = L.shape
+    bits, xf = mx_edge_tokens(T, k)
+    x = torch.from_numpy(bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+    experts = packed(sh, L.experts)
+    shared = packed(sh, L.shared[None])[0]
+    P = PRE if path == "prefill" else DEC
+    buf = LayerBuffers.allocate(sh, T, P)
+    run_layer(x, torch.from_numpy(L.w_router).cuda(), torch.from_numpy(L.bias).cuda(), experts,
+              shared, buf)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(xf, L.w_router, L.bias, L.experts, L.shared, s.d, s.f, s.n_experts,
+                           s.top_k, weights=oracle_mx.expert_weights)
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"],
+                            (ref["counts"], ref["offsets"], ref["perm"], ref["inv_perm"],
+                             ref["active"], ref["n_active"]))
+    n = T * s.top_k
+    got = dict(y=buf.y.float().cpu().numpy()[:n], y_shared=buf.y_shared.float().cpu().numpy()[:T],
+               out=buf.out.float().cpu().numpy())
+    for name in ("y", "y_shared", "out"):
+        g, r = got[name], ref[name]
+        if E == 255:
+            assert np.isnan(r).all() and np.isnan(g).all(), name
+            continue
+        assert np.isfinite(r).all() and np.isfinite(g).all(), name
+        if P == PRE:
+            assert prefill_err(g, r, name) <= 1.0, name
+        else:
+            e = rel_err(g, r)
+            say(f"  {name}: max|err|/rms = {e:.2e}")
+            assert e <= TOL_DECODE, name
 
 
 @pytest.mark.parametrize("fmt,path,T", [("int4", "prefill", 300), ("mxfp4", "prefill", 300),
@@ -966,9 +1068,10 @@ def test_layer_all_tokens_to_the_same_experts(fmt, path, T):
                              ref["active"], ref["n_active"]))
     n = T * s.top_k
     if P == PRE:
-        assert prefill_err(buf.y.float().cpu().numpy()[:n], ref["y"]) <= 1.0
-        assert prefill_err(buf.y_shared.float().cpu().numpy()[:T], ref["y_shared"]) <= 1.0
-        assert prefill_err(buf.out.float().cpu().numpy(), ref["out"]) <= 1.0
+        assert prefill_err(buf.y.float().cpu().numpy()[:n], ref["y"], "y") <= 1.0
+        assert prefill_err(buf.y_shared.float().cpu().numpy()[:T], ref["y_shared"],
+                           "y_shared") <= 1.0
+        assert prefill_err(buf.out.float().cpu().numpy(), ref["out"], "out") <= 1.0
     else:
         assert rel_err(buf.y.cpu().numpy()[:n], ref["y"]) <= TOL_DECODE
         assert rel_err(buf.y_shared.cpu().numpy()[:T], ref["y_shared"]) <= TOL_DECODE
