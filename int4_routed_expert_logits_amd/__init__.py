@@ -8,7 +8,8 @@ from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, MOE_BF16, MOE_F32, MOE_OK, MOE_PATH_DECODE_F32, MOE_PATH_PREFILL_BF16,
     MOE_QUANT_GS64, MOE_QUANT_ROW, MoeError, Shape, STATUS_NAMES, load, moe_combine,
     moe_expert_bytes, moe_expert_ffn, moe_ffn_workspace_bytes, moe_layer_decode,
-    moe_layer_decode_workspace_bytes, moe_pack_experts, moe_quantize,
+    moe_layer_decode_workspace_bytes, moe_layer_decode_static, moe_layer_decode_static_max_bytes,
+    moe_pack_experts, moe_quantize,
     moe_route, moe_route_union, moe_route_workspace_bytes, moe_status_str, moe_union,
     moe_cache_create, moe_cache_destroy, moe_cache_layer_decode, moe_cache_pin, moe_cache_plan,
     moe_cache_stats, moe_cache_last_fetch, moe_cache_workspace_bytes,

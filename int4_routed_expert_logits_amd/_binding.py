@@ -28,7 +28,8 @@ MOE_QUANT_GS64, MOE_QUANT_ROW = 0, 1
 EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_quantize", "moe_route_workspace_bytes",
            "moe_route", "moe_union", "moe_route_union", "moe_ffn_workspace_bytes",
            "moe_expert_ffn", "moe_combine", "moe_layer_decode_workspace_bytes",
-           "moe_layer_decode", "moe_cache_create", "moe_cache_destroy", "moe_cache_pin",
+           "moe_layer_decode", "moe_layer_decode_static", "moe_layer_decode_static_max_bytes",
+           "moe_cache_create", "moe_cache_destroy", "moe_cache_pin",
            "moe_cache_plan", "moe_cache_stats", "moe_cache_last_fetch", "moe_cache_workspace_bytes",
            "moe_cache_layer_decode", "moe_status_str")
 
@@ -90,6 +91,12 @@ def load():
                                       c_void_p] + [c_void_p] * 11 + [c_int32, c_void_p, c_size_t,
                                                                      c_void_p])
     lib.moe_layer_decode.restype = c_int32
+    lib.moe_layer_decode_static.argtypes = ([sp, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
+                                             c_void_p, c_void_p] + [c_void_p] * 11 +
+                                            [c_int32, c_void_p])
+    lib.moe_layer_decode_static.restype = c_int32
+    lib.moe_layer_decode_static_max_bytes.argtypes = []
+    lib.moe_layer_decode_static_max_bytes.restype = c_size_t
     vp = c_void_p
     lib.moe_cache_create.argtypes = [sp, c_int32, vp, vp, POINTER(vp)]
     lib.moe_cache_create.restype = c_int32
@@ -261,6 +268,23 @@ def moe_layer_decode(shape, x, w_router, bias, experts, shared, topk_idx, topk_w
         _ptr(perm), _ptr(inv_perm), _ptr(active), _ptr(n_active), _ptr(y), _ptr(y_shared),
         _ptr(out), _dtype(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def moe_layer_decode_static_max_bytes() -> int:
+    return load().moe_layer_decode_static_max_bytes()
+
+
+def moe_layer_decode_static(shape, x, w_router, bias, experts, shared, topk_idx, topk_w, counts,
+                            offsets, perm, inv_perm, active, n_active, y, y_shared, out,
+                            stream=None):
+    """moe_layer_decode without a workspace: the library's static per-GPU
+    scratch array stands in for it (include/moe_int4_static.h)."""
+    sh = _shape(shape)
+    _check("moe_layer_decode_static", load().moe_layer_decode_static(
+        ctypes.byref(sh), x.shape[0], _ptr(x), _dtype(x), _ptr(w_router), _ptr(bias),
+        _ptr(experts), _ptr(shared), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+        _ptr(perm), _ptr(inv_perm), _ptr(active), _ptr(n_active), _ptr(y), _ptr(y_shared),
+        _ptr(out), _dtype(out), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "api_internal.h"
 #include "launch.h"
 #include "moe_int4.h"
 
@@ -56,6 +57,53 @@ moe_status hip_status(hipError_t e) {
 }
 
 }  // namespace
+
+namespace moe {
+
+// Every argument check of moe_layer_decode except the workspace's.
+moe_status layer_decode_check(const moe_shape* shape, int32_t T, const void* x, moe_dtype x_dt,
+                              const float* w_router, const float* bias, const uint8_t* experts,
+                              const uint8_t* shared, const int32_t* topk_idx,
+                              const float* topk_w, const int32_t* counts,
+                              const int32_t* offsets, const int32_t* perm,
+                              const int32_t* inv_perm, const int32_t* active,
+                              const int32_t* n_active, const void* y, const void* y_shared,
+                              const void* out, moe_dtype out_dt) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(shape, T)) != MOE_OK) return st;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (out_dt != MOE_F32 && out_dt != MOE_BF16) return MOE_ERR_DTYPE;
+  const int E = shape->n_experts, d = shape->d;
+  const bool has_shared = shape->f_shared != 0;
+  moe::FfnProblem p{};
+  p.T = T;
+  p.d = d;
+  p.f = shape->f;
+  p.E = E;
+  p.k = shape->top_k;
+  p.has_shared = has_shared;
+  p.x_bf16 = x_dt == MOE_BF16;
+  p.block_bytes = moe_expert_bytes(shape->d, shape->f, shape->group);
+  if (T > 0 && !moe::ffn_decode_groups_batch(p, moe::route_parts(T, d, E)))
+    return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets || !active || !n_active) return MOE_ERR_NULL;
+  if (!aligned(counts, 4) || !aligned(offsets, 4) || !aligned(active, 4) || !aligned(n_active, 4))
+    return MOE_ERR_ALIGN;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !experts || !topk_idx || !topk_w || !perm || !inv_perm || !y || !out)
+    return MOE_ERR_NULL;
+  if (has_shared != (shared != nullptr) || has_shared != (y_shared != nullptr))
+    return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || (bias && !aligned(bias, 4)) ||
+      !aligned(experts, 16) || (shared && !aligned(shared, 16)) || !aligned(topk_idx, 4) ||
+      !aligned(topk_w, 4) || !aligned(perm, 4) || !aligned(inv_perm, 4) || !aligned(y, 16) ||
+      (y_shared && !aligned(y_shared, 16)) || !aligned(out, 16))
+    return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -261,43 +309,27 @@ moe_status moe_layer_decode(const moe_shape* shape, int32_t T, const void* x, mo
                             int32_t* active, int32_t* n_active, void* y, void* y_shared,
                             void* out, moe_dtype out_dt, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  moe_status st = check_shape(shape);
+  moe_status st = moe::layer_decode_check(shape, T, x, x_dt, w_router, bias, experts, shared,
+                                          topk_idx, topk_w, counts, offsets, perm, inv_perm,
+                                          active, n_active, y, y_shared, out, out_dt);
   if (st != MOE_OK) return st;
-  if ((st = check_tokens(shape, T)) != MOE_OK) return st;
-  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_DTYPE;
-  if (out_dt != MOE_F32 && out_dt != MOE_BF16) return MOE_ERR_DTYPE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   const int E = shape->n_experts, k = shape->top_k, d = shape->d;
-  const bool has_shared = shape->f_shared != 0;
+  if (T == 0)
+    return hip_status(moe::launch_union(0, E, nullptr, counts, offsets, nullptr, nullptr, active,
+                                        n_active, s));
+  if (!workspace) return MOE_ERR_NULL;
+  if (!aligned(workspace, kWorkspaceAlign)) return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_layer_decode_workspace_bytes(shape, T)) return MOE_ERR_WORKSPACE;
   moe::FfnProblem p{};
   p.T = T;
   p.d = d;
   p.f = shape->f;
   p.E = E;
   p.k = k;
-  p.has_shared = has_shared;
+  p.has_shared = shape->f_shared != 0;
   p.x_bf16 = x_dt == MOE_BF16;
   p.block_bytes = moe_expert_bytes(shape->d, shape->f, shape->group);
-  if (T > 0 && !moe::ffn_decode_groups_batch(p, moe::route_parts(T, d, E)))
-    return MOE_ERR_UNSUPPORTED;
-  if (!counts || !offsets || !active || !n_active) return MOE_ERR_NULL;
-  if (!aligned(counts, 4) || !aligned(offsets, 4) || !aligned(active, 4) || !aligned(n_active, 4))
-    return MOE_ERR_ALIGN;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (T == 0)
-    return hip_status(moe::launch_union(0, E, nullptr, counts, offsets, nullptr, nullptr, active,
-                                        n_active, s));
-  if (!x || !w_router || !experts || !topk_idx || !topk_w || !perm || !inv_perm || !y || !out ||
-      !workspace)
-    return MOE_ERR_NULL;
-  if (has_shared != (shared != nullptr) || has_shared != (y_shared != nullptr))
-    return MOE_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(w_router, 16) || (bias && !aligned(bias, 4)) ||
-      !aligned(experts, 16) || (shared && !aligned(shared, 16)) || !aligned(topk_idx, 4) ||
-      !aligned(topk_w, 4) || !aligned(perm, 4) || !aligned(inv_perm, 4) || !aligned(y, 16) ||
-      (y_shared && !aligned(y_shared, 16)) || !aligned(out, 16) ||
-      !aligned(workspace, kWorkspaceAlign))
-    return MOE_ERR_ALIGN;
-  if (workspace_bytes < moe_layer_decode_workspace_bytes(shape, T)) return MOE_ERR_WORKSPACE;
   // workspace: the router's partial sums, then the FFN's intermediate h
   const size_t route_bytes = moe_route_workspace_bytes(shape, T);
   double* part = static_cast<double*>(workspace);

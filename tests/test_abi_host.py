@@ -1,6 +1,6 @@
 """Host-side checks of the C ABI (no GPU needed).
 
-The library must load, export every function include/moe_int4.h declares,
+The library must load, export every function the headers in include/ declare,
 and reject malformed calls before enqueueing anything.  Every call below has
 at least one defect, so none of them reaches a kernel launch: they are safe on
 a machine with or without a GPU.
@@ -15,7 +15,8 @@ import int4_routed_expert_logits_amd as moe
 from int4_routed_expert_logits_amd import _binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe_int4.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 P = 1 << 20          # a 256-byte aligned stand-in address (never dereferenced)
 MIS = P + 4          # misaligned for 16-byte checks
@@ -27,7 +28,7 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
 
@@ -265,3 +266,31 @@ def test_combine_argument_checks(lib):
 def test_binding_names_match_the_c_entry_points():
     for name in B.EXPORTS:
         assert callable(getattr(moe, name)), name
+
+
+def test_layer_decode_static_argument_checks(lib):
+    """The workspace-free decode layer checks its arguments as
+    moe_layer_decode does, before it looks up its static array."""
+    s = ctypes.byref(shp())
+    ok = dict(T=4, x=P, xdt=0, w=P, bias=None, ex=P, sh=None, idx=P, tw=P, cnt=P, off=P, perm=P,
+              inv=P, act=P, na=P, y=P, ys=None, out=P, odt=0)
+
+    def call(shape=s, **kw):
+        a = dict(ok, **kw)
+        return lib.moe_layer_decode_static(shape, a["T"], a["x"], a["xdt"], a["w"], a["bias"],
+                                           a["ex"], a["sh"], a["idx"], a["tw"], a["cnt"], a["off"],
+                                           a["perm"], a["inv"], a["act"], a["na"], a["y"], a["ys"],
+                                           a["out"], a["odt"], None)
+
+    assert lib.moe_layer_decode_static_max_bytes() == 4 << 20
+    assert call(shape=None) == B.MOE_ERR_NULL
+    assert call(T=-1) == B.MOE_ERR_SHAPE
+    assert call(xdt=4) == B.MOE_ERR_DTYPE
+    assert call(T=9) == B.MOE_ERR_UNSUPPORTED
+    assert call(shape=ctypes.byref(shp(group=32))) == B.MOE_ERR_UNSUPPORTED
+    for name in ("x", "w", "ex", "idx", "tw", "cnt", "perm", "y", "out"):
+        assert call(**{name: None}) == B.MOE_ERR_NULL, name
+    assert call(x=MIS) == B.MOE_ERR_ALIGN
+    # every supported shape fits the array: the largest needs ~2.4 MiB
+    big = shp(d=8192, f=8192, E=256, k=8, fs=8192)
+    assert moe.moe_layer_decode_workspace_bytes(big, 8) <= lib.moe_layer_decode_static_max_bytes()
