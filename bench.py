@@ -168,9 +168,11 @@ def main():
 
     # --------------------------------------------------------- timed region
     def timed(step):
-        """ms per step over the timed region, and the number of steps timed."""
+        """Exactly args.steps steps, timed with HIP events on the launch
+        stream (synchronised on both sides); returns (ms per step, steps,
+        per-step us percentiles over >= 64 separately timed graph replays)."""
         steps = args.steps
-        graph = None
+        dist = None
         if not args.no_graph:
             s = torch.cuda.Stream()
             s.wait_stream(stream)
@@ -183,38 +185,62 @@ def main():
             with torch.cuda.graph(graph):
                 for i in range(nb):
                     step(i)
-            reps = max(1, (steps + nb - 1) // nb)
-            steps = reps * nb
+            rest = None
+            if steps % nb:
+                rest = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(rest):
+                    for i in range(steps % nb):
+                        step(i)
             for _ in range(max(1, args.warmup // nb)):
                 graph.replay()
             torch.cuda.synchronize()
-            t_start = time.perf_counter()
-            for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps // nb):
                 graph.replay()
+            if rest is not None:
+                rest.replay()
+            e1.record(stream)
             torch.cuda.synchronize()
-            elapsed = time.perf_counter() - t_start
+            elapsed_ms = e0.elapsed_time(e1)
+            # the distribution: graph replays of nb steps, each event-timed
+            reps = 64
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            for a_, b_ in evs:
+                a_.record(stream)
+                graph.replay()
+                b_.record(stream)
+            torch.cuda.synchronize()
+            per = np.array([a_.elapsed_time(b_) for a_, b_ in evs]) * 1e3 / nb
+            dist = {"us_p10": round(float(np.percentile(per, 10)), 2),
+                    "us_p50": round(float(np.percentile(per, 50)), 2),
+                    "us_p90": round(float(np.percentile(per, 90)), 2),
+                    "replays": reps, "steps_per_replay": nb}
+            del graph, rest
         else:
             for i in range(args.warmup):
                 step(i)
             torch.cuda.synchronize()
-            t_start = time.perf_counter()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
             for i in range(steps):
                 step(i)
+            e1.record(stream)
             torch.cuda.synchronize()
-            elapsed = time.perf_counter() - t_start
-        del graph
-        return elapsed * 1e3 / steps, steps
+            elapsed_ms = e0.elapsed_time(e1)
+        return elapsed_ms / steps, steps, dist
 
     step_bytes = float(np.mean(bytes_per_batch))
     graph = not args.no_graph
-    ms_calls, steps = timed(step_calls)
+    ms_calls, steps, dist_calls = timed(step_calls)
     log(f"decode step, separate calls: {ms_calls * 1e3:.1f} us, "
-        f"{step_bytes / (ms_calls * 1e-3) / 1e9:.0f} GB/s ({'graph' if graph else 'eager'})")
-    ms_per_step = ms_calls
+        f"{step_bytes / (ms_calls * 1e-3) / 1e9:.0f} GB/s ({'graph' if graph else 'eager'}) {dist_calls}")
+    ms_per_step, dist = ms_calls, dist_calls
     if one_call:
-        ms_per_step, steps = timed(step_one_call)
+        ms_per_step, steps, dist = timed(step_one_call)
         log(f"decode step, moe_layer_decode: {ms_per_step * 1e3:.1f} us, "
-            f"{step_bytes / (ms_per_step * 1e-3) / 1e9:.0f} GB/s")
+            f"{step_bytes / (ms_per_step * 1e-3) / 1e9:.0f} GB/s {dist}")
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     result = {
@@ -239,6 +265,9 @@ def main():
                       (", moe_layer_decode (4 launches)" if one_call
                        else ", moe_route_union + moe_expert_ffn + moe_combine (5 launches)"),
             "separate_calls_us_per_step": round(ms_calls * 1e3, 2),
+            "step_us_distribution": dist,
+            "timing": "HIP events on the launch stream around exactly `steps` steps "
+                      "(graph replays of 8 steps plus one of the remainder)",
             "expert_blocks_per_step": round(step_bytes / bb, 3),
             "hbm_pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         },
@@ -258,12 +287,12 @@ def main():
     # ------------------------------------------ decode batch of 8 tokens (one call)
     if T == 1 and not args.no_batch8:
         result["decode_8_tokens"] = bench_decode_batch(args, torch, moe, synth, LayerBuffers,
-                                                       run_layer_decode, sh, experts, shared,
-                                                       w_router, bb, 8)
+                                                       run_layer_decode, run_layer, sh, experts,
+                                                       shared, w_router, bb, 8)
         # a multi-token-prediction verify batch (the pages: 2.2-2.8 tokens per forward)
         result["decode_3_tokens_mtp_verify"] = bench_decode_batch(
-            args, torch, moe, synth, LayerBuffers, run_layer_decode, sh, experts, shared,
-            w_router, bb, 3)
+            args, torch, moe, synth, LayerBuffers, run_layer_decode, run_layer, sh, experts,
+            shared, w_router, bb, 3)
 
     # ----------------------------------------------------- MXFP4 decode FFN
     if T == 1 and not args.no_mxfp4:
@@ -275,8 +304,11 @@ def main():
     # ------------------------------------------------------- measured peaks
     if not args.no_peaks:
         peaks = measured_peaks(torch, dev)
+        peaks.update(stream_read_peak(torch, moe, experts, shared, bufs, bb, dev))
         result["measured_peaks"] = peaks
         result["roofline"]["frac_of_measured_copy"] = round(kern_gbps / peaks["torch_copy_gbps"], 4)
+        result["roofline"]["attainable_read_gbps"] = peaks["stream_read_gbps"]
+        result["roofline"]["frac_of_attainable"] = round(kern_gbps / peaks["stream_read_gbps"], 4)
 
     # --------------------------------------------------------------- prefill
     if not args.no_prefill:
@@ -305,13 +337,16 @@ def main():
     return 0
 
 
-def bench_decode_batch(args, torch, moe, synth, LayerBuffers, run_layer_decode, sh, experts,
-                       shared, w_router, bb, T):
+def bench_decode_batch(args, torch, moe, synth, LayerBuffers, run_layer_decode, run_layer, sh,
+                       experts, shared, w_router, bb, T):
     """Decode steps of T tokens (8: the 19 MB-expert layer's second decode
-    batch size; 3: a multi-token-prediction verify batch) through
-    moe_layer_decode, captured in a HIP graph over the rotating
-    layer copies; expert bytes = (distinct routed experts + shared) x block."""
+    batch size; 3: a multi-token-prediction verify batch), each form of the
+    step -- the one call moe_layer_decode and the separate calls
+    moe_route_union + moe_expert_ffn + moe_combine -- captured in a HIP graph
+    over the rotating layer copies and timed with HIP events; expert bytes =
+    (distinct routed experts + shared) x block."""
     dev = w_router.device
+    stream = torch.cuda.current_stream()
     nb = len(experts)
     xs, bufs = [], []
     for b in range(nb):
@@ -319,48 +354,56 @@ def bench_decode_batch(args, torch, moe, synth, LayerBuffers, run_layer_decode, 
         xs.append(torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16))
         bufs.append(LayerBuffers.allocate(sh, T, moe.MOE_PATH_DECODE_F32))
 
-    def step(i):
-        j = i % nb
-        run_layer_decode(xs[j], w_router, None, experts[j], shared[j], bufs[j])
+    def time_form(run):
+        def step(i):
+            j = i % nb
+            run(xs[j], w_router, None, experts[j], shared[j], bufs[j])
 
-    for i in range(nb):
-        step(i)
-    torch.cuda.synchronize()
+        for i in range(nb):
+            step(i)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            for i in range(nb):
+                step(i)
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(nb):
+                step(i)
+        reps = max(8, args.steps // nb)
+        for _ in range(max(1, args.warmup // nb)):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del graph
+        return e0.elapsed_time(e1) / (reps * nb)
+
+    ms = time_form(run_layer_decode)
+    ms_sep = time_form(run_layer)
     blocks = [int(b.n_active.item()) + 1 for b in bufs]
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for i in range(nb):
-            step(i)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(nb):
-            step(i)
-    reps = max(1, args.steps // nb)
-    for _ in range(max(1, args.warmup // nb)):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        graph.replay()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / (reps * nb)
-    del graph
     step_bytes = float(np.mean(blocks)) * bb
     gbps = step_bytes / (ms * 1e-3) / 1e9
-    log(f"decode step, {T} tokens, moe_layer_decode: {ms * 1e3:.1f} us, {gbps:.0f} GB/s "
-        f"({np.mean(blocks):.1f} expert blocks per step), {T / (ms * 1e-3):.0f} tokens/s")
+    log(f"decode step, {T} tokens: moe_layer_decode {ms * 1e3:.1f} us, separate calls "
+        f"{ms_sep * 1e3:.1f} us; {gbps:.0f} GB/s ({np.mean(blocks):.1f} expert blocks per step), "
+        f"{T / (ms * 1e-3):.0f} tokens/s")
     return {
         "value": round(gbps, 2),
         "unit": "GB/s",
         "us_per_step": round(ms * 1e3, 2),
+        "separate_calls_us_per_step": round(ms_sep * 1e3, 2),
         "tokens_per_s": round(T / (ms * 1e-3), 1),
         "expert_blocks_per_step": round(float(np.mean(blocks)), 2),
         "hbm_pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "workload": f"decode, {T} tokens per step, same layer, no router bias, hip graph over "
-                    f"{nb} layer copies",
+                    f"{nb} layer copies; value from moe_layer_decode",
     }
 
 
@@ -473,6 +516,48 @@ def measured_peaks(torch, dev, reps=10):
                "float32 (a library reduction, below what a plain streaming read reaches), "
                "torch.matmul 8192x8192x8192 bf16 (vendor BLAS); 10 timed repetitions each",
     }
+
+
+def stream_read_peak(torch, moe, experts, shared, bufs, bb, dev, rounds=8):
+    """What a plain read-only kernel attains on the decode step's own bytes:
+    moe_measure_stream_read over the shared block and the routed blocks of
+    each token batch (the 180.5 MB the decode FFN streams), rotating over the
+    layer copies as the timed steps do, for a few grid sizes; the best
+    (event-timed, mean over the rounds) is the attainable rate."""
+    nb = len(bufs)
+    sets = []
+    for j in range(nb):
+        act = bufs[j].active.cpu().numpy()
+        ids = [int(e) for e in act if e >= 0]
+        sets.append([shared[j % len(shared)].data_ptr()] +
+                    [experts[j % len(experts)].data_ptr() + e * bb for e in ids])
+    sink = torch.empty((1 << 16,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    best, table = 0.0, {}
+    for wg in (2304, 4608, 9216, 18432, 36864):
+        def run(j):
+            moe.moe_measure_stream_read(sets[j], bb, wg, sink)
+        for j in range(nb):
+            run(j)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(rounds * nb)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            run(i % nb)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+        nbytes = np.array([len(sets[i % nb]) * bb for i in range(len(evs))], dtype=np.float64)
+        gbps = float(nbytes.sum() / (us.sum() * 1e-6) / 1e9)
+        table[wg] = round(gbps, 1)
+        best = max(best, gbps)
+    log(f"measured: plain read of the decode step's expert blocks {best:.0f} GB/s "
+        f"(by workgroups: {table})")
+    return {"stream_read_gbps": round(best, 1), "stream_read_by_workgroups": table,
+            "stream_read_how": "moe_measure_stream_read over the shared + routed expert blocks "
+                               "of each 1-token step (9 x 20,054,016 B), layer copies rotated, "
+                               "event-timed; best grid of 2304..36864 workgroups"}
 
 
 def bench_quantizer(torch, moe, dev, reps=20):
@@ -762,22 +847,50 @@ def load_traffic(which="decode", fmt="int4"):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(L, bb):
-    """The float64 oracle, as it stands, on the host cores: one 1-token decode
-    step of the same layer (routing, grouping, 8 routed + 1 shared expert,
-    combine), repeated until ~10 s of CPU work."""
-    import oracle
+def cpu_info():
+    """Host CPU as the oracle sees it: logical CPUs this process may use, all
+    logical CPUs, and the model name."""
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return usable, os.cpu_count(), model
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        return None
+
+
+def cpu_baseline(L, bb):
+    """The float64 oracle, as it stands, on the host cores.
+    Decode (the headline unit): whole 1-token decode steps of the same layer
+    (routing, grouping, 8 routed + 1 shared expert, combine), repeated until
+    ~10 s of CPU work.  Prefill: the 2048-token Zipf batch's routing and
+    grouping in full, then the oracle's expert FFN on a sample of 16 of its
+    active experts spread over the row-count range (decode the block, SwiGLU
+    over the expert's rows); the whole batch's time is extrapolated as
+    (active experts) x (mean block decode time) + (all rows) x (SwiGLU time
+    per row of the sample)."""
+    import oracle
+    import synth
+    usable, logical, model = cpu_info()
+    threads = blas_threads() or usable
     sh = L.shape
     reps = 0
     elapsed = 0.0
     blocks = 0
     while elapsed < 10.0 and reps < 8:
-        _, xf = __import__("synth").make_tokens(4, 1, batch=100 + reps)
+        _, xf = synth.make_tokens(4, 1, batch=100 + reps)
         t = time.perf_counter()
         res = oracle.moe_layer(xf, L.w_router, None, L.experts, L.shared, sh.d, sh.f,
                                sh.n_experts, sh.top_k)
@@ -785,10 +898,49 @@ def cpu_baseline(L, bb):
         blocks += int(res["n_active"][0]) + 1
         reps += 1
     gbps = blocks * bb / elapsed / 1e9
-    log(f"cpu oracle: {reps} decode steps in {elapsed:.1f}s = {gbps:.4f} GB/s ({threads} threads)")
+    log(f"cpu oracle: {reps} decode steps in {elapsed:.1f}s = {gbps:.4f} GB/s ({threads} BLAS "
+        f"threads, {usable} usable CPUs, {model})")
+    # prefill sample
+    bias = synth.make_layer(5, experts=[]).bias
+    _, xf = synth.make_tokens(5, 2048)
+    t = time.perf_counter()
+    idx, w, _ = oracle.route(xf, L.w_router, bias, sh.top_k)
+    counts, offsets, perm, inv, active, n_active = oracle.batch_union(idx, sh.n_experts)
+    t_route = time.perf_counter() - t
+    act = [int(e) for e in active[: int(n_active[0])]]
+    order = sorted(act, key=lambda e: int(counts[e]))
+    pick = [order[i * (len(order) - 1) // 15] for i in range(16)]
+    t_dec = t_mm = 0.0
+    rows = 0
+    x64 = np.asarray(xf, dtype=np.float64)
+    for e in pick:
+        t0 = time.perf_counter()
+        wg, wu, wd = oracle.expert_weights(L.experts[e], sh.d, sh.f)
+        t1 = time.perf_counter()
+        toks = np.asarray(perm[offsets[e]:offsets[e + 1]], dtype=np.int64) // sh.top_k
+        oracle.swiglu(x64[toks], wg, wu, wd)
+        t2 = time.perf_counter()
+        t_dec += t1 - t0
+        t_mm += t2 - t1
+        rows += len(toks)
+        del wg, wu, wd
+    all_rows = 2048 * sh.top_k + 2048  # routed rows + the shared expert's
+    est = t_route + (len(act) + 1) * t_dec / len(pick) + all_rows * t_mm / rows
+    log(f"cpu oracle prefill: {len(pick)} of {len(act)} experts ({rows} rows) in "
+        f"{t_dec + t_mm:.1f}s; whole 2048-token batch extrapolated to {est:.0f}s = "
+        f"{2048 / est:.1f} tokens/s")
     return {"value": round(gbps, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} one-token decode steps of the same layer ({blocks} expert blocks), "
-                      f"float64 numpy oracle, {elapsed:.1f} s"}
+                      f"float64 numpy oracle, {elapsed:.1f} s",
+            "cpu_model": model, "usable_cpus": usable, "logical_cpus": logical,
+            "cores_note": "cores = threads of numpy's BLAS pool (the oracle's matrix products); "
+                          "its element-wise decoding runs on one thread",
+            "prefill": {"value": round(2048 / est, 2), "unit": "tokens/s", "extrapolated": True,
+                        "seconds_estimated": round(est, 1),
+                        "sample": f"routing and grouping of the 2048-token Zipf batch in full "
+                                  f"({t_route:.1f} s); the expert FFN of {len(pick)} of its "
+                                  f"{len(act)} active experts ({rows} rows) in "
+                                  f"{t_dec + t_mm:.1f} s, extrapolated by block count and rows"}}
 
 
 if __name__ == "__main__":

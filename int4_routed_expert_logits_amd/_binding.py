@@ -31,7 +31,7 @@ EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_quantize", "moe_route_wo
            "moe_layer_decode", "moe_layer_decode_static", "moe_layer_decode_static_max_bytes",
            "moe_cache_create", "moe_cache_destroy", "moe_cache_pin",
            "moe_cache_plan", "moe_cache_stats", "moe_cache_last_fetch", "moe_cache_workspace_bytes",
-           "moe_cache_layer_decode", "moe_status_str")
+           "moe_cache_layer_decode", "moe_status_str", "moe_measure_stream_read")
 
 
 class Shape(ctypes.Structure):
@@ -95,6 +95,9 @@ def load():
                                              c_void_p, c_void_p] + [c_void_p] * 11 +
                                             [c_int32, c_void_p])
     lib.moe_layer_decode_static.restype = c_int32
+    lib.moe_measure_stream_read.argtypes = [c_void_p, c_int32, c_size_t, c_int32, c_void_p,
+                                            c_void_p]
+    lib.moe_measure_stream_read.restype = c_int32
     lib.moe_layer_decode_static_max_bytes.argtypes = []
     lib.moe_layer_decode_static_max_bytes.restype = c_size_t
     vp = c_void_p
@@ -285,6 +288,15 @@ def moe_layer_decode_static(shape, x, w_router, bias, experts, shared, topk_idx,
         _ptr(experts), _ptr(shared), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
         _ptr(perm), _ptr(inv_perm), _ptr(active), _ptr(n_active), _ptr(y), _ptr(y_shared),
         _ptr(out), _dtype(out), _stream(stream)))
+
+
+def moe_measure_stream_read(block_ptrs, block_bytes: int, workgroups: int, sink, stream=None):
+    """Calibration read of the device blocks at block_ptrs (ints) once
+    (include/moe_int4_measure.h); sink: a device int32 tensor of at least
+    `workgroups` entries."""
+    arr = (c_void_p * len(block_ptrs))(*block_ptrs)
+    _check("moe_measure_stream_read", load().moe_measure_stream_read(
+        arr, len(block_ptrs), block_bytes, workgroups, _ptr(sink), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

@@ -596,27 +596,28 @@ TOL_PREFILL = 2e-2
 
 
 # An ideal kernel that keeps h and y in bf16 (the prefill path's storage
-# format) already reaches 1.6-2.5e-2 * rms at the worst element of these
-# layers (float64 simulation), so the strict ratio is printed and held to a
-# sanity cap, and the pass/fail bound is element-wise.
-STRICT_CAP = 3e-2
+# format) already reaches 1.6-2.5e-2 * rms at the worst element of the int4
+# parity layers (float64 simulation), above the 2e-2 * rms of the
+# arithmetic, so the bound is element-wise with the format's own rounding;
+# the strict max|err| / rms is printed beside it.
 
 
-def prefill_err(got, ref, name="", check=True):
+def prefill_err(got, ref, name=""):
     """Largest error of a bf16 prefill output in units of the bound actually
     checked, element by element: 2e-2 * rms(ref) for the arithmetic plus
     half an ulp of the bf16 result at |ref| (at most 2^-8 * |ref|: outputs
     here reach ~6.5 rms, where that rounding alone is ~2.5e-2 rms); <= 1
-    passes.  Also prints the strict max|err| / rms(ref) and, with check,
-    asserts it stays under STRICT_CAP."""
+    passes.  Prints the strict max|err| / rms(ref) and asserts the strict
+    form of the same bound: max|err| <= 2e-2 * rms + 2^-8 * max|ref|."""
     ref = np.asarray(ref, dtype=np.float64)
     got = np.asarray(got, dtype=np.float64)
     rms = float(np.sqrt(np.mean(ref ** 2)))
     strict = float(np.max(np.abs(got - ref))) / rms
     bound = float(np.max(np.abs(got - ref) / (TOL_PREFILL * rms + 2.0 ** -8 * np.abs(ref))))
-    say(f"  {name}: strict max|err|/rms = {strict:.4f}, element-wise bound ratio = {bound:.3f}")
-    if check:
-        assert strict <= STRICT_CAP, f"{name}: strict error {strict:.4f} * rms"
+    cap = TOL_PREFILL + 2.0 ** -8 * float(np.max(np.abs(ref))) / rms
+    say(f"  {name}: strict max|err|/rms = {strict:.4f} (strict bound {cap:.4f}), "
+        f"element-wise bound ratio = {bound:.3f}")
+    assert strict <= cap, f"{name}: strict error {strict:.4f} * rms > {cap:.4f}"
     return bound
 # (6, 512) and (6, 97): 128-row tiles (full and partial), odd group counts
 # along d and f, partial column tiles, an unrouted expert
