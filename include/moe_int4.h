@@ -19,7 +19,7 @@
  *   moe_route_union moe_route and moe_union in one call (one launch fewer
  *                   for decode batches)
  *   moe_layer_decode the whole layer (route, union, expert FFN, combine) for
- *                   a decode batch of at most 8 tokens, in four launches
+ *                   a decode batch of at most 8 tokens in one call
  *   moe_cache_*     a per-layer cache of experts in HBM (LRU, pinned experts)
  *                   whose misses stream from pinned host memory while the
  *                   resident experts compute
@@ -301,9 +301,12 @@ size_t moe_layer_decode_workspace_bytes(const moe_shape* shape, int32_t T);
  * the same outputs, bit for bit, as those three calls in sequence (pages:
  * zhichai.net, section on MTP speculative decoding -- the main model checks
  * 2-3 drafted tokens per forward pass, and draft and check must compute the
- * same function).  The gate/up kernel derives the top-k and the grouping of
- * the batch itself from the router's float64 partial sums, so a step is four
- * launches (router logits, gate/up, down, combine) instead of five.
+ * same function).  For one token the gate/up kernel derives the top-k and
+ * the grouping itself from the router's float64 partial sums, so the step is
+ * four launches (router logits, gate/up, down, combine) instead of five;
+ * from two tokens on, where each gate/up workgroup redoing the top-k of the
+ * whole batch costs more than the launch it saves, the call runs the
+ * separate calls' kernels (route + union, gate/up, down, combine).
  *  arguments as in the three calls; every output of theirs is written:
  *  topk_idx, topk_w, counts, offsets, perm, inv_perm, active, n_active, y and
  *  y_shared (float32), and out (out_dt).

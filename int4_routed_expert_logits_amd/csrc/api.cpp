@@ -16,6 +16,12 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int64_t kMaxSlots = int64_t(1) << 24;  // T * top_k
 constexpr size_t kWorkspaceAlign = 256;
+// moe_layer_decode: batches of at most this many tokens let every gate/up
+// workgroup derive the top-k and the grouping itself (a launch fewer); larger
+// ones group once.  Measured on the d=6144, f=2048 layer (HIP graphs): 1
+// token 50.5 us against 52.3 us; 2 tokens 90.4 us against 82.5 us; 8 tokens
+// 330 us against 240 us.
+constexpr int kLayerDecodePrologueMaxT = 1;
 constexpr int kMaxQuantK = 65536;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -343,10 +349,20 @@ moe_status moe_layer_decode(const moe_shape* shape, int32_t T, const void* x, mo
   p.y = y;
   p.y_shared = y_shared;
   p.workspace = static_cast<uint8_t*>(workspace) + route_bytes;
-  const moe::RouteGroup rg{part, moe::route_parts(T, d, E), bias, topk_idx, topk_w,
-                           moe::UnionOut{counts, offsets, perm, inv_perm, active, n_active}};
-  hipError_t err = moe::launch_router_logits(T, d, E, x, x_dt == MOE_BF16, w_router, part, s);
-  if (err == hipSuccess) err = moe::launch_ffn_decode_grouping(p, rg, s);
+  const moe::UnionOut u{counts, offsets, perm, inv_perm, active, n_active};
+  hipError_t err;
+  if (T <= kLayerDecodePrologueMaxT) {
+    // router logits, then gate/up workgroups that take the top-k and the
+    // grouping themselves (one launch fewer)
+    const moe::RouteGroup rg{part, moe::route_parts(T, d, E), bias, topk_idx, topk_w, u};
+    err = moe::launch_router_logits(T, d, E, x, x_dt == MOE_BF16, w_router, part, s);
+    if (err == hipSuccess) err = moe::launch_ffn_decode_grouping(p, rg, s);
+  } else {
+    // the separate calls' kernels: routing and grouping once for the batch
+    err = moe::launch_route_union(T, d, E, k, x, x_dt == MOE_BF16, w_router, bias, part,
+                                  topk_idx, topk_w, u, s);
+    if (err == hipSuccess) err = moe::launch_ffn_decode(p, s);
+  }
   if (err == hipSuccess)
     err = moe::launch_combine(T, d, k, y, y_shared, false, inv_perm, topk_w, out,
                               out_dt == MOE_BF16, s);

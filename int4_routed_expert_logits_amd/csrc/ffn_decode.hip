@@ -155,6 +155,7 @@ __device__ __forceinline__ int row_of(const FfnArgs& g, const Slot& sl, int m) {
 }
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer access
+constexpr int kLoadNonTemporal = 2;     // buffer-load cache policy: streaming (nt)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
@@ -187,7 +188,10 @@ __device__ __forceinline__ void load_step(const TileRes<NM>& res, int c, int cb,
     const int cc = max(min(c + i, ce - 1), cb);
 #pragma unroll
     for (int mat = 0; mat < NM; ++mat) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(res.q[mat], cc * 1024 + rt * 16, 0, 0);
+      // non-temporal: every code is read once per step (measured 4% faster
+      // on the 1-token step of the ~19 MB-expert layer than plain loads)
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(res.q[mat], cc * 1024 + rt * 16, 0,
+                                                           kLoadNonTemporal);
       d.q[mat][i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }

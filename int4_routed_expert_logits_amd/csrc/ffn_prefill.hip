@@ -406,38 +406,22 @@ __device__ __forceinline__ void small_math(const uint32_t* abuf, const SmallCode
                                                        0, 0, 0);
   }
   if constexpr (MX) {
-    // E8M0 byte of this lane's column in subtile sb of matrix mat, block b
-    // of the group (`sc` points at the lane's own block; blocks are 64 bytes
-    // apart)
-    const int own = kq >> 1;
-    auto ebyte = [&](int mat, int sb, int b) -> uint32_t {
-      return sc[2 * mat * 64 * NSUB + (sb >> 2) * 128 + (sb & 3) * 16 + (b - own) * 64];
-    };
-    // These tiles are bound by the weight stream, so the scale is not folded
-    // into the conversion: the elements convert unscaled (exact), each block
-    // of 32 gets its own MFMA chain (lanes of the other block pass zero
-    // codes), and the block's scale 2^(E - 127) multiplies the chain's sum in
-    // float32 -- exact for every E8M0 byte, as on the decode path.  Output
-    // lane (col, kq) holds column col: it applies that column's scale of
-    // each block.
+    // power-of-two scales folded into the conversion (every scale byte of
+    // the tile lies in 2 .. 252: prefill_small sends other tiles to
+    // small_tile_wide): the products accumulate straight into acc
 #pragma unroll
     for (int mat = 0; mat < NM; ++mat) {
 #pragma unroll
       for (int sb = 0; sb < NSUB; ++sb) {
+        const float sv = e8m0_to_f32(sc[2 * mat * 64 * NSUB + (sb >> 2) * 128 + (sb & 3) * 16]);
+        const bf16x8_t b0 = dequant_word_mx(st.q[mat][sb].x, sv);
+        const bf16x8_t b1 = dequant_word_mx(st.q[mat][sb].y, sv);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const float sv = e8m0_to_f32(ebyte(mat, sb, b));
-          const bf16x8_t b0 = dequant_word_mx(own == b ? st.q[mat][sb].x : 0u, 1.0f);
-          const bf16x8_t b1 = dequant_word_mx(own == b ? st.q[mat][sb].y : 0u, 1.0f);
-#pragma unroll
-          for (int rb = 0; rb < kSmallRB; ++rb) {
-            f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][0]), b0,
-                                                                f32x4_t{}, 0, 0, 0);
-            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][1]), b1, p, 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[rb][mat][sb][e] = fmaf(sv, p[e], acc[rb][mat][sb][e]);
-          }
-          __builtin_amdgcn_sched_barrier(0);  // one block's chains at a time
+        for (int rb = 0; rb < kSmallRB; ++rb) {
+          acc[rb][mat][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][0]), b0,
+                                                                     acc[rb][mat][sb], 0, 0, 0);
+          acc[rb][mat][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][1]), b1,
+                                                                     acc[rb][mat][sb], 0, 0, 0);
         }
       }
     }
@@ -479,6 +463,79 @@ __device__ __forceinline__ void small_a_store(uint32_t* abuf, const uint4& raw, 
 }
 
 constexpr int kSmallBufWords = 32 * kALdS / 2;
+
+// MXFP4 32-row tiles with a scale byte outside 2 .. 252 (an E2M1 value
+// times 2^(E - 127) that is not a normal bf16, or E = 255), a case real
+// checkpoints do not produce: one group at a time, without the ring of
+// codes in flight.  Each lane loads word kq of both 32-column chunks of the
+// group, so MFMA step b covers block b alone; the elements convert unscaled
+// (exact) and the block's scale multiplies the step's sum in float32, as on
+// the decode path.  Entered before anything of the fast path is live, so its
+// registers do not add to the fast path's.
+// sbase[mat]: the matrix's E8M0 bytes; tile0 / ntiles: the wavefront's first
+// packed 64-row tile and the matrix's tile count.
+template <int NM, int NSUB>
+__device__ __forceinline__ void small_tile_wide(uint32_t* abuf, const uint16_t* srcrow,
+                                                uint32_t akeep, int groups, int kq, int col,
+                                                const __amdgpu_buffer_rsrc_t (&rq)[NM], int rt0,
+                                                const uint8_t* const (&sbase)[2], int tile0,
+                                                int ntiles, bool active,
+                                                f32x4_t (&acc)[kSmallRB][NM][NSUB]) {
+  for (int grp = 0; grp < groups; ++grp) {
+    const uint4 araw = small_a_load(srcrow, grp);
+    uint2 q[NM][NSUB];
+    float sv[NM][NSUB][2];
+    if (active) {
+#pragma unroll
+      for (int mat = 0; mat < NM; ++mat) {
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+          const int rt = rt0 + sb * 16;
+          const int base = (rt >> 6) * 32 * (groups * 64) + (rt & 63) * 16 + kq * 4;
+          q[mat][sb] = make_uint2(
+              __builtin_amdgcn_raw_buffer_load_b32(rq[mat], base + (2 * grp) * 1024, 0, 0),
+              __builtin_amdgcn_raw_buffer_load_b32(rq[mat], base + (2 * grp + 1) * 1024, 0, 0));
+          const int tg = min(tile0 + (rt >> 6), ntiles - 1);
+          const uint8_t* e = sbase[mat] + static_cast<size_t>(tg) * groups * 128 + 2 * grp * 64 +
+                             (rt & 63);
+          sv[mat][sb][0] = e8m0_to_f32(e[0]);
+          sv[mat][sb][1] = e8m0_to_f32(e[64]);
+        }
+      }
+    }
+    __syncthreads();  // the previous group's A has been read
+    small_a_store(abuf, araw, akeep);
+    __syncthreads();
+    if (!active) continue;
+    uint4 a[kSmallRB][2];
+#pragma unroll
+    for (int rb = 0; rb < kSmallRB; ++rb) {
+      const int r = rb * 16 + col;
+      a[rb][0] = *reinterpret_cast<const uint4*>(abuf + (r * kALdS + kq * 8) / 2);
+      a[rb][1] = *reinterpret_cast<const uint4*>(abuf + (r * kALdS + 32 + kq * 8) / 2);
+    }
+#pragma unroll
+    for (int mat = 0; mat < NM; ++mat) {
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) {
+        const bf16x8_t w0 = dequant_word_mx(q[mat][sb].x, 1.0f);
+        const bf16x8_t w1 = dequant_word_mx(q[mat][sb].y, 1.0f);
+#pragma unroll
+        for (int rb = 0; rb < kSmallRB; ++rb) {
+          const f32x4_t p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][0]), w0,
+                                                                     f32x4_t{}, 0, 0, 0);
+          const f32x4_t p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb][1]), w1,
+                                                                     f32x4_t{}, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[rb][mat][sb][i] = fmaf(sv[mat][sb][0], p0[i], acc[rb][mat][sb][i]);
+            acc[rb][mat][sb][i] = fmaf(sv[mat][sb][1], p1[i], acc[rb][mat][sb][i]);
+          }
+        }
+      }
+    }
+  }
+}
 
 template <int NM, int NSUB, bool DOWN, bool MX>
 __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
@@ -551,6 +608,21 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
     for (int mat = 0; mat < NM; ++mat)
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) acc[rb][mat][s] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // MX: a tile with a scale byte outside 2 .. 252 takes small_tile_wide (this
+  // thread checks the scale pieces it would stage in every pass)
+  bool wide = false;
+  if constexpr (MX) {
+    for (int ps = 0; ps < (groups + kRing - 1) / kRing; ++ps) {
+      const uint4 v = small_scale_load(ssrc, ps, groups);
+      wide |= mx_wide(v.x) | mx_wide(v.y) | mx_wide(v.z) | mx_wide(v.w);
+    }
+    wide = __syncthreads_or(wide);
+  }
+  if (MX && wide) {
+    const uint8_t* const sbase[2] = {sl.blk + soff[0], sl.blk + soff[NM - 1]};
+    small_tile_wide<NM, NSUB>(abufs[0], srcrow, akeep, groups, kq, col, rq, rt0, sbase, nb / 64,
+                              N / 64, active, acc);
+  } else {
   // Loads are issued in the order they are consumed (scales of pass 0, A of
   // groups 0..2, codes of groups 0..kRing-1, scales of pass 1), and in the
   // loop A of group grp+3 goes out ahead of the codes of group grp+kRing.
@@ -605,6 +677,7 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
       }
     }
   }
+  }  // fast path
   if (!active) return;
   // lane (col, kq) holds rows 4*kq + e of each block, column col of every subtile
 #pragma unroll
