@@ -54,6 +54,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 32;        // rows per small M-tile
 constexpr int kBigM = 128;     // rows per big M-tile
@@ -729,9 +731,9 @@ struct Big {
 // Global loads of group grp (clamped to the last group): this thread's 32 A
 // columns of its row and kPieces 16-byte pieces of the codes.  Every address
 // is valid -- rows past the slot read a row of the slot, tiles past the end
-// of the matrix read its last tile -- and big_store masks those, so the loads
-// are unconditional and a wait for one group's loads leaves the next group's
-// in flight.
+// of the matrix read its last tile, and the outputs those give are never
+// stored -- so the loads are unconditional and a wait for one group's loads
+// leaves the next group's in flight.
 //
 // Code piece p = t + 256 i of a group (i < kPieces) is row `row` (of 64) of
 // half h (32 columns) of packed tile tt of matrix mat, with
@@ -750,16 +752,16 @@ __device__ __forceinline__ void big_piece(int i, int& mat, int& tt, int& h, int&
 template <int NM, int NS, bool MX>
 __device__ __forceinline__ void big_load(const uint16_t* rowp, const uint2* sump, int ahalf,
                                          int grp, int groups, int K, int ntv,
-                                         const uint8_t* const (&qbase)[NM], uint4 (&ra)[4],
-                                         uint2& rs, uint4 (&rb)[Big<NM, NS>::kPieces]) {
+                                         const uint8_t* const (&qbase)[NM], u32x4_t (&ra)[4],
+                                         u32x2_t& rs, u32x4_t (&rb)[Big<NM, NS>::kPieces]) {
   grp = min(grp, groups - 1);
   if constexpr (MX)
-    rs = make_uint2(0u, 0u);  // (no offset to correct)
+    rs = u32x2_t{0u, 0u};  // (no offset to correct)
   else
-    rs = sump[grp];
+    rs = *reinterpret_cast<const u32x2_t*>(sump + grp);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    ra[j] = *reinterpret_cast<const uint4*>(rowp + grp * 64 + ahalf * 32 + j * 8);
+    ra[j] = *reinterpret_cast<const u32x4_t*>(rowp + grp * 64 + ahalf * 32 + j * 8);
 #pragma unroll
   for (int i = 0; i < Big<NM, NS>::kPieces; ++i) {
     int mat, tt, h, row;
@@ -769,35 +771,31 @@ __device__ __forceinline__ void big_load(const uint16_t* rowp, const uint2* sump
 #pragma unroll
     for (int mm = 1; mm < NM; ++mm)
       if (mat == mm) src = qbase[mm];
-    rb[i] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(tt) * 32 * K +
-                                            static_cast<size_t>(2 * grp + h) * 1024 + row * 16);
+    rb[i] = *reinterpret_cast<const u32x4_t*>(src + static_cast<size_t>(tt) * 32 * K +
+                                              static_cast<size_t>(2 * grp + h) * 1024 + row * 16);
   }
 }
 
-__device__ __forceinline__ uint4 masked(const uint4& v, uint32_t keep) {
-  return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
-}
-
-// The loaded group into LDS buffer `buf`: A rows (zero past the slot), then
-// the codes (zero past the matrix).
+// The loaded group into LDS buffer `buf`: A rows, then the codes.
 template <int NM, int NS, bool MX>
-__device__ __forceinline__ void big_store(uint32_t* buf, int arow, int ahalf, const uint4 (&ra)[4],
-                                          const uint2& rs, const uint4 (&rb)[Big<NM, NS>::kPieces],
-                                          uint32_t akeep, int ntv) {
+__device__ __forceinline__ void big_store(uint32_t* buf, int arow, int ahalf, const u32x4_t (&ra)[4],
+                                          const u32x2_t& rs, const u32x4_t (&rb)[Big<NM, NS>::kPieces]) {
   using C = Big<NM, NS>;
-  uint4* a = reinterpret_cast<uint4*>(buf + (arow * kALd + ahalf * 32) / 2);
+  // Nothing is masked: rows past the slot hold a copy of a row of the slot
+  // and columns past the matrix a copy of its last tile, finite values whose
+  // outputs (each output row and column depends on its own A row and B
+  // column only) are never stored.
+  u32x4_t* a = reinterpret_cast<u32x4_t*>(buf + (arow * kALd + ahalf * 32) / 2);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) a[j] = masked(ra[j], akeep);
+  for (int j = 0; j < 4; ++j) a[j] = ra[j];
   // the row's sum parts as the first three elements of an 8-element A operand
   if (!MX && ahalf == 0)
-    reinterpret_cast<uint4*>(buf + C::kAWords + C::kBWords)[arow] =
-        make_uint4(rs.x & akeep, rs.y & akeep, 0u, 0u);
+    reinterpret_cast<u32x4_t*>(buf + C::kAWords + C::kBWords)[arow] = u32x4_t{rs.x, rs.y, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < C::kPieces; ++i) {
     int mat, tt, h, row;
     big_piece<NM, NS>(i, mat, tt, h, row);
-    reinterpret_cast<uint4*>(buf + C::kAWords)[(mat * 2 + h) * C::kWgCols + tt * 64 + row] =
-        masked(rb[i], tt < ntv ? 0xFFFFFFFFu : 0u);
+    reinterpret_cast<u32x4_t*>(buf + C::kAWords)[(mat * 2 + h) * C::kWgCols + tt * 64 + row] = rb[i];
   }
 }
 
@@ -960,11 +958,10 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   }
   const int t = threadIdx.x, arow = t >> 1, ahalf = t & 1;
   const int m = m0 + arow;
-  const uint32_t akeep = m < sl.M ? 0xFFFFFFFFu : 0u;
   const uint16_t* rowp;
   const uint2* sump;
   {
-    const int mr = m < sl.M ? m : m0;  // rows past the slot read the first row (masked)
+    const int mr = m < sl.M ? m : m0;  // rows past the slot read its first row (never stored)
     if (DOWN) {
       const size_t hr = row_of(g, sl, mr);
       rowp = g.h + hr * g.f;
@@ -988,11 +985,11 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
     constexpr bool W = decltype(wide_tag)::value;
     // Two register sets: group g+1 is stored to LDS while g+2 is in flight,
     // so every group's loads have two groups of math to land.
-    uint4 ra[2][4], rb[2][C::kPieces];
-    uint2 rs[2];
+    u32x4_t ra[2][4], rb[2][C::kPieces];
+    u32x2_t rs[2];
     big_load<NM, NS, MX>(rowp, sump, ahalf, 0, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
     big_load<NM, NS, MX>(rowp, sump, ahalf, 1, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
-    big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
+    big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0]);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1006,12 +1003,12 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
       // group g0 is in buf0, group g0 + 1 in register set 1
       big_load<NM, NS, MX>(rowp, sump, ahalf, g0 + 2, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
       big_math<NM, NS, MX, W>(buf0, zero16, sc, groups, g0, wm, wn, col, half, acc);
-      big_store<NM, NS, MX>(buf1, arow, ahalf, ra[1], rs[1], rb[1], akeep, ntv);
+      big_store<NM, NS, MX>(buf1, arow, ahalf, ra[1], rs[1], rb[1]);
       __syncthreads();
       if (g0 + 1 < groups) {
         big_load<NM, NS, MX>(rowp, sump, ahalf, g0 + 3, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
         big_math<NM, NS, MX, W>(buf1, zero16, sc, groups, g0 + 1, wm, wn, col, half, acc);
-        big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0], akeep, ntv);
+        big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0]);
         __syncthreads();
       }
     }
