@@ -63,7 +63,6 @@ constexpr int kBigMinRows = 96;  // fewest rows a big tile is used for
 constexpr uint32_t kMask = 0x000F000Fu;
 constexpr uint32_t kMagic = 0x43004300u;
 constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kMaxLds = 160 * 1024;
 // E8M0 exponents for which every E2M1 value times 2^(E - 127) is a normal
 // bf16 (0.5 * 2^-125 .. 6 * 2^125), so the scale can be folded into the
 // element conversion exactly; groups with other exponents take the
@@ -272,9 +271,6 @@ __device__ __forceinline__ bf16x8_t dequant_word_mx(uint32_t w, float sv) {
   return as_bf16x8(b);
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& q, int j) {
-  return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-}
 
 // B operand holding -136 in every element (bf16 0xC308).  With codes dequantised
 // to 136 + q, the product with it gives the -136 * sum(A) that turns
@@ -705,99 +701,17 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// 128-row tiles: A and the codes staged in LDS (double-buffered per 64-column
-// scale group) and shared by the 4 wavefronts, 2 along M x 2 along N; each
-// wavefront computes 64 rows x 32*NS columns of each of NM matrices.
+// 128-row tiles: a workgroup of 4 wavefronts, 2 along M x 2 along N, each
+// computing 64 rows x 32 * NS columns of each of NM matrices with
+// v_mfma_f32_32x32x16_bf16.
 // ---------------------------------------------------------------------------
-
-constexpr int kALd = 72;  // LDS row stride of A in bf16 (64 + 16 bytes of padding)
 
 template <int NM, int NS>
 struct Big {
   static constexpr int kWaveCols = 32 * NS;
   static constexpr int kWgCols = 2 * kWaveCols;
   static constexpr int kTilesN = kWgCols / 64;            // packed 64-row tiles per matrix
-  static constexpr int kAWords = kBigM * kALd / 2;        // A buffer (32-bit words)
-  static constexpr int kBWords = NM * kWgCols * 32 / 4;   // codes of one group
-  static constexpr int kCWords = kBigM * 4;                // row sums: 16 bytes per row
-  static constexpr int kBufWords = kAWords + kBWords + kCWords;
-  static constexpr int kPieces = NM * kTilesN / 2;        // 16-byte code pieces per thread
-  static_assert(kPieces >= 1 && NM * kTilesN % 2 == 0, "codes of a group: whole pieces per thread");
-  static int lds_bytes(int groups) {
-    return (2 * kBufWords + NM * kWgCols * groups / 2 + 4) * 4;  // + 16 zero bytes
-  }
 };
-
-// Global loads of group grp (clamped to the last group): this thread's 32 A
-// columns of its row and kPieces 16-byte pieces of the codes.  Every address
-// is valid -- rows past the slot read a row of the slot, tiles past the end
-// of the matrix read its last tile, and the outputs those give are never
-// stored -- so the loads are unconditional and a wait for one group's loads
-// leaves the next group's in flight.
-//
-// Code piece p = t + 256 i of a group (i < kPieces) is row `row` (of 64) of
-// half h (32 columns) of packed tile tt of matrix mat, with
-// p = ((mat * kTilesN + tt) * 2 + h) * 64 + row.
-template <int NM, int NS>
-__device__ __forceinline__ void big_piece(int i, int& mat, int& tt, int& h, int& row) {
-  using C = Big<NM, NS>;
-  const int p = threadIdx.x + 256 * i;
-  mat = p / (C::kTilesN * 128);
-  const int r = p - mat * (C::kTilesN * 128);
-  tt = r / 128;
-  h = (r / 64) & 1;
-  row = r & 63;
-}
-
-template <int NM, int NS, bool MX>
-__device__ __forceinline__ void big_load(const uint16_t* rowp, const uint2* sump, int ahalf,
-                                         int grp, int groups, int K, int ntv,
-                                         const uint8_t* const (&qbase)[NM], u32x4_t (&ra)[4],
-                                         u32x2_t& rs, u32x4_t (&rb)[Big<NM, NS>::kPieces]) {
-  grp = min(grp, groups - 1);
-  if constexpr (MX)
-    rs = u32x2_t{0u, 0u};  // (no offset to correct)
-  else
-    rs = *reinterpret_cast<const u32x2_t*>(sump + grp);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    ra[j] = *reinterpret_cast<const u32x4_t*>(rowp + grp * 64 + ahalf * 32 + j * 8);
-#pragma unroll
-  for (int i = 0; i < Big<NM, NS>::kPieces; ++i) {
-    int mat, tt, h, row;
-    big_piece<NM, NS>(i, mat, tt, h, row);
-    tt = min(tt, ntv - 1);
-    const uint8_t* src = qbase[0];
-#pragma unroll
-    for (int mm = 1; mm < NM; ++mm)
-      if (mat == mm) src = qbase[mm];
-    rb[i] = *reinterpret_cast<const u32x4_t*>(src + static_cast<size_t>(tt) * 32 * K +
-                                              static_cast<size_t>(2 * grp + h) * 1024 + row * 16);
-  }
-}
-
-// The loaded group into LDS buffer `buf`: A rows, then the codes.
-template <int NM, int NS, bool MX>
-__device__ __forceinline__ void big_store(uint32_t* buf, int arow, int ahalf, const u32x4_t (&ra)[4],
-                                          const u32x2_t& rs, const u32x4_t (&rb)[Big<NM, NS>::kPieces]) {
-  using C = Big<NM, NS>;
-  // Nothing is masked: rows past the slot hold a copy of a row of the slot
-  // and columns past the matrix a copy of its last tile, finite values whose
-  // outputs (each output row and column depends on its own A row and B
-  // column only) are never stored.
-  u32x4_t* a = reinterpret_cast<u32x4_t*>(buf + (arow * kALd + ahalf * 32) / 2);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) a[j] = ra[j];
-  // the row's sum parts as the first three elements of an 8-element A operand
-  if (!MX && ahalf == 0)
-    reinterpret_cast<u32x4_t*>(buf + C::kAWords + C::kBWords)[arow] = u32x4_t{rs.x, rs.y, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < C::kPieces; ++i) {
-    int mat, tt, h, row;
-    big_piece<NM, NS>(i, mat, tt, h, row);
-    reinterpret_cast<u32x4_t*>(buf + C::kAWords)[(mat * 2 + h) * C::kWgCols + tt * 64 + row] = rb[i];
-  }
-}
 
 // B operand of the correction: -136 at k = 0, 1, 2 (the three sum parts),
 // zero elsewhere.
@@ -805,88 +719,162 @@ __device__ __forceinline__ bf16x8_t minus136_x3() {
   return as_bf16x8(make_uint4(0xC308C308u, 0x0000C308u, 0u, 0u));
 }
 
-// sc: the staged scales.  int4: fp16 [NM][64-row tile][groups][64 rows].
-// MX: E8M0 bytes [NM][64-row tile][2 * groups blocks][64 rows], the same
-// size.
-template <int NM, int NS, bool MX, bool WIDE = false>
-__device__ __forceinline__ void big_math(const uint32_t* buf, const uint32_t* zero16,
-                                         const uint16_t* sc, int groups, int grp, int wm, int wn,
-                                         int col, int half, f32x16_t (&acc)[2][NM][NS]) {
+// The operands of a 64-column scale group go from
+// memory straight into LDS (global_load_lds, 16 bytes per lane), three
+// groups deep, with no staging registers and one barrier per group.
+//  * A stage holds one group: A [128 rows][64 bf16] with the eight 16-byte
+//    segments of row r stored in the order seg ^ ((r >> 1) & 7) (a 1 KB DMA
+//    write is contiguous, so the layout is chosen by which segment each lane
+//    fetches; the swizzle keeps the 32-row fragment reads of the MFMAs free
+//    of bank conflicts without padding); the codes of the group
+//    [(mat * 2 + half) * kWgCols + column] x 16 bytes, as packed; the scales
+//    of the group, 128 bytes per packed 64-row tile; the row sums of the
+//    group, 8 bytes per row.
+//  * Group g + 2 is fetched while group g is multiplied, into the stage group
+//    g - 1 used; the stages are three distinct LDS arrays and the loop is
+//    unrolled by three, so each read names its stage and the compiler's own
+//    waits do not cover the fetches of the other stages.
+// The arithmetic: exact bf16 (136 + q)
+// operands, the -136 * row-sum correction by one MFMA per row block, the
+// fp16 scale per group in float32; MXFP4 blocks fold E8M0 into the
+// conversion, or take the per-block float32 scaling (tiles with a scale
+// byte outside 2 .. 252).
+// ---------------------------------------------------------------------------
+
+constexpr int kSt2A = kBigM * 128;                      // A, 16 KB
+constexpr int kSt2B = 4096;                             // codes (NM * kTilesN * 2 KB)
+constexpr int kSt2S = 256;                              // scales: two 128-byte pieces
+constexpr int kSt2R = kBigM * 8;                        // row sums
+constexpr int kSt2Bytes = kSt2A + kSt2B + kSt2S + kSt2R;
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Byte offset of A[row][8 * seg ..] in a stage.
+__device__ __forceinline__ int a2_off(int row, int seg) {
+  return row * 128 + ((seg ^ ((row >> 1) & 7)) << 4);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), expcnt untouched (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
+// This lane's sources of group 0 (each advanced by the group index).
+struct Big2Src {
+  const uint8_t* a[4];  // A: its 16-byte segment of row 8 * (4 * wv + j) + lane / 8
+  const uint8_t* b;     // codes: its 16 bytes of the wavefront's 1 KB run
+  const uint8_t* s;     // scales: its 16 bytes (lanes 0..3)
+  const uint8_t* r;     // row sums: its 4 bytes
+};
+
+// DMA instructions per group and wavefront.
+template <bool MX>
+constexpr int big2_dmas() { return 4 + 1 + 1 + (MX ? 0 : 1); }
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)p));
+}
+
+// One LDS DMA instruction: every active lane's 16 (or 4) bytes at g go to LDS
+// at m0 + 16 (or 4) * lane.  Written as asm rather than the builtin: the
+// compiler's own wait bookkeeping cannot tell the three stages apart and
+// would wait for every fetch in flight before each read of a stage; these
+// fetches are waited for explicitly (wait_vm_lgkm0) instead.  The statement
+// has no register outputs; the address register is read when it issues.
+__device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+template <bool MX>
+__device__ __forceinline__ void big2_issue(const Big2Src& src, int grp, uint8_t* st, int wv,
+                                           int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma16(src.a[j] + grp * 128, lds_addr(st + (wv * 4 + j) * 1024));
+  dma16(src.b + grp * 2048, lds_addr(st + kSt2A + wv * 1024));
+  if (lane < 4)
+    dma16(src.s + grp * 128, lds_addr(st + kSt2A + kSt2B + (wv >> 1) * 128 + (wv & 1) * 64));
+  if constexpr (!MX) dma4(src.r + grp * 8, lds_addr(st + kSt2A + kSt2B + kSt2S + wv * 256));
+}
+
+template <int NM, int NS, bool MX, bool WIDE>
+__device__ __forceinline__ void big2_math(const uint8_t* st, int wm, int wn, int col, int half,
+                                          f32x16_t (&acc)[2][NM][NS]) {
   using C = Big<NM, NS>;
-  uint4 a[2][4];
+  u32x4_t a[2][4];
   f32x16_t corr[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = wm * 64 + i * 32 + col;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      a[i][j] = *reinterpret_cast<const uint4*>(buf + (r * kALd + half * 32 + j * 8) / 2);
+    for (int j = 0; j < 4; ++j) a[i][j] = *reinterpret_cast<const u32x4_t*>(st + a2_off(r, half * 4 + j));
     if constexpr (MX) continue;
-    // -136 * (row sums of the group), the same for every column: one MFMA
-    // per row block from the staged sum parts (the lanes of the upper K half
-    // read zeros), shared by every matrix and column tile
-    const uint32_t* sp = half ? zero16 : buf + C::kAWords + C::kBWords + r * 4;
-    corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        as_bf16x8(*reinterpret_cast<const uint4*>(sp)), minus136_x3(), f32x16_t{}, 0, 0, 0);
+    // -136 * (row sums of the group): one MFMA per row block from the sum
+    // parts of the lane's row (the lanes of the upper K half pass zeros)
+    const u32x2_t rs = *reinterpret_cast<const u32x2_t*>(st + kSt2A + kSt2B + kSt2S + r * 8);
+    const u32x4_t op = half ? u32x4_t{0u, 0u, 0u, 0u} : u32x4_t{rs.x, rs.y, 0u, 0u};
+    corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, op),
+                                                      minus136_x3(), f32x16_t{}, 0, 0, 0);
   }
-  const uint4* bq = reinterpret_cast<const uint4*>(buf + C::kAWords);
+  const uint8_t* bq = st + kSt2A;
+  const uint8_t* sc = st + kSt2A + kSt2B;
+  auto bword = [&](int mat, int n) -> u32x4_t {
+    return *reinterpret_cast<const u32x4_t*>(bq + ((mat * 2 + half) * C::kWgCols + n) * 16);
+  };
   if constexpr (MX) {
-    // the lane's block of 32 is K half `half` of the group; E8M0 byte of
-    // column n, block b of this group:
-    const uint8_t* sb = reinterpret_cast<const uint8_t*>(sc);
     auto ebyte = [&](int mat, int n, int b) -> uint32_t {
-      return sb[2 * mat * C::kWgCols * groups + (n >> 6) * 128 * groups + grp * 128 + b * 64 +
-                (n & 63)];
+      return sc[(mat * C::kTilesN + (n >> 6)) * 128 + b * 64 + (n & 63)];
     };
     if constexpr (!WIDE) {
-      // power-of-two scales folded into the conversion, products straight
-      // into acc
 #pragma unroll
       for (int mat = 0; mat < NM; ++mat) {
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
           const int n = wn * C::kWaveCols + ns * 32 + col;
-          const uint4 q = bq[(mat * 2 + half) * C::kWgCols + n];
+          const u32x4_t q = bword(mat, n);
           const float sv = e8m0_to_f32(ebyte(mat, n, half));
           bf16x8_t bw[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) bw[j] = dequant_word_mx(word_of(q, j), sv);
+          for (int j = 0; j < 4; ++j) bw[j] = dequant_word_mx(q[j], sv);
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               acc[i][mat][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  as_bf16x8(a[i][j]), bw[j], acc[i][mat][ns], 0, 0, 0);
+                  __builtin_bit_cast(bf16x8_t, a[i][j]), bw[j], acc[i][mat][ns], 0, 0, 0);
         }
       }
       return;
     }
-    // The tile has a scale outside 2 .. 252 (a product E2M1 * 2^(E-127) that
-    // is not a normal bf16, or E = 255): the elements convert unscaled
-    // (exact), each block of 32 gets its own MFMA chain -- the lanes of the
-    // other K half pass zero codes -- and its scale multiplies the chain's
-    // sum in float32, as on the decode path.  Output lane (col, half) holds
-    // column col, so it applies that column's scale of each block.
 #pragma unroll
     for (int mat = 0; mat < NM; ++mat) {
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         const int n = wn * C::kWaveCols + ns * 32 + col;
-        const uint4 q = bq[(mat * 2 + half) * C::kWgCols + n];
+        const u32x4_t q = bword(mat, n);
 #pragma unroll 1
         for (int b = 0; b < 2; ++b) {  // (a loop: one block's operands live at a time)
           const float sv = e8m0_to_f32(ebyte(mat, n, b));
           bf16x8_t bw[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) bw[j] = dequant_word_mx(half == b ? word_of(q, j) : 0u, 1.0f);
+          for (int j = 0; j < 4; ++j) bw[j] = dequant_word_mx(half == b ? q[j] : 0u, 1.0f);
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            f32x16_t p = f32x16_t{};
+            f32x16_t pp = f32x16_t{};
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][j]), bw[j], p, 0, 0, 0);
+              pp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i][j]),
+                                                           bw[j], pp, 0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = fmaf(sv, p[e], acc[i][mat][ns][e]);
+            for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = fmaf(sv, pp[e], acc[i][mat][ns][e]);
           }
         }
       }
@@ -897,22 +885,22 @@ __device__ __forceinline__ void big_math(const uint32_t* buf, const uint32_t* ze
   for (int mat = 0; mat < NM; ++mat) {
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
-      const int n = wn * C::kWaveCols + ns * 32 + col;  // column inside the workgroup
-      const uint4 q = bq[(mat * 2 + half) * C::kWgCols + n];
-      const float sv = static_cast<float>(
-          __builtin_bit_cast(_Float16, sc[mat * C::kWgCols * groups + (n >> 6) * 64 * groups +
-                                          grp * 64 + (n & 63)]));
+      const int n = wn * C::kWaveCols + ns * 32 + col;
+      const u32x4_t q = bword(mat, n);
+      const float sv = static_cast<float>(*reinterpret_cast<const _Float16*>(
+          sc + (mat * C::kTilesN + (n >> 6)) * 128 + (n & 63) * 2));
       bf16x8_t bw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bw[j] = dequant_word(word_of(q, j));
+      for (int j = 0; j < 4; ++j) bw[j] = dequant_word(q[j]);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        f32x16_t p = corr[i];
+        f32x16_t pp = corr[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][j]), bw[j], p, 0, 0, 0);
+          pp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i][j]), bw[j],
+                                                       pp, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = fmaf(sv, p[e], acc[i][mat][ns][e]);
+        for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = fmaf(sv, pp[e], acc[i][mat][ns][e]);
       }
     }
   }
@@ -921,7 +909,10 @@ __device__ __forceinline__ void big_math(const uint32_t* buf, const uint32_t* ze
 template <int NM, int NS, bool DOWN, bool MX>
 __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   using C = Big<NM, NS>;
-  extern __shared__ __align__(16) uint32_t lds[];
+  static_assert(NM * C::kTilesN == 2, "two 128-byte scale pieces and four 1 KB code runs");
+  __shared__ __align__(16) uint8_t st0[kSt2Bytes];
+  __shared__ __align__(16) uint8_t st1[kSt2Bytes];
+  __shared__ __align__(16) uint8_t st2[kSt2Bytes];
   const int N = DOWN ? g.d : g.f, K = DOWN ? g.f : g.d;
   int ti, cblk;
   if (!xcd_item(__builtin_amdgcn_readfirstlane(g.n_big[0]), (N + C::kWgCols - 1) / C::kWgCols, ti,
@@ -934,87 +925,95 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   const Slot sl = resolve_slot(g, slot);
   const int groups = K / 64;
   const int ntv = min(C::kTilesN, (N - n0) / 64);  // packed tiles inside the matrix
-  uint32_t* buf0 = lds;
-  uint32_t* buf1 = lds + C::kBufWords;
-  // scales as packed: [NM][64-row tile][groups][64] fp16 (MX: the E8M0 bytes
-  // [NM][64-row tile][2 * groups][64], byte for byte the same size)
-  uint16_t* sc = reinterpret_cast<uint16_t*>(lds + 2 * C::kBufWords);
-
+  const int t = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const size_t soff[2] = {DOWN ? g.s_down : g.s_gate, g.s_up};
   const size_t qoff[2] = {DOWN ? g.q_down : g.q_gate, g.q_up};
-  const uint8_t* qbase[NM];
-  bool wide = false;  // MX: a staged scale byte outside 2 .. 252
-#pragma unroll
-  for (int mat = 0; mat < NM; ++mat) {
-    qbase[mat] = sl.blk + qoff[mat] + static_cast<size_t>(n0 / 64) * 32 * K;
-    const uint4* src = reinterpret_cast<const uint4*>(sl.blk + soff[mat] +
-                                                      static_cast<size_t>(n0) * groups * 2);
-    uint4* dst = reinterpret_cast<uint4*>(sc + mat * C::kWgCols * groups);
-    for (int i = threadIdx.x; i < ntv * 64 * groups / 8; i += 256) {
-      const uint4 v = src[i];
-      dst[i] = v;
-      if constexpr (MX) wide |= mx_wide(v.x) | mx_wide(v.y) | mx_wide(v.z) | mx_wide(v.w);
-    }
-  }
-  const int t = threadIdx.x, arow = t >> 1, ahalf = t & 1;
-  const int m = m0 + arow;
-  const uint16_t* rowp;
-  const uint2* sump;
-  {
-    const int mr = m < sl.M ? m : m0;  // rows past the slot read its first row (never stored)
+  // tile row m -> this row's activations and row sums (rows past the slot
+  // read the slot's first row; their outputs are never stored)
+  auto row_src = [&](int m, const uint8_t*& rp, const uint8_t*& sp) {
+    const int mr = m < sl.M ? m : m0;
     if (DOWN) {
       const size_t hr = row_of(g, sl, mr);
-      rowp = g.h + hr * g.f;
-      sump = g.sum_h + hr * groups;
+      rp = reinterpret_cast<const uint8_t*>(g.h + hr * g.f);
+      sp = reinterpret_cast<const uint8_t*>(g.sum_h + hr * groups);
     } else {
       const int tok = sl.shared ? mr : g.perm[sl.p0 + mr] / g.top_k;
-      rowp = g.x + static_cast<size_t>(tok) * g.d;
-      sump = g.sum_x + static_cast<size_t>(tok) * groups;
-    }
-  }
-  uint32_t* zero16 = lds + 2 * C::kBufWords + NM * C::kWgCols * groups / 2;
-  if (t < 4) zero16[t] = 0u;  // visible after the first barrier
-  const int wv = t >> 6, lane = t & 63;
-  const int wm = wv & 1, wn = wv >> 1, col = lane & 31, half = lane >> 5;
-
-  f32x16_t acc[2][NM][NS];
-  // The main loop, with the scales folded into the element conversion or
-  // (MX tiles with a scale byte outside 2 .. 252) applied per block in
-  // float32.  The choice is per workgroup and uniform.
-  auto main_loop = [&](auto wide_tag) {
-    constexpr bool W = decltype(wide_tag)::value;
-    // Two register sets: group g+1 is stored to LDS while g+2 is in flight,
-    // so every group's loads have two groups of math to land.
-    u32x4_t ra[2][4], rb[2][C::kPieces];
-    u32x2_t rs[2];
-    big_load<NM, NS, MX>(rowp, sump, ahalf, 0, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
-    big_load<NM, NS, MX>(rowp, sump, ahalf, 1, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
-    big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0]);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int mat = 0; mat < NM; ++mat)
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = 0.0f;
-    for (int g0 = 0; g0 < groups; g0 += 2) {
-      // group g0 is in buf0, group g0 + 1 in register set 1
-      big_load<NM, NS, MX>(rowp, sump, ahalf, g0 + 2, groups, K, ntv, qbase, ra[0], rs[0], rb[0]);
-      big_math<NM, NS, MX, W>(buf0, zero16, sc, groups, g0, wm, wn, col, half, acc);
-      big_store<NM, NS, MX>(buf1, arow, ahalf, ra[1], rs[1], rb[1]);
-      __syncthreads();
-      if (g0 + 1 < groups) {
-        big_load<NM, NS, MX>(rowp, sump, ahalf, g0 + 3, groups, K, ntv, qbase, ra[1], rs[1], rb[1]);
-        big_math<NM, NS, MX, W>(buf1, zero16, sc, groups, g0 + 1, wm, wn, col, half, acc);
-        big_store<NM, NS, MX>(buf0, arow, ahalf, ra[0], rs[0], rb[0]);
-        __syncthreads();
-      }
+      rp = reinterpret_cast<const uint8_t*>(g.x + static_cast<size_t>(tok) * g.d);
+      sp = reinterpret_cast<const uint8_t*>(g.sum_x + static_cast<size_t>(tok) * groups);
     }
   };
+  Big2Src src;
+  {
+    const uint8_t* sp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 8 * (wv * 4 + j) + (lane >> 3);
+      const uint8_t* rp;
+      row_src(m0 + r, rp, sp);
+      src.a[j] = rp + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+    }
+    // codes: piece wv = (mat * 2 + half) * kTilesN + tt
+    const int tt = min(wv % C::kTilesN, ntv - 1), hh = (wv / C::kTilesN) & 1,
+              mat = wv / (2 * C::kTilesN);
+    src.b = sl.blk + qoff[mat] + static_cast<size_t>(n0 / 64 + tt) * 32 * K + hh * 1024 + lane * 16;
+    // scales: piece wv / 2 = mat * kTilesN + tt, 64-byte half wv % 2
+    const int ps = wv >> 1, smat = ps / C::kTilesN;
+    const int spt = min(n0 / 64 + ps % C::kTilesN, N / 64 - 1);
+    src.s = sl.blk + soff[smat] + static_cast<size_t>(spt) * groups * 128 + (wv & 1) * 64 + lane * 16;
+    // row sums: 4-byte part (wv * 64 + lane) & 1 of row (wv * 64 + lane) / 2
+    const int d = wv * 64 + lane;
+    const uint8_t* rp;
+    row_src(m0 + (d >> 1), rp, sp);
+    src.r = sp + (d & 1) * 4;
+  }
+  const int wm = wv & 1, wn = wv >> 1, col = lane & 31, half = lane >> 5;
+  // MX: whether any scale byte of the tile leaves 2 .. 252 (this thread reads
+  // its share of the tile's scale runs once)
+  bool wide = false;
   if constexpr (MX) {
-    if (__syncthreads_or(wide))
+    const int run = groups * 128;  // bytes per piece
+    for (int e = t * 16; e < 2 * run; e += 256 * 16) {
+      const int ps = e / run, smat = ps / C::kTilesN;
+      const int spt = min(n0 / 64 + ps % C::kTilesN, N / 64 - 1);
+      const uint4 v = *reinterpret_cast<const uint4*>(sl.blk + soff[smat] +
+                                                      static_cast<size_t>(spt) * run + e % run);
+      wide |= mx_wide(v.x) | mx_wide(v.y) | mx_wide(v.z) | mx_wide(v.w);
+    }
+    wide = __syncthreads_or(wide);
+  }
+  f32x16_t acc[2][NM][NS];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int mat = 0; mat < NM; ++mat)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = 0.0f;
+  constexpr int kD = big2_dmas<MX>();
+  auto main_loop = [&](auto wide_tag) {
+    constexpr bool W = decltype(wide_tag)::value;
+    big2_issue<MX>(src, 0, st0, wv, lane);
+    big2_issue<MX>(src, min(1, groups - 1), st1, wv, lane);
+    // step of group grp in stage `cur`: its fetches done (the next group's
+    // may still run), every wavefront done with the previous group (whose
+    // stage `nxt2` receives group grp + 2), then the math
+    auto step = [&](int grp, uint8_t* cur, uint8_t* nxt2) {
+      wait_vm_lgkm0<kD>();
+      __builtin_amdgcn_s_barrier();
+      big2_issue<MX>(src, min(grp + 2, groups - 1), nxt2, wv, lane);
+      big2_math<NM, NS, MX, W>(cur, wm, wn, col, half, acc);
+    };
+    for (int g0 = 0; g0 < groups; g0 += 3) {
+      step(g0, st0, st2);
+      if (g0 + 1 < groups) step(g0 + 1, st1, st0);
+      if (g0 + 2 < groups) step(g0 + 2, st2, st1);
+    }
+    wait_vm_lgkm0<0>();  // no fetch into LDS outlives the workgroup
+  };
+  if constexpr (MX) {
+    if (wide)
       main_loop(std::true_type{});
     else
       main_loop(std::false_type{});
@@ -1082,13 +1081,6 @@ PrefillLayout prefill_layout(int T, int k, int E, int d, int f, bool has_shared)
   return l;
 }
 
-// Dynamic LDS above 64 KB has to be enabled per kernel.
-template <typename K>
-hipError_t allow_lds(K kernel, int bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
-
 }  // namespace
 
 namespace {
@@ -1100,15 +1092,11 @@ template <bool MX>
 hipError_t prefill_kernels(const FfnProblem& p, const PrefillArgs& g, hipStream_t stream) {
   const int ms = max_small(p.T, p.k, g.slots, p.has_shared);
   const int mb = max_big(p.T, p.k, p.has_shared);
-  // gate/up: 64 columns of both matrices per workgroup (128 columns measured
-  // slower: the scales of the wider tile leave LDS for one workgroup per CU)
+  // gate/up: 64 columns of both matrices per workgroup, down: 128 columns
+  // (three LDS stages of 21.3 KB each; two workgroups per CU)
   using GU = Big<2, 1>;
   using DN = Big<1, 2>;
-  const int lds_gu = GU::lds_bytes(p.d / 64), lds_dn = DN::lds_bytes(p.f / 64);
-  if (lds_gu > kMaxLds || lds_dn > kMaxLds) return hipErrorNotSupported;
   hipError_t err;
-  if ((err = allow_lds(prefill_big<2, 1, false, MX>, lds_gu)) != hipSuccess) return err;
-  if ((err = allow_lds(prefill_big<1, 2, true, MX>, lds_dn)) != hipSuccess) return err;
   if ((err = launch(prefill_tiles, dim3(1), dim3(1024), 0, stream, g)) != hipSuccess) return err;
   // 1-D grids: enough workgroups for the largest possible tile lists, in
   // whole rounds of the XCDs
@@ -1124,13 +1112,13 @@ hipError_t prefill_kernels(const FfnProblem& p, const PrefillArgs& g, hipStream_
                   stream, src, rows, K, dst);
   };
   if (!MX && (err = rowsums(g.x, p.T, p.d, g.sum_x)) != hipSuccess) return err;
-  err = launch(prefill_big<2, 1, false, MX>, grid(mb, cgu), dim3(256), lds_gu, stream, g);
+  err = launch(prefill_big<2, 1, false, MX>, grid(mb, cgu), dim3(256), 0, stream, g);
   if (err != hipSuccess) return err;
   err = launch(prefill_small<2, kSmallNSubGU, false, MX>, grid(ms, sgu), dim3(256), 0, stream, g);
   if (err != hipSuccess) return err;
   if (!MX && (err = rowsums(g.h, rows_of(p.T, p.k, p.has_shared), p.f, g.sum_h)) != hipSuccess)
     return err;
-  err = launch(prefill_big<1, 2, true, MX>, grid(mb, cdn), dim3(256), lds_dn, stream, g);
+  err = launch(prefill_big<1, 2, true, MX>, grid(mb, cdn), dim3(256), 0, stream, g);
   if (err != hipSuccess) return err;
   return launch(prefill_small<1, kSmallNSubDN, true, MX>, grid(ms, sdn), dim3(256), 0, stream, g);
 }
