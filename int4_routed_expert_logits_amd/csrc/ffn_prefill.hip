@@ -1002,8 +1002,8 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
     auto step = [&](int grp, uint8_t* cur, uint8_t* nxt2) {
       wait_vm_lgkm0<kD>();
       __builtin_amdgcn_s_barrier();
-      big2_issue<MX>(src, min(grp + 2, groups - 1), nxt2, wv, lane);
       big2_math<NM, NS, MX, W>(cur, wm, wn, col, half, acc);
+      big2_issue<MX>(src, min(grp + 2, groups - 1), nxt2, wv, lane);
     };
     for (int g0 = 0; g0 < groups; g0 += 3) {
       step(g0, st0, st2);
