@@ -384,6 +384,14 @@ moe_status moe_cache_stats(const moe_expert_cache* cache, int64_t* hits, int64_t
 moe_status moe_cache_last_fetch(const moe_expert_cache* cache, int32_t capacity, int32_t* fetched,
                                 int32_t* evicted, int32_t* n_fetched);
 
+/* Undo the latest step's placements (what moe_cache_last_fetch reports):
+ * the slots it filled become empty, its misses are taken back, and the
+ * latest-step record is cleared; the experts it displaced stay evicted.
+ * For callers of moe_cache_plan whose own copies into the slots failed;
+ * moe_cache_layer_decode does the same when its copies cannot be queued.
+ * Calling it twice in a row changes nothing the second time. */
+moe_status moe_cache_unplan_last(moe_expert_cache* cache);
+
 /* Device scratch bytes of moe_cache_layer_decode (0 for an invalid shape). */
 size_t moe_cache_workspace_bytes(const moe_shape* shape, int32_t T, int32_t n_slots);
 

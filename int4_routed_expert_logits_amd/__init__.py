@@ -12,7 +12,7 @@ from ._binding import (  # noqa: F401
     moe_pack_experts, moe_quantize,
     moe_route, moe_route_union, moe_route_workspace_bytes, moe_status_str, moe_union,
     moe_cache_create, moe_cache_destroy, moe_cache_layer_decode, moe_cache_pin, moe_cache_plan,
-    moe_cache_stats, moe_cache_last_fetch, moe_cache_workspace_bytes, moe_measure_stream_read,
+    moe_cache_stats, moe_cache_last_fetch, moe_cache_unplan_last, moe_cache_workspace_bytes, moe_measure_stream_read,
 )
 
 

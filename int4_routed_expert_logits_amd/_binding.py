@@ -30,7 +30,8 @@ EXPORTS = ("moe_expert_bytes", "moe_pack_experts", "moe_quantize", "moe_route_wo
            "moe_expert_ffn", "moe_combine", "moe_layer_decode_workspace_bytes",
            "moe_layer_decode", "moe_layer_decode_static", "moe_layer_decode_static_max_bytes",
            "moe_cache_create", "moe_cache_destroy", "moe_cache_pin",
-           "moe_cache_plan", "moe_cache_stats", "moe_cache_last_fetch", "moe_cache_workspace_bytes",
+           "moe_cache_plan", "moe_cache_stats", "moe_cache_last_fetch", "moe_cache_unplan_last",
+           "moe_cache_workspace_bytes",
            "moe_cache_layer_decode", "moe_status_str", "moe_measure_stream_read")
 
 
@@ -113,6 +114,8 @@ def load():
     lib.moe_cache_stats.restype = c_int32
     lib.moe_cache_last_fetch.argtypes = [vp, c_int32, vp, vp, vp]
     lib.moe_cache_last_fetch.restype = c_int32
+    lib.moe_cache_unplan_last.argtypes = [vp]
+    lib.moe_cache_unplan_last.restype = c_int32
     lib.moe_cache_workspace_bytes.argtypes = [sp, c_int32, c_int32]
     lib.moe_cache_workspace_bytes.restype = c_size_t
     lib.moe_cache_layer_decode.argtypes = [vp, c_int32, vp, c_int32, vp, vp, vp, vp, vp, vp, vp,
@@ -356,6 +359,11 @@ def moe_cache_last_fetch(cache: int, capacity: int):
     _check("moe_cache_last_fetch", load().moe_cache_last_fetch(
         cache, capacity, ctypes.addressof(f), ctypes.addressof(e), ctypes.addressof(n)))
     return list(f[:n.value]), list(e[:n.value])
+
+
+def moe_cache_unplan_last(cache: int) -> None:
+    """Undo the latest step's placements (its fetched slots become empty)."""
+    _check("moe_cache_unplan_last", load().moe_cache_unplan_last(cache))
 
 
 def moe_cache_workspace_bytes(shape, T: int, n_slots: int) -> int:

@@ -140,16 +140,18 @@ bool plan_step(moe_expert_cache* c, int n, const int32_t* experts, int32_t* slot
   return true;
 }
 
-// Undo the placement of a step's fetched experts after their copies could not
-// all be queued: their slots become empty (whatever part of a block reached
-// a slot is never read as a hit), and the latest-step record is cleared.
-// The experts they displaced were already unmapped by the plan.
-void unplace_fetched(moe_expert_cache* c, const int32_t* fetched, const int32_t* fetched_slot,
-                     int nf) {
-  for (int i = 0; i < nf; ++i) {
-    c->slot_expert[fetched_slot[i]] = -1;
-    c->slot_used[fetched_slot[i]] = 0;
-    c->expert_slot[fetched[i]] = -1;
+// Undo the placement of the latest step's fetched experts: their slots
+// become empty (whatever part of a block reached a slot is never read as a
+// hit), their misses are taken back, and the latest-step record is cleared.
+// The experts they displaced stay unmapped (their slots' contents are gone).
+void unplace_last(moe_expert_cache* c) {
+  for (const int32_t e : c->last_fetched) {
+    const int s = c->expert_slot[e];
+    if (s < 0) continue;
+    c->slot_expert[s] = -1;
+    c->slot_used[s] = 0;
+    c->expert_slot[e] = -1;
+    --c->misses;
   }
   c->last_fetched.clear();
   c->last_evicted.clear();
@@ -289,6 +291,12 @@ moe_status moe_cache_last_fetch(const moe_expert_cache* cache, int32_t capacity,
   return MOE_OK;
 }
 
+moe_status moe_cache_unplan_last(moe_expert_cache* cache) {
+  if (!cache) return MOE_ERR_NULL;
+  unplace_last(cache);
+  return MOE_OK;
+}
+
 size_t moe_cache_workspace_bytes(const moe_shape* shape, int32_t T, int32_t n_slots) {
   if (check_cache_shape(shape) != MOE_OK || T < 0 || n_slots < 1) return 0;
   return cache_ws(*shape, T, n_slots).total;
@@ -359,15 +367,15 @@ moe_status moe_cache_layer_decode(moe_expert_cache* cache, int32_t T, const void
     err = hipMemcpyAsync(cache->dev_slots + static_cast<size_t>(fslot[i]) * cache->block_bytes,
                          cache->host_blocks + static_cast<size_t>(fetched[i]) * cache->block_bytes,
                          cache->block_bytes, hipMemcpyHostToDevice, cs);
-    if (err == hipSuccess) cache->bytes_fetched += static_cast<int64_t>(cache->block_bytes);
   }
   if (err == hipSuccess && nf > 0) err = hipEventRecord(cache->fetched_ev, cs);
   if (err != hipSuccess) {
     // a slot whose copy was not queued (or not fenced by the event) must not
     // be taken for its expert later
-    unplace_fetched(cache, fetched.data(), fslot.data(), nf);
+    unplace_last(cache);
     return MOE_ERR_HIP;
   }
+  cache->bytes_fetched += static_cast<int64_t>(nf) * static_cast<int64_t>(cache->block_bytes);
   // list A: the slots of this step's hits, list B: the fetched slots (both
   // ascending, -1 padded)
   int32_t* la = h_up + n;

@@ -85,6 +85,36 @@ def test_a_step_that_cannot_fit_leaves_the_state_unchanged():
         moe.moe_cache_destroy(h)
 
 
+def test_undoing_a_step_empties_its_slots_and_keeps_the_rest():
+    """What a failed copy leaves behind (moe_cache_layer_decode undoes a step
+    whose copies cannot be queued the same way): the step's fetched experts
+    lose their slots and their misses, the experts they displaced stay
+    evicted, the hits and every other mapping stand, and the next step
+    places into the freed slots as into any empty slot."""
+    h = moe.moe_cache_create(shp(E=16, k=2), 4)
+    ref = ExpertCache(4)
+    try:
+        for step in ([0, 1], [2, 3], [0, 2]):  # fills the four slots, then two hits
+            moe.moe_cache_plan(h, step)
+            ref.step(np.array(step))
+        assert moe.moe_cache_stats(h) == (2, 4, 0)
+        slot_of, fetched, evicted = moe.moe_cache_plan(h, [0, 4, 5])  # 4, 5 evict 1, 3
+        assert list(fetched) == [4, 5] and list(evicted) == [1, 3]
+        moe.moe_cache_unplan_last(h)
+        assert moe.moe_cache_last_fetch(h, 16) == ([], [])
+        assert moe.moe_cache_stats(h) == (3, 4, 0)  # the hit on 0 stands, 4 and 5 do not count
+        moe.moe_cache_unplan_last(h)  # nothing recorded: no change
+        assert moe.moe_cache_stats(h) == (3, 4, 0)
+        # 0 and 2 are still resident; 1, 3, 4, 5 are not
+        slot_of, fetched, _ = moe.moe_cache_plan(h, [0, 2])
+        assert fetched.size == 0 and sorted(slot_of.tolist()) == sorted(set(slot_of.tolist()))
+        slot_of, fetched, evicted = moe.moe_cache_plan(h, [1, 3])
+        assert list(fetched) == [1, 3] and list(evicted) == [-1, -1]  # the freed slots
+        assert moe.moe_cache_stats(h) == (5, 6, 0)
+    finally:
+        moe.moe_cache_destroy(h)
+
+
 def test_cache_argument_checks():
     lib = moe.load()
     h = ctypes.c_void_p()

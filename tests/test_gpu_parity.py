@@ -448,6 +448,49 @@ def test_layer_decode_mtp_verify_batch_sampled():
     assert rel_err(buf.out.cpu().numpy(), np.stack([ref["out"][t] for t in range(3)])) <= TOL_DECODE
 
 
+@pytest.mark.parametrize("cfg,T", [(2, 1), (4, 1), (4, 3)])
+def test_layer_decode_call_replays_in_a_hip_graph(cfg, T):
+    """The benchmark's form of the decode step: moe_layer_decode captured in a
+    HIP graph and replayed, each replay on new tokens copied into the
+    captured input buffer, with eager work and synchronisations between the
+    replays; every replay's outputs equal an eager call's on the same tokens,
+    bit for bit."""
+    say(f"moe_layer_decode in a HIP graph cfg={cfg} T={T}")
+    L, dev = dev_layer(cfg)
+    sh = moe.shape_of(L.shape)
+    xs = [tokens(cfg, T, batch=b)[0] for b in range(4)]
+    x_in = xs[0].clone()
+    g_buf = LayerBuffers.allocate(sh, T, DEC)
+    run = lambda buf, x: run_layer_decode(x, dev["w_router"], dev["bias"], dev["experts"],
+                                          dev["shared"], buf)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        run(g_buf, x_in)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(g_buf, x_in)
+    torch.cuda.synchronize()
+    for rep, x in enumerate([xs[1], xs[2], xs[1], xs[3]]):
+        e_buf = LayerBuffers.allocate(sh, T, DEC)
+        run(e_buf, x)  # eager, on the same tokens
+        torch.cuda.synchronize()
+        x_in.copy_(x)
+        graph.replay()
+        torch.cuda.synchronize()
+        n = T * sh.top_k
+        for name in LAYER_OUTPUTS:
+            ta, tb = getattr(e_buf, name), getattr(g_buf, name)
+            if ta is None:
+                continue
+            if name in ("perm", "inv_perm", "y"):
+                ta, tb = ta[:n], tb[:n]
+            assert torch.equal(ta.cpu(), tb.cpu()), (rep, name)
+    del graph
+
+
 def test_layer_decode_call_reuses_its_workspace():
     say("moe_layer_decode workspace reuse")
     for cfg, T in ((4, 1), (2, 8)):
