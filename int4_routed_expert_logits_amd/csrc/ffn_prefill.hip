@@ -12,10 +12,11 @@
 // chose it -- are cut into M-tiles: 128-row tiles while at least 96 rows are
 // left, the rest in 32-row tiles.  A small kernel lists both kinds.
 //  * 128-row tiles (the heavy experts of a Zipf-routed batch, the shared
-//    expert): compute-bound.  A workgroup of 4 wavefronts stages the
-//    activations and the codes of one 64-column scale group in LDS (double
-//    buffered), and each wavefront computes 64 rows x 32 or 64 columns with
-//    v_mfma_f32_32x32x16_bf16.
+//    expert): compute-bound.  A workgroup of 4 wavefronts fetches the
+//    activations, codes, scales and row sums of one 64-column scale group
+//    straight into LDS (three stages, one group fetched while another is
+//    multiplied), and each wavefront computes 64 rows x 32 or 64 columns
+//    with v_mfma_f32_32x32x16_bf16.
 //  * 32-row tiles (the many experts with a handful of tokens): bound by the
 //    weight stream.  The activations of a group go through LDS, each
 //    wavefront keeps 4 groups of its own codes in flight in registers and
