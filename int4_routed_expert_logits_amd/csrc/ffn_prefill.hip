@@ -16,7 +16,9 @@
 //    activations, codes, scales and row sums of one 64-column scale group
 //    straight into LDS (three stages, one group fetched while another is
 //    multiplied), and each wavefront computes 64 rows x 32 or 64 columns
-//    with v_mfma_f32_32x32x16_bf16.
+//    (int4) or 64 or 128 columns (MXFP4, which has no per-group scale
+//    multiply-adds and so the registers for twice the columns) with
+//    v_mfma_f32_32x32x16_bf16.
 //  * 32-row tiles (the many experts with a handful of tokens): bound by the
 //    weight stream.  The activations of a group go through LDS, each
 //    wavefront keeps 4 groups of its own codes in flight in registers and
@@ -704,7 +706,8 @@ __global__ __launch_bounds__(256) void prefill_small(PrefillArgs g) {
 // ---------------------------------------------------------------------------
 // 128-row tiles: a workgroup of 4 wavefronts, 2 along M x 2 along N, each
 // computing 64 rows x 32 * NS columns of each of NM matrices with
-// v_mfma_f32_32x32x16_bf16.
+// v_mfma_f32_32x32x16_bf16.  int4: NM * NS = 2 (64 columns of gate and up,
+// or 128 of down, per workgroup); MXFP4: NM * NS = 4 (128, or 256).
 // ---------------------------------------------------------------------------
 
 template <int NM, int NS>
@@ -712,6 +715,13 @@ struct Big {
   static constexpr int kWaveCols = 32 * NS;
   static constexpr int kWgCols = 2 * kWaveCols;
   static constexpr int kTilesN = kWgCols / 64;            // packed 64-row tiles per matrix
+  static constexpr int kPieces = NM * kTilesN;            // 128-byte scale pieces per group
+  static constexpr int kRuns = kPieces / 2;               // 1 KB code runs per wavefront
+  // one stage: A, the codes, the scales, the row sums
+  static constexpr int kB = kPieces * 2048;
+  static constexpr int kS = kPieces * 128;
+  static constexpr int kBytes = kBigM * 128 + kB + kS + kBigM * 8;
+  static_assert(kPieces == 2 || kPieces == 4, "two or four scale pieces (one or two code runs per wavefront)");
 };
 
 // B operand of the correction: -136 at k = 0, 1, 2 (the three sum parts),
@@ -728,9 +738,10 @@ __device__ __forceinline__ bf16x8_t minus136_x3() {
 //    write is contiguous, so the layout is chosen by which segment each lane
 //    fetches; the swizzle keeps the 32-row fragment reads of the MFMAs free
 //    of bank conflicts without padding); the codes of the group
-//    [(mat * 2 + half) * kWgCols + column] x 16 bytes, as packed; the scales
-//    of the group, 128 bytes per packed 64-row tile; the row sums of the
-//    group, 8 bytes per row.
+//    [(mat * 2 + half) * kWgCols + column] x 16 bytes, as packed (one or two
+//    1 KB runs per wavefront); the scales of the group, 128 bytes per packed
+//    64-row tile (a quarter per wavefront); the row sums of the group, 8
+//    bytes per row.
 //  * Group g + 2 is fetched while group g is multiplied, into the stage group
 //    g - 1 used; the stages are three distinct LDS arrays and the loop is
 //    unrolled by three, so each read names its stage and the compiler's own
@@ -743,10 +754,6 @@ __device__ __forceinline__ bf16x8_t minus136_x3() {
 // ---------------------------------------------------------------------------
 
 constexpr int kSt2A = kBigM * 128;                      // A, 16 KB
-constexpr int kSt2B = 4096;                             // codes (NM * kTilesN * 2 KB)
-constexpr int kSt2S = 256;                              // scales: two 128-byte pieces
-constexpr int kSt2R = kBigM * 8;                        // row sums
-constexpr int kSt2Bytes = kSt2A + kSt2B + kSt2S + kSt2R;
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -766,14 +773,14 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // This lane's sources of group 0 (each advanced by the group index).
 struct Big2Src {
   const uint8_t* a[4];  // A: its 16-byte segment of row 8 * (4 * wv + j) + lane / 8
-  const uint8_t* b;     // codes: its 16 bytes of the wavefront's 1 KB run
-  const uint8_t* s;     // scales: its 16 bytes (lanes 0..3)
+  const uint8_t* b[2];  // codes: its 16 bytes of each of the wavefront's 1 KB runs
+  const uint8_t* s;     // scales: its 16 bytes (lanes 0..3, or 0..7 with four pieces)
   const uint8_t* r;     // row sums: its 4 bytes
 };
 
 // DMA instructions per group and wavefront.
-template <bool MX>
-constexpr int big2_dmas() { return 4 + 1 + 1 + (MX ? 0 : 1); }
+template <class C, bool MX>
+constexpr int big2_dmas() { return 4 + C::kRuns + 1 + (MX ? 0 : 1); }
 
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
@@ -795,15 +802,17 @@ __device__ __forceinline__ void dma4(const uint8_t* g, uint32_t lds) {
                : "memory", "m0");
 }
 
-template <bool MX>
+template <class C, bool MX>
 __device__ __forceinline__ void big2_issue(const Big2Src& src, int grp, uint8_t* st, int wv,
                                            int lane) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) dma16(src.a[j] + grp * 128, lds_addr(st + (wv * 4 + j) * 1024));
-  dma16(src.b + grp * 2048, lds_addr(st + kSt2A + wv * 1024));
-  if (lane < 4)
-    dma16(src.s + grp * 128, lds_addr(st + kSt2A + kSt2B + (wv >> 1) * 128 + (wv & 1) * 64));
-  if constexpr (!MX) dma4(src.r + grp * 8, lds_addr(st + kSt2A + kSt2B + kSt2S + wv * 256));
+#pragma unroll
+  for (int u = 0; u < C::kRuns; ++u)
+    dma16(src.b[u] + grp * 2048, lds_addr(st + kSt2A + (wv * C::kRuns + u) * 1024));
+  // each wavefront fetches a quarter of the scales (64 or 128 bytes)
+  if (lane < C::kS / 64) dma16(src.s + grp * 128, lds_addr(st + kSt2A + C::kB + wv * C::kS / 4));
+  if constexpr (!MX) dma4(src.r + grp * 8, lds_addr(st + kSt2A + C::kB + C::kS + wv * 256));
 }
 
 template <int NM, int NS, bool MX, bool WIDE>
@@ -820,13 +829,13 @@ __device__ __forceinline__ void big2_math(const uint8_t* st, int wm, int wn, int
     if constexpr (MX) continue;
     // -136 * (row sums of the group): one MFMA per row block from the sum
     // parts of the lane's row (the lanes of the upper K half pass zeros)
-    const u32x2_t rs = *reinterpret_cast<const u32x2_t*>(st + kSt2A + kSt2B + kSt2S + r * 8);
+    const u32x2_t rs = *reinterpret_cast<const u32x2_t*>(st + kSt2A + C::kB + C::kS + r * 8);
     const u32x4_t op = half ? u32x4_t{0u, 0u, 0u, 0u} : u32x4_t{rs.x, rs.y, 0u, 0u};
     corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, op),
                                                       minus136_x3(), f32x16_t{}, 0, 0, 0);
   }
   const uint8_t* bq = st + kSt2A;
-  const uint8_t* sc = st + kSt2A + kSt2B;
+  const uint8_t* sc = st + kSt2A + C::kB;
   auto bword = [&](int mat, int n) -> u32x4_t {
     return *reinterpret_cast<const u32x4_t*>(bq + ((mat * 2 + half) * C::kWgCols + n) * 16);
   };
@@ -910,10 +919,9 @@ __device__ __forceinline__ void big2_math(const uint8_t* st, int wm, int wn, int
 template <int NM, int NS, bool DOWN, bool MX>
 __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   using C = Big<NM, NS>;
-  static_assert(NM * C::kTilesN == 2, "two 128-byte scale pieces and four 1 KB code runs");
-  __shared__ __align__(16) uint8_t st0[kSt2Bytes];
-  __shared__ __align__(16) uint8_t st1[kSt2Bytes];
-  __shared__ __align__(16) uint8_t st2[kSt2Bytes];
+  __shared__ __align__(16) uint8_t st0[C::kBytes];
+  __shared__ __align__(16) uint8_t st1[C::kBytes];
+  __shared__ __align__(16) uint8_t st2[C::kBytes];
   const int N = DOWN ? g.d : g.f, K = DOWN ? g.f : g.d;
   int ti, cblk;
   if (!xcd_item(__builtin_amdgcn_readfirstlane(g.n_big[0]), (N + C::kWgCols - 1) / C::kWgCols, ti,
@@ -954,14 +962,22 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
       row_src(m0 + r, rp, sp);
       src.a[j] = rp + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
     }
-    // codes: piece wv = (mat * 2 + half) * kTilesN + tt
-    const int tt = min(wv % C::kTilesN, ntv - 1), hh = (wv / C::kTilesN) & 1,
-              mat = wv / (2 * C::kTilesN);
-    src.b = sl.blk + qoff[mat] + static_cast<size_t>(n0 / 64 + tt) * 32 * K + hh * 1024 + lane * 16;
-    // scales: piece wv / 2 = mat * kTilesN + tt, 64-byte half wv % 2
-    const int ps = wv >> 1, smat = ps / C::kTilesN;
+    // codes: runs pc = wv * kRuns + u = (mat * 2 + half) * kTilesN + tt
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pc = min(wv * C::kRuns + u, 4 * C::kRuns - 1);
+      const int tt = min(pc % C::kTilesN, ntv - 1), hh = (pc / C::kTilesN) & 1,
+                mat = pc / (2 * C::kTilesN);
+      src.b[u] = sl.blk + qoff[mat] + static_cast<size_t>(n0 / 64 + tt) * 32 * K + hh * 1024 +
+                 lane * 16;
+    }
+    // scales: quarter wv of the kPieces pieces (piece ps = mat * kTilesN + tt;
+    // two quarters per piece with two pieces, one with four)
+    const int ps = wv * C::kPieces / 4, smat = ps / C::kTilesN;
     const int spt = min(n0 / 64 + ps % C::kTilesN, N / 64 - 1);
-    src.s = sl.blk + soff[smat] + static_cast<size_t>(spt) * groups * 128 + (wv & 1) * 64 + lane * 16;
+    const int sq = C::kPieces == 2 ? (wv & 1) * 64 : 0;  // byte offset of the quarter in its piece
+    src.s = sl.blk + soff[smat] + static_cast<size_t>(spt) * groups * 128 + sq +
+            min(lane, C::kS / 64 - 1) * 16;
     // row sums: 4-byte part (wv * 64 + lane) & 1 of row (wv * 64 + lane) / 2
     const int d = wv * 64 + lane;
     const uint8_t* rp;
@@ -974,7 +990,7 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
   bool wide = false;
   if constexpr (MX) {
     const int run = groups * 128;  // bytes per piece
-    for (int e = t * 16; e < 2 * run; e += 256 * 16) {
+    for (int e = t * 16; e < C::kPieces * run; e += 256 * 16) {
       const int ps = e / run, smat = ps / C::kTilesN;
       const int spt = min(n0 / 64 + ps % C::kTilesN, N / 64 - 1);
       const uint4 v = *reinterpret_cast<const uint4*>(sl.blk + soff[smat] +
@@ -992,11 +1008,11 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
       for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][mat][ns][e] = 0.0f;
-  constexpr int kD = big2_dmas<MX>();
+  constexpr int kD = big2_dmas<C, MX>();
   auto main_loop = [&](auto wide_tag) {
     constexpr bool W = decltype(wide_tag)::value;
-    big2_issue<MX>(src, 0, st0, wv, lane);
-    big2_issue<MX>(src, min(1, groups - 1), st1, wv, lane);
+    big2_issue<C, MX>(src, 0, st0, wv, lane);
+    big2_issue<C, MX>(src, min(1, groups - 1), st1, wv, lane);
     // step of group grp in stage `cur`: its fetches done (the next group's
     // may still run), every wavefront done with the previous group (whose
     // stage `nxt2` receives group grp + 2), then the math
@@ -1004,7 +1020,7 @@ __global__ __launch_bounds__(256) void prefill_big(PrefillArgs g) {
       wait_vm_lgkm0<kD>();
       __builtin_amdgcn_s_barrier();
       big2_math<NM, NS, MX, W>(cur, wm, wn, col, half, acc);
-      big2_issue<MX>(src, min(grp + 2, groups - 1), nxt2, wv, lane);
+      big2_issue<C, MX>(src, min(grp + 2, groups - 1), nxt2, wv, lane);
     };
     for (int g0 = 0; g0 < groups; g0 += 3) {
       step(g0, st0, st2);
@@ -1093,10 +1109,12 @@ template <bool MX>
 hipError_t prefill_kernels(const FfnProblem& p, const PrefillArgs& g, hipStream_t stream) {
   const int ms = max_small(p.T, p.k, g.slots, p.has_shared);
   const int mb = max_big(p.T, p.k, p.has_shared);
-  // gate/up: 64 columns of both matrices per workgroup, down: 128 columns
-  // (three LDS stages of 21.3 KB each; two workgroups per CU)
-  using GU = Big<2, 1>;
-  using DN = Big<1, 2>;
+  // int4: gate/up 64 columns of both matrices per workgroup, down 128
+  // (three LDS stages of 21.3 KB each; two workgroups per CU).  MXFP4 blocks,
+  // with no scale multiply-adds, fit twice the columns in two waves per SIMD:
+  // 128 and 256 (stages of 25.5 KB).
+  using GU = Big<2, MX ? 2 : 1>;
+  using DN = Big<1, MX ? 4 : 2>;
   hipError_t err;
   if ((err = launch(prefill_tiles, dim3(1), dim3(1024), 0, stream, g)) != hipSuccess) return err;
   // 1-D grids: enough workgroups for the largest possible tile lists, in
@@ -1113,13 +1131,13 @@ hipError_t prefill_kernels(const FfnProblem& p, const PrefillArgs& g, hipStream_
                   stream, src, rows, K, dst);
   };
   if (!MX && (err = rowsums(g.x, p.T, p.d, g.sum_x)) != hipSuccess) return err;
-  err = launch(prefill_big<2, 1, false, MX>, grid(mb, cgu), dim3(256), 0, stream, g);
+  err = launch(prefill_big<2, GU::kWaveCols / 32, false, MX>, grid(mb, cgu), dim3(256), 0, stream, g);
   if (err != hipSuccess) return err;
   err = launch(prefill_small<2, kSmallNSubGU, false, MX>, grid(ms, sgu), dim3(256), 0, stream, g);
   if (err != hipSuccess) return err;
   if (!MX && (err = rowsums(g.h, rows_of(p.T, p.k, p.has_shared), p.f, g.sum_h)) != hipSuccess)
     return err;
-  err = launch(prefill_big<1, 2, true, MX>, grid(mb, cdn), dim3(256), 0, stream, g);
+  err = launch(prefill_big<1, DN::kWaveCols / 32, true, MX>, grid(mb, cdn), dim3(256), 0, stream, g);
   if (err != hipSuccess) return err;
   return launch(prefill_small<1, kSmallNSubDN, true, MX>, grid(ms, sdn), dim3(256), 0, stream, g);
 }
