@@ -19,8 +19,9 @@
 //    (int4) or 64 or 128 columns (MXFP4, which has no per-group scale
 //    multiply-adds and so the registers for twice the columns) with
 //    v_mfma_f32_32x32x16_bf16.
-//  * 32-row tiles (the many experts with a handful of tokens): bound by the
-//    weight stream.  The activations of a group go through LDS, each
+//  * 32-row tiles (the many experts with a handful of tokens): they stream
+//    the weights, one read per tile, and are held by issue and latency on
+//    their CUs (the vector ALUs and the waits) more than by HBM.  The activations of a group go through LDS, each
 //    wavefront keeps 4 groups of its own codes in flight in registers and
 //    multiplies both 16-row blocks with v_mfma_f32_16x16x32_bf16.
 // The weights are read once per tile; the codes go from memory straight to
@@ -299,8 +300,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ int out_row(int i, int half) { return (i >> 2) * 8 + half * 4 + (i & 3); }
 
 // ---------------------------------------------------------------------------
-// 32-row tiles (small experts and the rows big tiles leave): bound by the
-// weight stream.  The workgroup stages the tile's activations for one
+// 32-row tiles (small experts and the rows big tiles leave): they stream
+// their weights at ~4.5 TB/s but are held by issue and latency on their CUs
+// (their time grows almost in proportion when they are given fewer CUs).
+// The workgroup stages the tile's activations for one
 // 64-column group at a time in LDS (double-buffered, with each row's sum);
 // every wavefront owns 16*NSUB columns of each of NM matrices, keeps kRing
 // groups of its codes in flight in registers, and multiplies both 16-row
