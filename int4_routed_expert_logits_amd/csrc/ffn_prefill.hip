@@ -20,8 +20,8 @@
 //    multiply-adds and so the registers for twice the columns) with
 //    v_mfma_f32_32x32x16_bf16.
 //  * 32-row tiles (the many experts with a handful of tokens): they stream
-//    the weights, one read per tile, and are held by issue and latency on
-//    their CUs (the vector ALUs and the waits) more than by HBM.  The activations of a group go through LDS, each
+//    the weights, one read per tile, near the read rate their access
+//    pattern reaches, with the vector ALUs about half busy.  The activations of a group go through LDS, each
 //    wavefront keeps 4 groups of its own codes in flight in registers and
 //    multiplies both 16-row blocks with v_mfma_f32_16x16x32_bf16.
 // The weights are read once per tile; the codes go from memory straight to
@@ -301,8 +301,9 @@ __device__ __forceinline__ int out_row(int i, int half) { return (i >> 2) * 8 + 
 
 // ---------------------------------------------------------------------------
 // 32-row tiles (small experts and the rows big tiles leave): they stream
-// their weights at ~4.5 TB/s but are held by issue and latency on their CUs
-// (their time grows almost in proportion when they are given fewer CUs).
+// their weights at ~4.5-4.9 TB/s, near the read rate their access pattern
+// reaches on the whole GPU, and on fewer CUs they are held by issue and
+// latency (their time then grows almost in proportion).
 // The workgroup stages the tile's activations for one
 // 64-column group at a time in LDS (double-buffered, with each row's sum);
 // every wavefront owns 16*NSUB columns of each of NM matrices, keeps kRing
