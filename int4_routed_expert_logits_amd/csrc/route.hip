@@ -104,8 +104,9 @@ __global__ __launch_bounds__(256) void logits_split(const void* __restrict__ x,
 // workgroup computes 64 tokens x 128 experts over one of P parts of d, each
 // wavefront 64 tokens x 32 experts as 4 x 2 tiles of 16 x 16.  x and w are
 // staged in LDS in their own types, 32 columns at a time (the next chunk's
-// loads in flight during the current one's MFMAs), and widened to float64 --
-// exactly -- as each operand is read.  Operand layout of the 16x16x4 f64
+// loads in flight during the current one's MFMAs); each lane reads its eight
+// columns of a row with one vector read and widens them to float64 --
+// exactly -- one per MFMA step.  Operand layout of the 16x16x4 f64
 // MFMA: lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]; it receives
 // D[l / 16 + 4 * v][l % 16], v = 0..3.  Parts are multiples of 32 columns.
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
@@ -179,18 +180,49 @@ __global__ __launch_bounds__(256) void logits_mfma(const void* __restrict__ x,
   for (int k0 = k_begin; k0 < k_end; k0 += kMK) {
     const bool more = k0 + kMK < k_end;
     if (more) load(k0 + kMK);
+    // lane (fr, fk) takes columns 8 fk .. 8 fk + 7 of the chunk, one per
+    // MFMA step (step s multiplies columns s, 8 + s, 16 + s, 24 + s), so its
+    // operands are one contiguous LDS read per row
+    XT xa[4][8];
+    float wb[2][8];
 #pragma unroll
-    for (int kk = 0; kk < kMK; kk += 4) {
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (sizeof(XT) == 2) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&sh.x[buf][i * 16 + fr][8 * fk]);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xa[i][2 * q] = static_cast<XT>(u[q] & 0xFFFFu);
+          xa[i][2 * q + 1] = static_cast<XT>(u[q] >> 16);
+        }
+      } else {
+        const float4 v0 = *reinterpret_cast<const float4*>(&sh.x[buf][i * 16 + fr][8 * fk]);
+        const float4 v1 = *reinterpret_cast<const float4*>(&sh.x[buf][i * 16 + fr][8 * fk + 4]);
+        const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xa[i][q] = f[q];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float4 v0 = *reinterpret_cast<const float4*>(&sh.w[buf][wv * 32 + j * 16 + fr][8 * fk]);
+      const float4 v1 = *reinterpret_cast<const float4*>(&sh.w[buf][wv * 32 + j * 16 + fr][8 * fk + 4]);
+      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wb[j][q] = f[q];
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
       double a[4], b[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (sizeof(XT) == 2)
-          a[i] = static_cast<double>(bf16_to_f32(sh.x[buf][i * 16 + fr][kk + fk]));
+          a[i] = static_cast<double>(bf16_to_f32(xa[i][st]));
         else
-          a[i] = static_cast<double>(sh.x[buf][i * 16 + fr][kk + fk]);
+          a[i] = static_cast<double>(xa[i][st]);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = static_cast<double>(sh.w[buf][wv * 32 + j * 16 + fr][kk + fk]);
+      for (int j = 0; j < 2; ++j) b[j] = static_cast<double>(wb[j][st]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
