@@ -2,13 +2,17 @@
 // expert needed by several positions of one batch is read once; "capability
 // 3" -- a worker receives one layer's routed batch-union and runs the FFN).
 //
-// One workgroup of 1024 threads does the whole grouping in LDS: a histogram
-// of the T*k routing slots per expert, an exclusive scan into offsets, the
-// active-expert list, then a stable counting sort of the slots.  Slots are
-// taken in chunks of 1024 in id order; inside a chunk each wavefront ranks its
-// lanes among equal keys with ballots, and wavefronts are ordered by a
-// per-chunk table of per-wave key counts, so the permutation is the stable
-// one regardless of the order in which hardware atomics land.
+// One workgroup of 1024 threads does the whole grouping in LDS: a stable
+// counting sort of the T*k routing slots by expert.  Each of the 16
+// wavefronts owns a contiguous range of the slots.  It counts its slots per
+// expert (a step of 64 slots ranks each lane among the lanes with the same
+// expert by ballots, and the expert's lowest lane adds their number); a
+// prefix over the wavefronts per expert and an exclusive scan over the
+// experts give the offsets, the active-expert list and each wavefront's first
+// position per expert; then each wavefront walks its range again in slot
+// order and places every slot at its expert's next position plus its rank.
+// No atomics, three barriers between the phases, and the permutation is the
+// stable one by construction.
 #include "common.h"
 #include "launch.h"
 #include "union_wave.h"
@@ -20,6 +24,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxE = 1024;
+constexpr int kKeys = 16;  // slot keys a lane holds at a time
 
 // Exclusive scan of n <= 2 * kThreads ints in LDS (in place), returns the
 // total.
@@ -65,32 +70,48 @@ __global__ __launch_bounds__(kThreads) void batch_union(const int32_t* __restric
                                                         int32_t* __restrict__ active,
                                                         int32_t* __restrict__ n_active) {
   __shared__ int cnt[kMaxE];
-  __shared__ int start[kMaxE];    // next free grouped position per expert
+  __shared__ int start[kMaxE];    // the experts' counts, then their offsets
   __shared__ int flag[kMaxE];
   __shared__ int scan_tmp[kWaves];
-  extern __shared__ int dyn[];
-  int* wave_cnt = dyn;            // [kWaves][E] slots of the chunk per wave and expert
-  int* wave_pre = dyn + kWaves * E;  // [kWaves][E] first grouped position of each
+  extern __shared__ int tab[];    // [kWaves][E]: slots per wavefront and expert, then the
+                                  // wavefront's next grouped position per expert
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-
-  for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
-  for (int i = tid; i < kWaves * E; i += kThreads) wave_cnt[i] = 0;
+  const int nbits = key_bits(E);
+  // wavefront wv owns the slots [s0, s0 + 64 * spw), whole 64-slot steps
+  const int spw = ((n + 63) / 64 + kWaves - 1) / kWaves;
+  const int s0 = wv * spw * 64;
+  for (int i = tid; i < kWaves * E; i += kThreads) tab[i] = 0;
   __syncthreads();
-  // histogram: four keys per thread in flight at a time
-  for (int s0 = tid; s0 < n; s0 += 4 * kThreads) {
-    int e[4];
+  // counts per wavefront and expert: in each step the expert's lowest lane
+  // adds the lanes that share it (16 keys in flight per lane)
+  for (int b0 = 0; b0 < spw; b0 += kKeys) {
+    int key[kKeys];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) e[u] = key_of(topk_idx, s0 + u * kThreads, n, E);
+    for (int u = 0; u < kKeys; ++u) key[u] = key_of(topk_idx, s0 + (b0 + u) * 64 + lane, n, E);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (e[u] >= 0) atomicAdd(&cnt[e[u]], 1);
+    for (int u = 0; u < kKeys; ++u) {
+      if (b0 + u >= spw) break;  // (uniform)
+      const bool valid = key[u] >= 0;
+      const uint64_t same = match_key(key[u], valid, nbits);
+      if (valid && __popcll(same & ((1ull << lane) - 1ull)) == 0)
+        tab[wv * E + key[u]] += __popcll(same);
+    }
   }
   __syncthreads();
+  // per expert: exclusive prefix over the wavefronts, and the total
   for (int e = tid; e < E; e += kThreads) {
-    counts[e] = cnt[e];
-    start[e] = cnt[e];
-    flag[e] = cnt[e] > 0 ? 1 : 0;
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = tab[w * E + e];
+      tab[w * E + e] = run;
+      run += c;
+    }
+    counts[e] = run;
+    cnt[e] = run;
+    start[e] = run;
+    flag[e] = run > 0 ? 1 : 0;
   }
   __syncthreads();
   const int total = block_exclusive_scan(start, E, scan_tmp);
@@ -98,6 +119,8 @@ __global__ __launch_bounds__(kThreads) void batch_union(const int32_t* __restric
   for (int e = tid; e < E; e += kThreads) {
     offsets[e] = start[e];
     if (cnt[e] > 0) active[flag[e]] = e;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tab[w * E + e] += start[e];
   }
   for (int i = n_act + tid; i < E; i += kThreads) active[i] = -1;
   if (tid == 0) {
@@ -105,49 +128,32 @@ __global__ __launch_bounds__(kThreads) void batch_union(const int32_t* __restric
     n_active[0] = n_act;
   }
   __syncthreads();
-
-  // Stable placement, one chunk of kThreads slots at a time (the next
-  // chunk's keys are loaded while this one is placed).  A slot's position is
-  // its expert's next free position, plus the expert's slots in lower
-  // wavefronts of the chunk, plus its rank among the lower lanes of its own
-  // wavefront with the same expert.
-  const int nbits = key_bits(E);
-  int e_next = key_of(topk_idx, tid, n, E);
-  for (int c0 = 0; c0 < n; c0 += kThreads) {
-    const int s = c0 + tid;
-    const int e = e_next;
-    e_next = key_of(topk_idx, s + kThreads, n, E);
-    const bool valid = e >= 0;
-    const uint64_t same = match_key(e, valid, nbits);
-    const int rank = __popcll(same & ((1ull << lane) - 1ull));
-    // the expert's lowest lane in the wavefront writes its count
-    if (valid && rank == 0) wave_cnt[wv * E + e] = __popcll(same);
-    __syncthreads();
-    // per expert: exclusive prefix over the wavefronts, from its next free
-    // position
-    for (int ee = tid; ee < E; ee += kThreads) {
-      int run = start[ee];
+  // Stable placement: each wavefront walks its slots in order; a slot goes
+  // to its expert's next position for this wavefront plus its rank among the
+  // lower lanes of its step with the same expert, and the expert's lowest
+  // lane then advances that position past the step's lanes.
+  for (int b0 = 0; b0 < spw; b0 += kKeys) {
+    int key[kKeys];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        wave_pre[w * E + ee] = run;
-        run += wave_cnt[w * E + ee];
-      }
-      start[ee] = run;
-    }
-    __syncthreads();
-    if (s < n) {
+    for (int u = 0; u < kKeys; ++u) key[u] = key_of(topk_idx, s0 + (b0 + u) * 64 + lane, n, E);
+#pragma unroll
+    for (int u = 0; u < kKeys; ++u) {
+      if (b0 + u >= spw) break;  // (uniform)
+      const int s = s0 + (b0 + u) * 64 + lane;
+      const bool valid = key[u] >= 0;
+      const uint64_t same = match_key(key[u], valid, nbits);
+      const int rank = __popcll(same & ((1ull << lane) - 1ull));
       if (valid) {
-        const int pos = wave_pre[wv * E + e] + rank;
+        const int pos = tab[wv * E + key[u]] + rank;
         perm[pos] = s;
         inv_perm[s] = pos;
-      } else {
+      } else if (s < n) {
         inv_perm[s] = -1;
       }
+      __builtin_amdgcn_wave_barrier();
+      if (valid && rank == 0) tab[wv * E + key[u]] += __popcll(same);
+      __builtin_amdgcn_wave_barrier();
     }
-    // the lane of rank 0 of each expert in a wavefront is the one that wrote
-    // its count: it clears it for the next chunk
-    if (valid && rank == 0) wave_cnt[wv * E + e] = 0;
-    __syncthreads();
   }
 }
 
@@ -181,7 +187,7 @@ hipError_t launch_union(int n_slots, int E, const int32_t* topk_idx, int32_t* co
     return launch(batch_union_small<16>, dim3(1), dim3(64), 0, stream, topk_idx, n_slots, E,
                   counts, offsets, perm, inv_perm, active, n_active);
   }
-  const int lds = 2 * kWaves * E * static_cast<int>(sizeof(int));
+  const int lds = kWaves * E * static_cast<int>(sizeof(int));
   if (lds > 48 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(batch_union),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
