@@ -5,14 +5,14 @@
 // One workgroup of 1024 threads does the whole grouping in LDS: a stable
 // counting sort of the T*k routing slots by expert.  Each of the 16
 // wavefronts owns a contiguous range of the slots.  It counts its slots per
-// expert (a step of 64 slots ranks each lane among the lanes with the same
-// expert by ballots, and the expert's lowest lane adds their number); a
-// prefix over the wavefronts per expert and an exclusive scan over the
+// expert (LDS atomic adds: a count does not depend on the order they land
+// in); a prefix over the wavefronts per expert and an exclusive scan over the
 // experts give the offsets, the active-expert list and each wavefront's first
 // position per expert; then each wavefront walks its range again in slot
-// order and places every slot at its expert's next position plus its rank.
-// No atomics, three barriers between the phases, and the permutation is the
-// stable one by construction.
+// order and places every slot at its expert's next position plus its rank
+// among the lanes of its 64-slot step with the same expert (ballots).  Three
+// barriers between the phases, and the permutation is the stable one by
+// construction.
 #include "common.h"
 #include "launch.h"
 #include "union_wave.h"
@@ -83,20 +83,16 @@ __global__ __launch_bounds__(kThreads) void batch_union(const int32_t* __restric
   const int s0 = wv * spw * 64;
   for (int i = tid; i < kWaves * E; i += kThreads) tab[i] = 0;
   __syncthreads();
-  // counts per wavefront and expert: in each step the expert's lowest lane
-  // adds the lanes that share it (16 keys in flight per lane)
+  // counts per wavefront and expert: LDS atomic adds (counts do not depend
+  // on the order the adds land in; 16 keys in flight per lane)
   for (int b0 = 0; b0 < spw; b0 += kKeys) {
     int key[kKeys];
 #pragma unroll
-    for (int u = 0; u < kKeys; ++u) key[u] = key_of(topk_idx, s0 + (b0 + u) * 64 + lane, n, E);
+    for (int u = 0; u < kKeys; ++u)  // (steps past the wavefront's range are not its slots)
+      key[u] = b0 + u < spw ? key_of(topk_idx, s0 + (b0 + u) * 64 + lane, n, E) : -1;
 #pragma unroll
-    for (int u = 0; u < kKeys; ++u) {
-      if (b0 + u >= spw) break;  // (uniform)
-      const bool valid = key[u] >= 0;
-      const uint64_t same = match_key(key[u], valid, nbits);
-      if (valid && __popcll(same & ((1ull << lane) - 1ull)) == 0)
-        tab[wv * E + key[u]] += __popcll(same);
-    }
+    for (int u = 0; u < kKeys; ++u)
+      if (key[u] >= 0) atomicAdd(&tab[wv * E + key[u]], 1);
   }
   __syncthreads();
   // per expert: exclusive prefix over the wavefronts, and the total
