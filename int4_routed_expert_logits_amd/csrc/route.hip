@@ -119,6 +119,10 @@ struct MfmaLogitsLds {
   static constexpr int kWLd = kMK + kWPad;
   XT x[2][kMT][kXLd];
   float w[2][kME][kWLd];
+  // each lane reads 8 consecutive columns of a row as 16-byte pieces
+  static_assert(kXLd * sizeof(XT) % 16 == 0 && kWLd * sizeof(float) % 16 == 0 &&
+                    sizeof(x) % 16 == 0 && kMK == 32,
+                "16-byte aligned rows, four lanes of 8 columns per chunk");
 };
 
 template <typename XT>
