@@ -234,8 +234,11 @@ def test_union_parity_on_workload_routing(cfg, T):
     check_union(idx, L.shape.n_experts)
 
 
+# (65, 1, ...): one slot past the one-wavefront kernel; (3000, 6, ...) and
+# (6250, 8, ...): wavefront ranges longer than one block of held keys
 @pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (1000, 1, 8, 1), (100, 32, 1024, 2),
-                                        (777, 8, 256, 3), (3000, 6, 40, 4), (513, 2, 3, 5)])
+                                        (777, 8, 256, 3), (3000, 6, 40, 4), (513, 2, 3, 5),
+                                        (65, 1, 7, 6), (6250, 8, 256, 7)])
 def test_union_parity_random(T, k, E, seed):
     say(f"union random T={T} k={k} E={E}")
     rng = np.random.default_rng(seed)
