@@ -66,10 +66,21 @@ typedef enum {
   MOE_ERR_ALIGN = 4,       /* a pointer is not aligned as documented          */
   MOE_ERR_UNSUPPORTED = 5, /* well-formed but not provided (e.g. group 16)    */
   MOE_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required      */
-  MOE_ERR_HIP = 7          /* a HIP launch failed                             */
+  MOE_ERR_HIP = 7,         /* a HIP launch failed                             */
+  /* The *_INT_MIN_ / *_INT_MAX_ members of this and the enums below are not
+   * values to pass or expect: they give each type the range of a 32-bit int,
+   * so that the (C++) implementation may hold whatever int a C caller passes
+   * and reject it with a status instead of having undefined behaviour. */
+  MOE_STATUS_INT_MIN_ = -2147483647 - 1,
+  MOE_STATUS_INT_MAX_ = 2147483647
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_DTYPE_INT_MIN_ = -2147483647 - 1,
+  MOE_DTYPE_INT_MAX_ = 2147483647
+} moe_dtype;
 
 /* Which expert-FFN kernel family runs (moe_expert_ffn):
  *  DECODE_F32    HBM-bound int4 GEMV for small batches; activations bf16 or
@@ -77,12 +88,22 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *  PREFILL_BF16  grouped GEMM on bf16 MFMA for large batches; activations
  *                must be bf16; h, y and y_shared are bfloat16 (fp32
  *                accumulation).  An f32 x is rejected, never rounded. */
-typedef enum { MOE_PATH_DECODE_F32 = 0, MOE_PATH_PREFILL_BF16 = 1 } moe_path;
+typedef enum {
+  MOE_PATH_DECODE_F32 = 0,
+  MOE_PATH_PREFILL_BF16 = 1,
+  MOE_PATH_INT_MIN_ = -2147483647 - 1,
+  MOE_PATH_INT_MAX_ = 2147483647
+} moe_path;
 
 /* Scale granularity of moe_quantize: one float16 scale per 64 consecutive
  * input columns of a row (the layout every other call reads), or one per row
  * (for comparison only). */
-typedef enum { MOE_QUANT_GS64 = 0, MOE_QUANT_ROW = 1 } moe_quant_mode;
+typedef enum {
+  MOE_QUANT_GS64 = 0,
+  MOE_QUANT_ROW = 1,
+  MOE_QUANT_INT_MIN_ = -2147483647 - 1,
+  MOE_QUANT_INT_MAX_ = 2147483647
+} moe_quant_mode;
 
 /* Layer geometry.
  *  d          hidden size; multiple of 64, 64..8192
