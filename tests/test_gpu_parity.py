@@ -90,7 +90,9 @@ def min_gap(logits, k):
 # router
 # ----------------------------------------------------------------------------
 
-ROUTE_CASES = [(1, 4), (1, 3), (2, 1), (2, 16), (3, 64), (3, 5), (4, 1), (4, 8), (4, 33), (5, 2048)]
+# (1, 100): float32 x on the matrix-core path (more than 32 tokens)
+ROUTE_CASES = [(1, 4), (1, 3), (1, 100), (2, 1), (2, 16), (3, 64), (3, 5), (4, 1), (4, 8), (4, 33),
+               (5, 2048)]
 
 
 @pytest.mark.parametrize("cfg,T", ROUTE_CASES)
