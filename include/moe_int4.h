@@ -110,6 +110,8 @@ typedef enum {
  *  f          routed-expert intermediate size; multiple of 64, 64..8192
  *  n_experts  routed experts E, 1..1024
  *  top_k      experts per token k, 1..min(E, 32)
+ *             (every call taking T tokens: T >= 0 (MOE_ERR_SHAPE) and
+ *             T * top_k <= 2^24 (MOE_ERR_UNSUPPORTED))
  *  group      the expert block format, named by its quantisation group along
  *             the input dimension:
  *               64  int4 codes with a float16 scale per 64 elements (gs64,
@@ -205,7 +207,8 @@ moe_status moe_pack_experts(const moe_shape* shape, int64_t n_blocks, const uint
 moe_status moe_quantize(int32_t N, int32_t K, const void* w, moe_dtype w_dt, moe_quant_mode mode,
                         uint8_t* codes, void* scales, void* stream);
 
-/* Scratch bytes moe_route needs for T tokens (router logits, float64). */
+/* Scratch bytes moe_route needs for T tokens (router logits, float64); 0 for
+ * a shape the call rejects, T < 0 or T * top_k > 2^24. */
 size_t moe_route_workspace_bytes(const moe_shape* shape, int32_t T);
 
 /* Router: for every token t,
@@ -261,7 +264,8 @@ moe_status moe_route_union(const moe_shape* shape, int32_t T, const void* x, moe
                            int32_t* inv_perm, int32_t* active, int32_t* n_active,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Scratch bytes moe_expert_ffn needs for T tokens on `path`. */
+/* Scratch bytes moe_expert_ffn needs for T tokens on `path`; 0 for a shape
+ * or path the call rejects, T < 0 or T * top_k > 2^24. */
 size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path);
 
 /* Expert FFN over the batch-union: for every active expert e and each of its
@@ -313,8 +317,8 @@ moe_status moe_combine(const moe_shape* shape, int32_t T, const void* y, const v
                        moe_dtype y_dt, const int32_t* inv_perm, const float* topk_w, void* out,
                        moe_dtype out_dt, void* stream);
 
-/* Scratch bytes moe_layer_decode needs for T tokens (0 if the shape is
- * invalid). */
+/* Scratch bytes moe_layer_decode needs for T tokens; 0 for a shape the call
+ * rejects, T < 0 or T * top_k > 2^24. */
 size_t moe_layer_decode_workspace_bytes(const moe_shape* shape, int32_t T);
 
 /* The whole layer for a small decode batch -- moe_route_union, then
@@ -413,7 +417,8 @@ moe_status moe_cache_last_fetch(const moe_expert_cache* cache, int32_t capacity,
  * Calling it twice in a row changes nothing the second time. */
 moe_status moe_cache_unplan_last(moe_expert_cache* cache);
 
-/* Device scratch bytes of moe_cache_layer_decode (0 for an invalid shape). */
+/* Device scratch bytes of moe_cache_layer_decode; 0 for a shape the cache
+ * rejects, T < 0, n_slots < 1 or T * top_k > 1024. */
 size_t moe_cache_workspace_bytes(const moe_shape* shape, int32_t T, int32_t n_slots);
 
 /* One decode step of the layer through the cache: the router (as

@@ -56,6 +56,9 @@ moe_status check_tokens(const moe_shape* s, int32_t T) {
   return MOE_OK;
 }
 
+// The workspace sizes are 0 for a token count the calls reject.
+bool shape_tokens_ok(const moe_shape* s, int32_t T) { return check_tokens(s, T) == MOE_OK; }
+
 moe_status hip_status(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
   if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
@@ -154,7 +157,7 @@ moe_status moe_quantize(int32_t N, int32_t K, const void* w, moe_dtype w_dt, moe
 }
 
 size_t moe_route_workspace_bytes(const moe_shape* shape, int32_t T) {
-  if (check_shape(shape, true) != MOE_OK || T < 0) return 0;
+  if (check_shape(shape, true) != MOE_OK || !shape_tokens_ok(shape, T)) return 0;
   return round_up(moe::route_workspace(T, shape->d, shape->n_experts));
 }
 
@@ -225,7 +228,7 @@ moe_status moe_route_union(const moe_shape* shape, int32_t T, const void* x, moe
 }
 
 size_t moe_ffn_workspace_bytes(const moe_shape* shape, int32_t T, moe_path path) {
-  if (check_shape(shape, true) != MOE_OK || T < 0) return 0;
+  if (check_shape(shape, true) != MOE_OK || !shape_tokens_ok(shape, T)) return 0;
   const bool sh = shape->f_shared != 0;
   if (path == MOE_PATH_DECODE_F32)
     return round_up(moe::ffn_decode_workspace(T, shape->top_k, shape->n_experts, shape->d,
@@ -304,7 +307,7 @@ moe_status moe_combine(const moe_shape* shape, int32_t T, const void* y, const v
 }
 
 size_t moe_layer_decode_workspace_bytes(const moe_shape* shape, int32_t T) {
-  if (check_shape(shape) != MOE_OK || T < 0) return 0;
+  if (check_shape(shape) != MOE_OK || !shape_tokens_ok(shape, T)) return 0;
   return moe_route_workspace_bytes(shape, T) + moe_ffn_workspace_bytes(shape, T, MOE_PATH_DECODE_F32);
 }
 

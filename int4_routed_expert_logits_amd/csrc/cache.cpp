@@ -298,7 +298,9 @@ moe_status moe_cache_unplan_last(moe_expert_cache* cache) {
 }
 
 size_t moe_cache_workspace_bytes(const moe_shape* shape, int32_t T, int32_t n_slots) {
-  if (check_cache_shape(shape) != MOE_OK || T < 0 || n_slots < 1) return 0;
+  if (check_cache_shape(shape) != MOE_OK || T < 0 || n_slots < 1 ||
+      static_cast<int64_t>(T) * shape->top_k > kMaxCacheSlots)
+    return 0;
   return cache_ws(*shape, T, n_slots).total;
 }
 

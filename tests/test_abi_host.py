@@ -72,6 +72,28 @@ def test_workspace_sizes(lib):
     assert moe.moe_route_workspace_bytes(shp(group=32), 4) == moe.moe_route_workspace_bytes(shp(), 4)
 
 
+def test_workspace_sizes_are_zero_for_token_counts_the_calls_reject(lib):
+    """T * top_k may reach 2^24: the sizes there are exact (size_t, no 32-bit
+    wrap), and one token more, or T < 0, gives 0 from every size function."""
+    s = shp(8192, 8192, 1024, 32, 64, 8192)
+    T = (1 << 24) // 32
+    rows = T * 32 + T  # routed slots plus the shared expert's rows
+    # the matrix-core router's parts of d: d / 768, at most 4 for E > 512
+    assert moe.moe_route_workspace_bytes(s, T) == T * 1024 * 4 * 8
+    assert moe.moe_ffn_workspace_bytes(s, T, moe.MOE_PATH_PREFILL_BF16) >= rows * 8192 * 2 > 2**38
+    assert moe.moe_ffn_workspace_bytes(s, T, moe.MOE_PATH_DECODE_F32) > 0
+    assert moe.moe_layer_decode_workspace_bytes(s, T) > 0
+    for t in (T + 1, -1):
+        assert moe.moe_route_workspace_bytes(s, t) == 0
+        assert moe.moe_ffn_workspace_bytes(s, t, moe.MOE_PATH_DECODE_F32) == 0
+        assert moe.moe_ffn_workspace_bytes(s, t, moe.MOE_PATH_PREFILL_BF16) == 0
+        assert moe.moe_layer_decode_workspace_bytes(s, t) == 0
+    # the cache's limit is T * top_k <= 1024
+    assert moe.moe_cache_workspace_bytes(s, 32, 64) > 0
+    assert moe.moe_cache_workspace_bytes(s, 33, 64) == 0
+    assert moe.moe_cache_workspace_bytes(s, -1, 64) == 0
+
+
 def test_status_strings(lib):
     for code in range(8):
         assert moe.moe_status_str(code)
