@@ -64,7 +64,7 @@ class LayerShape:
 # The five workloads: tiny parity layer, small-expert decode layer,
 # many-small-experts layer with a shared expert and skewed routing, the
 # ~19 MB-expert layer for decode, and the same layer for 2048-token prefill;
-# plus one more parity-test layer (6).
+# plus parity-test layers (6, 7).
 WORKLOADS = {
     1: dict(shape=LayerShape(512, 256, 8, 2, 0, False, "f32"), tokens=(4,)),
     2: dict(shape=LayerShape(2048, 1024, 64, 8, 0, False, "bf16"), tokens=(1, 16)),
@@ -78,6 +78,12 @@ WORKLOADS = {
     # bias, experts of well over 96 rows, so the 128-row prefill tiles are
     # checked against the full oracle.
     6: dict(shape=LayerShape(320, 192, 8, 2, 192, True, "bf16"), tokens=(512,)),
+    # A parity-test layer at the largest hidden and intermediate sizes the
+    # library takes (8192 each; 107 MB per expert block): four routed experts
+    # top-2 with a Zipf bias plus a shared expert, so a few tokens reach the
+    # longest rows on the decode path, and 160 tokens give experts of more
+    # than 96 rows (128-row prefill tiles) next to 32-row tiles.
+    7: dict(shape=LayerShape(8192, 8192, 4, 2, 8192, True, "bf16"), tokens=(3, 160)),
 }
 # Workload 5 runs on workload 4's layer (same router weights and expert
 # blocks); only its Zipf router bias and its token batches are its own.

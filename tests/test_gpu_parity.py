@@ -124,6 +124,33 @@ def test_route_parity(cfg, T):
     assert np.max(np.abs(glg - lg)) <= 1e-12 * max(1.0, np.max(np.abs(lg)))
 
 
+@pytest.mark.parametrize("T", [1, 7, 40])
+def test_route_parity_largest_router(T):
+    """The largest router the library takes: E = 1024 experts, top_k = 32,
+    d = 8192, with a router bias; T = 1 and 7 on the split kernel, 40 on
+    the matrix-core kernel, and the top-k kernels' form for E > 512.  Then
+    moe_union on the routing, all against the oracle."""
+    say(f"route E=1024 k=32 d=8192 T={T}")
+    E, k, d = 1024, 32, 8192
+    rng = np.random.default_rng(8192 + T)
+    xb = synth.bf16_round(rng.standard_normal((T, d)).astype(np.float32))
+    xf = synth.bf16_to_f32(xb)
+    wr = (rng.standard_normal((E, d)) * 0.02).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    sh = moe.Shape(d, 64, E, k, 64, 0)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_route_workspace_bytes(sh, T), dtype=torch.uint8, device="cuda")
+    moe.moe_route(sh, dev_x(xb), torch.from_numpy(wr).cuda(), torch.from_numpy(bias).cuda(),
+                  idx, w, ws)
+    torch.cuda.synchronize()
+    ridx, rw, lg = oracle.route(xf, wr, bias, k)
+    gap = min_gap(lg, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx), f"top-k differs (smallest k/k+1 logit gap {gap:.3e})"
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-6
+    check_union(ridx, E)
+
+
 def route_parts(T, d, E):
     """Parts of d per router logit; mirrors the library's host rule."""
     cap = 16 if E <= 256 else (8 if E <= 512 else 4)
@@ -718,6 +745,57 @@ def test_layer_prefill_parity_19mb_layer_sampled(cfg, T, sample):
                        "y_shared") <= 1.0
     out = buf.out.float().cpu().numpy()
     assert prefill_err(out[sample], np.stack([ref["out"][t] for t in sample]), "out") <= 1.0
+
+
+def _largest_layer_check(T, path):
+    L, xf, buf = gpu_layer(7, T, path=path)
+    sh = L.shape
+    ref = oracle_sampled(L, xf, list(range(T)))
+    check_routing_and_union(buf, ref["topk_idx"], ref["topk_w"], ref["union"])
+    pos = sorted(ref["y"])
+    y = buf.y.float().cpu().numpy()
+    ysh = buf.y_shared.float().cpu().numpy()
+    out = buf.out.float().cpu().numpy()
+    got = [y[pos], ysh[:T], out[:T]]
+    want = [np.stack([ref["y"][p] for p in pos]), np.stack([ref["y_shared"][t] for t in range(T)]),
+            np.stack([ref["out"][t] for t in range(T)])]
+    return L, buf, got, want
+
+
+@pytest.mark.timeout(600)
+def test_layer_decode_parity_largest_layer():
+    """d = f = 8192 (the largest sizes the library takes) on the decode path,
+    through the separate calls and through moe_layer_decode: every output of
+    the 3-token batch against the oracle."""
+    say("layer decode cfg=7 (d = f = 8192) T=3")
+    _, _, got, want = _largest_layer_check(3, DEC)
+    for g, r, name in zip(got, want, ("y", "y_shared", "out")):
+        e = rel_err(g, r)
+        say(f"  {name}: max|err|/rms = {e:.2e}")
+        assert e <= TOL_DECODE, name
+    L, dev = dev_layer(7)
+    x, _ = tokens(7, 3)
+    sh = moe.shape_of(L.shape)
+    a = LayerBuffers.allocate(sh, 3, DEC)
+    b = LayerBuffers.allocate(sh, 3, DEC)
+    run_layer(x, dev["w_router"], dev["bias"], dev["experts"], dev["shared"], a)
+    run_layer_decode(x, dev["w_router"], dev["bias"], dev["experts"], dev["shared"], b)
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, b.out) and torch.equal(a.y_shared, b.y_shared)
+
+
+@pytest.mark.timeout(600)
+def test_layer_prefill_parity_largest_layer():
+    """d = f = 8192 on the prefill path: 160 tokens, whose Zipf routing gives
+    an expert of more than 96 rows and the shared expert's 160 (128-row tiles
+    and 32-row tiles, 128 groups along K); every output against the oracle."""
+    say("layer prefill cfg=7 (d = f = 8192) T=160")
+    L, buf, got, want = _largest_layer_check(160, PRE)
+    counts = buf.counts.cpu().numpy()
+    say(f"  rows per expert {counts.tolist()}")
+    assert counts.max() >= 96  # a 128-row tile of a routed expert
+    for g, r, name in zip(got, want, ("y", "y_shared", "out")):
+        assert prefill_err(g, r, name) <= 1.0
 
 
 @pytest.mark.timeout(900)
