@@ -1012,7 +1012,8 @@ def mx_layer(cfg):
     return _mx_layers[cfg]
 
 
-@pytest.mark.parametrize("cfg,T", [(6, 8), (6, 37), (2, 1), (2, 16), (4, 1)])
+# (7, 3): d = f = 8192, the largest sizes taken
+@pytest.mark.parametrize("cfg,T", [(6, 8), (6, 37), (2, 1), (2, 16), (4, 1), (7, 3)])
 def test_layer_decode_parity_mxfp4(cfg, T):
     """MXFP4 experts through route, union, the decode FFN (shape group 32)
     and combine, against the float64 oracle with MXFP4 block decoding."""
@@ -1038,8 +1039,9 @@ def test_layer_decode_parity_mxfp4(cfg, T):
 
 
 # (6, 512) and (6, 97): 128-row tiles full and partial, odd group counts,
-# partial column tiles; (3, 64): 256 experts with the shared expert
-@pytest.mark.parametrize("cfg,T", [(6, 512), (6, 97), (2, 16), (3, 64)])
+# partial column tiles; (3, 64): 256 experts with the shared expert;
+# (7, 160): d = f = 8192, both tile kinds over 256 MXFP4 blocks along K
+@pytest.mark.parametrize("cfg,T", [(6, 512), (6, 97), (2, 16), (3, 64), (7, 160)])
 def test_layer_prefill_parity_mxfp4(cfg, T):
     """bf16 x through route, union, the MFMA FFN over MXFP4 blocks (the E8M0
     scale folded into the E2M1 -> bf16 conversion) and a bf16 combine,
