@@ -64,7 +64,7 @@ class LayerShape:
 # The five workloads: tiny parity layer, small-expert decode layer,
 # many-small-experts layer with a shared expert and skewed routing, the
 # ~19 MB-expert layer for decode, and the same layer for 2048-token prefill;
-# plus parity-test layers (6, 7).
+# plus parity-test layers (6, 7, 8).
 WORKLOADS = {
     1: dict(shape=LayerShape(512, 256, 8, 2, 0, False, "f32"), tokens=(4,)),
     2: dict(shape=LayerShape(2048, 1024, 64, 8, 0, False, "bf16"), tokens=(1, 16)),
@@ -84,6 +84,10 @@ WORKLOADS = {
     # longest rows on the decode path, and 160 tokens give experts of more
     # than 96 rows (128-row prefill tiles) next to 32-row tiles.
     7: dict(shape=LayerShape(8192, 8192, 4, 2, 8192, True, "bf16"), tokens=(3, 160)),
+    # ... and at the smallest (64 each: one group along K, one packed 64-row
+    # tile per matrix, most lanes of a decode row and most columns of a
+    # prefill workgroup past the matrix).
+    8: dict(shape=LayerShape(64, 64, 4, 2, 64, True, "bf16"), tokens=(1, 5, 300)),
 }
 # Workload 5 runs on workload 4's layer (same router weights and expert
 # blocks); only its Zipf router bias and its token batches are its own.

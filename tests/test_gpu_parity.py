@@ -393,7 +393,9 @@ def check_routing_and_union(buf, ref_idx, ref_w, union):
     assert np.array_equal(buf.n_active.cpu().numpy(), n_active)
 
 
-FULL_CASES = [(1, 4), (1, 3), (2, 1), (2, 16), (2, 5), (3, 64), (3, 13), (4, 1), (6, 8), (6, 37)]
+# (8, 1), (8, 5): d = f = 64, the smallest sizes taken
+FULL_CASES = [(1, 4), (1, 3), (2, 1), (2, 16), (2, 5), (3, 64), (3, 13), (4, 1), (6, 8), (6, 37),
+              (8, 1), (8, 5)]
 
 
 # the separate calls, and (batches of at most 8 tokens) the one-call moe_layer_decode
@@ -696,7 +698,8 @@ def prefill_err(got, ref, name=""):
     return bound
 # (6, 512) and (6, 97): 128-row tiles (full and partial), odd group counts
 # along d and f, partial column tiles, an unrouted expert
-PREFILL_FULL = [(2, 16), (2, 5), (3, 64), (3, 13), (6, 512), (6, 97)]
+# (8, 5), (8, 300): d = f = 64 (one group along K, columns past the matrix)
+PREFILL_FULL = [(2, 16), (2, 5), (3, 64), (3, 13), (6, 512), (6, 97), (8, 5), (8, 300)]
 
 
 @pytest.mark.parametrize("cfg,T", PREFILL_FULL)
@@ -1013,7 +1016,7 @@ def mx_layer(cfg):
 
 
 # (7, 3): d = f = 8192, the largest sizes taken
-@pytest.mark.parametrize("cfg,T", [(6, 8), (6, 37), (2, 1), (2, 16), (4, 1), (7, 3)])
+@pytest.mark.parametrize("cfg,T", [(6, 8), (6, 37), (2, 1), (2, 16), (4, 1), (7, 3), (8, 5)])
 def test_layer_decode_parity_mxfp4(cfg, T):
     """MXFP4 experts through route, union, the decode FFN (shape group 32)
     and combine, against the float64 oracle with MXFP4 block decoding."""
@@ -1041,7 +1044,7 @@ def test_layer_decode_parity_mxfp4(cfg, T):
 # (6, 512) and (6, 97): 128-row tiles full and partial, odd group counts,
 # partial column tiles; (3, 64): 256 experts with the shared expert;
 # (7, 160): d = f = 8192, both tile kinds over 256 MXFP4 blocks along K
-@pytest.mark.parametrize("cfg,T", [(6, 512), (6, 97), (2, 16), (3, 64), (7, 160)])
+@pytest.mark.parametrize("cfg,T", [(6, 512), (6, 97), (2, 16), (3, 64), (7, 160), (8, 300)])
 def test_layer_prefill_parity_mxfp4(cfg, T):
     """bf16 x through route, union, the MFMA FFN over MXFP4 blocks (the E8M0
     scale folded into the E2M1 -> bf16 conversion) and a bf16 combine,
