@@ -64,7 +64,7 @@ class LayerShape:
 # The five workloads: tiny parity layer, small-expert decode layer,
 # many-small-experts layer with a shared expert and skewed routing, the
 # ~19 MB-expert layer for decode, and the same layer for 2048-token prefill;
-# plus parity-test layers (6, 7, 8).
+# plus parity-test layers (6 to 9).
 WORKLOADS = {
     1: dict(shape=LayerShape(512, 256, 8, 2, 0, False, "f32"), tokens=(4,)),
     2: dict(shape=LayerShape(2048, 1024, 64, 8, 0, False, "bf16"), tokens=(1, 16)),
@@ -88,6 +88,9 @@ WORKLOADS = {
     # tile per matrix, most lanes of a decode row and most columns of a
     # prefill workgroup past the matrix).
     8: dict(shape=LayerShape(64, 64, 4, 2, 64, True, "bf16"), tokens=(1, 5, 300)),
+    # ... and at the most experts and the largest top-k (1024 and 32) with a
+    # shared expert: 40 tokens make 1025 expert slots.
+    9: dict(shape=LayerShape(128, 128, 1024, 32, 128, True, "bf16"), tokens=(1, 3, 40)),
 }
 # Workload 5 runs on workload 4's layer (same router weights and expert
 # blocks); only its Zipf router bias and its token batches are its own.

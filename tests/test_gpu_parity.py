@@ -393,14 +393,15 @@ def check_routing_and_union(buf, ref_idx, ref_w, union):
     assert np.array_equal(buf.n_active.cpu().numpy(), n_active)
 
 
-# (8, 1), (8, 5): d = f = 64, the smallest sizes taken
+# (8, 1), (8, 5): d = f = 64, the smallest sizes taken; (9, 1), (9, 3): 1024
+# experts, top-32 (the separate calls only: moe_layer_decode takes E <= 256)
 FULL_CASES = [(1, 4), (1, 3), (2, 1), (2, 16), (2, 5), (3, 64), (3, 13), (4, 1), (6, 8), (6, 37),
-              (8, 1), (8, 5)]
+              (8, 1), (8, 5), (9, 1), (9, 3)]
 
 
 # the separate calls, and (batches of at most 8 tokens) the one-call moe_layer_decode
 @pytest.mark.parametrize("cfg,T,fused", [(c, T, f) for c, T in FULL_CASES
-                                         for f in ((False, True) if T <= 8 else (False,))])
+                                         for f in ((False, True) if T <= 8 and c != 9 else (False,))])
 def test_layer_decode_parity(cfg, T, fused):
     say(f"layer decode cfg={cfg} T={T} fused={fused}")
     L, xf, buf = gpu_layer(cfg, T, fused=fused)
@@ -698,8 +699,9 @@ def prefill_err(got, ref, name=""):
     return bound
 # (6, 512) and (6, 97): 128-row tiles (full and partial), odd group counts
 # along d and f, partial column tiles, an unrouted expert
-# (8, 5), (8, 300): d = f = 64 (one group along K, columns past the matrix)
-PREFILL_FULL = [(2, 16), (2, 5), (3, 64), (3, 13), (6, 512), (6, 97), (8, 5), (8, 300)]
+# (8, 5), (8, 300): d = f = 64 (one group along K, columns past the matrix);
+# (9, 40): 1024 experts, top-32, 1025 slots (two chunks of the tile lists)
+PREFILL_FULL = [(2, 16), (2, 5), (3, 64), (3, 13), (6, 512), (6, 97), (8, 5), (8, 300), (9, 40)]
 
 
 @pytest.mark.parametrize("cfg,T", PREFILL_FULL)
