@@ -16,13 +16,13 @@ extern "C" {
 #endif
 
 /* Read n_blocks device blocks of block_bytes each once: every block split
- * into wpb = max(1, workgroups / n_blocks) equal shares, one workgroup of
+ * into wpb = workgroups / n_blocks equal shares, one workgroup of
  * 256 threads (16-byte loads) per share, wpb * n_blocks workgroups in all;
  * the loaded words are folded into one uint32 per workgroup in sink.
  *  blocks      HOST array of n_blocks device pointers (1 <= n_blocks <= 64),
  *              each 16-byte aligned
  *  block_bytes a positive multiple of 16
- *  workgroups  1 .. 65536
+ *  workgroups  n_blocks .. 65536 (else MOE_ERR_SHAPE)
  *  sink        device uint32 [wpb * n_blocks] (at most `workgroups`
  *              entries), 4-byte aligned (contents unused) */
 moe_status moe_measure_stream_read(const uint8_t* const* blocks, int32_t n_blocks,

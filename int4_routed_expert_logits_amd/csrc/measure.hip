@@ -65,8 +65,8 @@ moe_status moe_measure_stream_read(const uint8_t* const* blocks, int32_t n_block
                                    size_t block_bytes, int32_t workgroups, uint32_t* sink,
                                    void* stream) {
   if (!blocks || !sink) return MOE_ERR_NULL;
-  if (n_blocks < 1 || n_blocks > moe::kMaxReadBlocks || workgroups < 1 || workgroups > 65536 ||
-      block_bytes == 0 || block_bytes % 16)
+  if (n_blocks < 1 || n_blocks > moe::kMaxReadBlocks || workgroups < n_blocks ||
+      workgroups > 65536 || block_bytes == 0 || block_bytes % 16)
     return MOE_ERR_SHAPE;
   moe::ReadArgs a{};
   for (int i = 0; i < n_blocks; ++i) {
@@ -75,8 +75,9 @@ moe_status moe_measure_stream_read(const uint8_t* const* blocks, int32_t n_block
     a.blocks[i] = blocks[i];
   }
   if (reinterpret_cast<uintptr_t>(sink) % 4) return MOE_ERR_ALIGN;
-  // wpb equal shares of every block, each a whole number of 16-byte pieces
-  const int wpb = workgroups / n_blocks > 0 ? workgroups / n_blocks : 1;
+  // wpb equal shares of every block, each a whole number of 16-byte pieces;
+  // wpb * n_blocks <= workgroups, the size of sink
+  const int wpb = workgroups / n_blocks;
   unsigned long long per = (static_cast<unsigned long long>(block_bytes) + wpb - 1) / wpb;
   per = (per + 15) / 16 * 16;
   const hipError_t err =

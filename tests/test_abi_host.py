@@ -236,6 +236,41 @@ def test_quantize_argument_checks(lib):
     assert q(N=0, w=None, c=None, sc=None) == B.MOE_OK
 
 
+def test_pack_argument_checks(lib):
+    s = ctypes.byref(shp())
+    bb = lib.moe_expert_bytes(512, 256, 64)  # the block of shp()
+    assert lib.moe_pack_experts(s, -1, P, P + 4 * bb, None) == B.MOE_ERR_SHAPE
+    assert lib.moe_pack_experts(s, 2, None, P, None) == B.MOE_ERR_NULL
+    assert lib.moe_pack_experts(s, 2, P, None, None) == B.MOE_ERR_NULL
+    assert lib.moe_pack_experts(s, 2, MIS, P + 4 * bb, None) == B.MOE_ERR_ALIGN
+    assert lib.moe_pack_experts(s, 2, P, P + 4 * bb + 8, None) == B.MOE_ERR_ALIGN
+    # source and destination overlapping by one 16-byte piece, either way round
+    assert lib.moe_pack_experts(s, 2, P, P + 2 * bb - 16, None) == B.MOE_ERR_SHAPE
+    assert lib.moe_pack_experts(s, 2, P + 2 * bb - 16, P, None) == B.MOE_ERR_SHAPE
+    assert lib.moe_pack_experts(ctypes.byref(shp(group=16)), 2, P, P + 4 * bb, None) == \
+        B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_pack_experts(s, 0, None, None, None) == B.MOE_OK  # nothing to pack
+
+
+def test_stream_read_argument_checks(lib):
+    blocks = (ctypes.c_void_p * 3)(P, P + 4096, P + 8192)
+    r = lambda bl=blocks, n=3, bb=4096, wg=12, sink=P: lib.moe_measure_stream_read(
+        bl, n, bb, wg, sink, None)
+    assert r(bl=None) == B.MOE_ERR_NULL
+    assert r(sink=None) == B.MOE_ERR_NULL
+    assert r(n=0) == B.MOE_ERR_SHAPE
+    assert r(n=65) == B.MOE_ERR_SHAPE
+    assert r(bb=0) == B.MOE_ERR_SHAPE
+    assert r(bb=4100) == B.MOE_ERR_SHAPE
+    assert r(wg=65537) == B.MOE_ERR_SHAPE
+    # fewer workgroups than blocks: sink (sized by workgroups) could not hold
+    # one word per block
+    assert r(wg=2) == B.MOE_ERR_SHAPE
+    assert r(bl=(ctypes.c_void_p * 3)(P, None, P)) == B.MOE_ERR_NULL
+    assert r(bl=(ctypes.c_void_p * 3)(P, MIS, P)) == B.MOE_ERR_ALIGN
+    assert r(sink=P + 2) == B.MOE_ERR_ALIGN
+
+
 def test_union_argument_checks(lib):
     s = ctypes.byref(shp())
     assert lib.moe_union(s, 4, None, P, P, P, P, P, P, None) == B.MOE_ERR_NULL
