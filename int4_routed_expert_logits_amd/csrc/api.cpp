@@ -382,6 +382,8 @@ const char* moe_status_str(moe_status status) {
     case MOE_ERR_UNSUPPORTED: return "well-formed request this library does not provide";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "a HIP launch failed";
+    case MOE_STATUS_INT_MIN_:
+    case MOE_STATUS_INT_MAX_: break;  // range members, not statuses
   }
   return "unknown status";
 }

@@ -18,7 +18,6 @@ template <bool BF16>
 struct Vec;
 template <>
 struct Vec<false> {
-  static constexpr int kN = 4;
   __device__ static void load(const void* p, size_t i, float (&v)[4]) {
     const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
@@ -26,7 +25,6 @@ struct Vec<false> {
 };
 template <>
 struct Vec<true> {
-  static constexpr int kN = 8;
   __device__ static void load(const void* p, size_t i, float (&v)[8]) {
     const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -62,7 +60,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const void* __restrict__ y,
                                                      const void* __restrict__ y_shared,
                                                      const int32_t* __restrict__ inv_perm,
                                                      const float* __restrict__ topk_w,
-                                                     void* __restrict__ out, int T, int d,
+                                                     void* __restrict__ out,
+                                                     int /*T, the grid's y extent*/, int d,
                                                      int k) {
   constexpr int V = 8;   // columns per thread
   constexpr int KU = 8;  // slots in flight

@@ -79,7 +79,7 @@ __device__ __forceinline__ uint32_t pack8(const float (&v)[8], float s) {
 // GS64: 8 lanes per group, 8 consecutive weights per lane; the group's
 // absolute maximum is reduced over its 8 lanes.
 template <bool F32>
-__global__ __launch_bounds__(256) void quant_gs64(const void* __restrict__ w, int K, long long groups,
+__global__ __launch_bounds__(256) void quant_gs64(const void* __restrict__ w, int /*K*/, long long groups,
                                                   uint32_t* __restrict__ codes,
                                                   _Float16* __restrict__ scales) {
   const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
