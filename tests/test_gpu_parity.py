@@ -1275,3 +1275,39 @@ def test_mxfp4_rejected_where_not_built():
                              buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.perm,
                              buf.inv_perm, buf.active, buf.n_active, buf.y, buf.y_shared, buf.out,
                              buf.layer_workspace)
+
+
+# ----------------------------------------------------------------------------
+# the benchmark's calibration read
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,block_bytes,workgroups", [(3, 1 << 20, 3), (3, (1 << 20) + 48, 7),
+                                                      (9, 20_054_016, 2304), (2, 4096, 4096),
+                                                      (5, 160, 37)])
+def test_stream_read_folds_every_piece_of_its_share_once(n, block_bytes, workgroups):
+    """moe_measure_stream_read: workgroup w XORs the 16-byte pieces of its
+    share (block w / wpb, bytes [per * s, per * s + per) cut at the block's
+    end, s = w % wpb, wpb = workgroups / n, per = block_bytes / wpb rounded
+    up to 16) into one word; on random blocks every word must equal that
+    XOR of the share's 32-bit words, so no piece is skipped or read twice.
+    Shapes: ragged blocks, shares past a block's end (empty), one
+    workgroup per block, the decode step's nine 19 MB blocks."""
+    say(f"stream read n={n} bytes={block_bytes} workgroups={workgroups}")
+    rng = np.random.default_rng(block_bytes + workgroups)
+    host = rng.integers(0, 2 ** 32, size=(n, block_bytes // 4), dtype=np.uint32)
+    dev = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = torch.full((workgroups,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    moe.moe_measure_stream_read([dev[b].data_ptr() for b in range(n)], block_bytes, workgroups,
+                                sink)
+    torch.cuda.synchronize()
+    wpb = workgroups // n
+    per = -(-block_bytes // wpb)
+    per = -(-per // 16) * 16
+    got = sink.cpu().numpy().view(np.uint32)
+    for w in range(wpb * n):
+        b, sh = divmod(w, wpb)
+        lo, hi = min(per * sh, block_bytes), min(per * sh + per, block_bytes)
+        want = np.bitwise_xor.reduce(host[b, lo // 4: hi // 4]) if hi > lo else np.uint32(0)
+        assert got[w] == want, f"workgroup {w} (block {b}, share {sh})"
+    # entries past wpb * n are not written
+    assert np.all(got[wpb * n:] == 0x5A5A5A5A)
